@@ -1,0 +1,72 @@
+"""fp64 forward and backward of the QLoRA linear (oracle; test infrastructure
+only).
+
+The method reaches, up to rounding order, the plain dense result, so the
+oracle is that definition written out: the bf16 inputs are widened exactly to
+fp64 and every product is a fp64 matmul (a library primitive).  No result is
+rounded.
+
+Shapes (row-major):  X [T, in], W_hat [out, in], A [r, in], B [out, r],
+dY [T, out].  Scale s = alpha / r.
+
+Forward (paperclase "QLoRA", Parte 4, "El gradiente atraviesa la base de 4
+bits", h = W_hat x + (alpha/r) B A x; same page, the layer's forward adds
+escala * x A^T B^T to the linear):
+    U = X A^T                      [T, r]
+    Y = X W_hat^T + s U B^T        [T, out]
+Backward (same section: dL/dx = (W_hat + (alpha/r) B A)^T dL/dh; no gradient
+for W_hat, the codes are not parameters; A and B are the only trained
+tensors, their gradients by the chain rule):
+    V  = dY B                      [T, r]
+    dX = dY W_hat + s V A          [T, in]
+    dA = s V^T X                   [r, in]
+    dB = s dY^T U                  [out, r]
+"""
+
+import numpy as np
+
+from .nf4 import bf16_bits_to_f32
+
+
+def widen(bits_or_f32: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or fp32 values -> exact fp64."""
+    a = np.asarray(bits_or_f32)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def lora_down(X, A) -> np.ndarray:
+    """U = X A^T (also V = dY B with (dY, B^T))."""
+    return widen(X) @ widen(A).T
+
+
+def linear_fwd(W_hat, X, A, B, alpha: float, r: int) -> np.ndarray:
+    """Y = X W_hat^T + (alpha/r) (X A^T) B^T, fp64."""
+    s = float(alpha) / float(r)
+    Xd, Wd, Ad, Bd = widen(X), widen(W_hat), widen(A), widen(B)
+    U = Xd @ Ad.T
+    return Xd @ Wd.T + s * (U @ Bd.T)
+
+
+def linear_bwd(W_hat, X, dY, A, B, alpha: float, r: int):
+    """(dX, dA, dB) in fp64 for the forward above."""
+    s = float(alpha) / float(r)
+    Xd, Wd, Ad, Bd, Gd = widen(X), widen(W_hat), widen(A), widen(B), widen(dY)
+    U = Xd @ Ad.T
+    V = Gd @ Bd
+    dX = Gd @ Wd + s * (V @ Ad)
+    dA = s * (V.T @ Xd)
+    dB = s * (Gd.T @ U)
+    return dX, dA, dB
+
+
+def rel_frobenius(got, ref) -> float:
+    """||got - ref||_F / ||ref||_F in fp64 (the acceptance measure)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(r)
+    num = np.linalg.norm(g - r)
+    if den == 0:
+        return 0.0 if num == 0 else float("inf")
+    return float(num / den)
