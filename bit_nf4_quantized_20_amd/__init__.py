@@ -1,0 +1,239 @@
+"""Python binding of libqlora.so, the gfx950 NF4 / QLoRA-linear library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory (``torch.empty``), raw pointers
+(``data_ptr``) and the current stream; it computes nothing here.  If the
+library has not been built, importing this package raises.
+
+Names and semantics follow include/qlora.h:
+    nf4_storage_bytes, nf4_quantize, nf4_dequantize, qlora_workspace_bytes,
+    qlora_linear_fwd, qlora_linear_bwd, nf4_codebook, nf4_code_thresholds,
+    qlora_status_string
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+QLORA_OK = 0
+STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_ALIGN", -4: "ERR_WORKSPACE",
+          -5: "ERR_LAUNCH", -6: "ERR_DEVICE", -7: "ERR_VALUE"}
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_status_string(status)})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_nf4_quantized_20_amd.build` "
+                      "(hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class _NF4WeightC(ctypes.Structure):
+    _fields_ = [("codes", _p), ("absmax_q", _p), ("absmax_scale", _p), ("rows", _i64),
+                ("cols", _i64)]
+
+
+_lib.nf4_storage_bytes.argtypes = [_i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+_lib.nf4_storage_bytes.restype = ctypes.c_int
+_lib.nf4_quantize.argtypes = [_p, _i64, _p, _p, _p, _p]
+_lib.nf4_quantize.restype = ctypes.c_int
+_lib.nf4_dequantize.argtypes = [_p, _p, _p, _i64, _p, _p]
+_lib.nf4_dequantize.restype = ctypes.c_int
+_lib.qlora_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+_lib.qlora_workspace_bytes.restype = _sz
+_lib.qlora_linear_fwd.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _i64, _p, _p, _i64, ctypes.c_float,
+                                  _p, _p, _sz, _p]
+_lib.qlora_linear_fwd.restype = ctypes.c_int
+_lib.qlora_linear_bwd.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, _p, _i64,
+                                  ctypes.c_float, _p, _p, _p, _p, _sz, _p]
+_lib.qlora_linear_bwd.restype = ctypes.c_int
+_lib.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+_lib.nf4_codebook.restype = None
+_lib.nf4_code_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
+_lib.nf4_code_thresholds.restype = None
+_lib.qlora_status_string.argtypes = [ctypes.c_int]
+_lib.qlora_status_string.restype = ctypes.c_char_p
+
+
+def _status_string(status: int) -> str:
+    return _lib.qlora_status_string(int(status)).decode()
+
+
+qlora_status_string = _status_string
+
+
+def _check(status: int, where: str):
+    if status != QLORA_OK:
+        raise QloraError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, numel: int = None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+@dataclass
+class NF4Weight:
+    """Frozen NF4 weight [rows = out_features, cols = in_features]."""
+    codes: torch.Tensor          # uint8 [rows*cols/2]
+    absmax_q: torch.Tensor       # uint8 [rows*cols/64]
+    absmax_scale: torch.Tensor   # float32 [ceil(rows*cols/16384)]
+    rows: int
+    cols: int
+
+    def _c(self):
+        return _NF4WeightC(self.codes.data_ptr(), self.absmax_q.data_ptr(),
+                           self.absmax_scale.data_ptr(), self.rows, self.cols)
+
+
+def nf4_storage_bytes(numel: int):
+    c, q, s = _sz(), _sz(), _sz()
+    _check(_lib.nf4_storage_bytes(numel, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s)),
+           "nf4_storage_bytes")
+    return c.value, q.value, s.value
+
+
+def nf4_quantize(w: torch.Tensor, codes=None, absmax_q=None, absmax_scale=None):
+    """fp32 device tensor (any shape, numel % 64 == 0) -> (codes, absmax_q, absmax_scale)."""
+    _need(w, torch.float32, "w")
+    n = w.numel()
+    cb, qb, sb = nf4_storage_bytes(n)
+    dev = w.device
+    if codes is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    if absmax_q is None:
+        absmax_q = torch.empty(qb, dtype=torch.uint8, device=dev)
+    if absmax_scale is None:
+        absmax_scale = torch.empty(sb // 4, dtype=torch.float32, device=dev)
+    _need(codes, torch.uint8, "codes", cb)
+    _need(absmax_q, torch.uint8, "absmax_q", qb)
+    _need(absmax_scale, torch.float32, "absmax_scale", sb // 4)
+    _check(_lib.nf4_quantize(_ptr(w), n, _ptr(codes), _ptr(absmax_q), _ptr(absmax_scale),
+                             _stream(dev)), "nf4_quantize")
+    return codes, absmax_q, absmax_scale
+
+
+def nf4_quantize_weight(w: torch.Tensor) -> NF4Weight:
+    """Quantizes a [out, in] fp32 weight into an NF4Weight."""
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D [out, in]")
+    c, q, s = nf4_quantize(w)
+    return NF4Weight(c, q, s, w.shape[0], w.shape[1])
+
+
+def nf4_dequantize(codes, absmax_q, absmax_scale, numel: int, out=None):
+    """-> bf16 device tensor [numel]."""
+    if out is None:
+        out = torch.empty(numel, dtype=torch.bfloat16, device=codes.device)
+    _need(out, torch.bfloat16, "out", numel)
+    _check(_lib.nf4_dequantize(_ptr(codes), _ptr(absmax_q), _ptr(absmax_scale), numel, _ptr(out),
+                               _stream(codes.device)), "nf4_dequantize")
+    return out
+
+
+def qlora_workspace_bytes(T: int, in_features: int, out_features: int, r: int, backward: bool) -> int:
+    return int(_lib.qlora_workspace_bytes(T, in_features, out_features, r, 1 if backward else 0))
+
+
+def _workspace(ws, T, n_in, n_out, r, backward, device):
+    need = qlora_workspace_bytes(T, n_in, n_out, r, backward)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def qlora_linear_fwd(W: NF4Weight, X, A, B, r: int, alpha: float, Y=None, ws=None):
+    """Y [T, out] bf16 = X W_hat^T + (alpha/r) (X A^T) B^T."""
+    T = X.shape[0]
+    _need(X, torch.bfloat16, "X", T * W.cols)
+    _need(A, torch.bfloat16, "A", r * W.cols)
+    _need(B, torch.bfloat16, "B", W.rows * r)
+    if Y is None:
+        Y = torch.empty(T, W.rows, dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", T * W.rows)
+    ws, ws_bytes = _workspace(ws, T, W.cols, W.rows, r, False, X.device)
+    wc = W._c()
+    _check(_lib.qlora_linear_fwd(ctypes.byref(wc), _ptr(X), T, _ptr(A), _ptr(B), r, float(alpha),
+                                 _ptr(Y), _ptr(ws), ws_bytes, _stream(X.device)), "qlora_linear_fwd")
+    return Y
+
+
+def qlora_linear_bwd(W: NF4Weight, X, dY, A, B, r: int, alpha: float, dX=None, dA=None, dB=None,
+                     ws=None):
+    """-> (dX [T, in] bf16, dA [r, in] fp32, dB [out, r] fp32)."""
+    T = X.shape[0]
+    _need(X, torch.bfloat16, "X", T * W.cols)
+    _need(dY, torch.bfloat16, "dY", T * W.rows)
+    _need(A, torch.bfloat16, "A", r * W.cols)
+    _need(B, torch.bfloat16, "B", W.rows * r)
+    dev = X.device
+    if dX is None:
+        dX = torch.empty(T, W.cols, dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty(r, W.cols, dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty(W.rows, r, dtype=torch.float32, device=dev)
+    _need(dX, torch.bfloat16, "dX", T * W.cols)
+    _need(dA, torch.float32, "dA", r * W.cols)
+    _need(dB, torch.float32, "dB", W.rows * r)
+    ws, ws_bytes = _workspace(ws, T, W.cols, W.rows, r, True, dev)
+    wc = W._c()
+    _check(_lib.qlora_linear_bwd(ctypes.byref(wc), _ptr(X), _ptr(dY), T, _ptr(A), _ptr(B), r,
+                                 float(alpha), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
+                                 _stream(dev)), "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+def nf4_codebook():
+    out = (ctypes.c_float * 16)()
+    _lib.nf4_codebook(out)
+    return [float(v) for v in out]
+
+
+def nf4_code_thresholds():
+    out = (ctypes.c_float * 15)()
+    _lib.nf4_code_thresholds(out)
+    return [float(v) for v in out]
+
+
+class QLoRALinearFunction(torch.autograd.Function):
+    """Pairs qlora_linear_fwd / qlora_linear_bwd as an autograd function
+    (inputs X, A, B; the NF4 weight gets no gradient)."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, W: NF4Weight, r: int, alpha: float):
+        ctx.save_for_backward(X, A, B)
+        ctx.W, ctx.r, ctx.alpha = W, r, alpha
+        return qlora_linear_fwd(W, X.contiguous(), A.contiguous(), B.contiguous(), r, alpha)
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B = ctx.saved_tensors
+        dX, dA, dB = qlora_linear_bwd(ctx.W, X, dY.contiguous().to(torch.bfloat16), A, B, ctx.r,
+                                      ctx.alpha)
+        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None

@@ -1,0 +1,77 @@
+// common.hpp -- vector types, DPP helpers and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// DPP lane moves within a row of 16 lanes (bound_ctrl off, all rows/banks).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                               0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+// max over each aligned group of 16 lanes, result in every lane of the group
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
+  return v;
+}
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// ---------------------------------------------------------------------------
+// Launchers (host side).  Each returns hipSuccess or the launch error.
+// Shapes are validated by the caller (the C ABI layer).
+// ---------------------------------------------------------------------------
+hipError_t launch_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
+                               float* scale, hipStream_t s);
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
+                                 int64_t numel, uint16_t* out, hipStream_t s);
+// out[c][r] = W_hat[r][c] for W_hat [rows][cols]; rows % 64 == 0, cols % 64 == 0
+hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t* absmax_q,
+                                            const float* scale, int64_t rows, int64_t cols,
+                                            uint16_t* out, hipStream_t s);
+
+// U[t][j] = sum_k in[t][k] * P(j, k), j < r, fp32; optionally also the
+// bf16 pair u_pad[t][j] = hi, u_pad[t][rp + j] = lo with hi + lo = scale*U
+// (to bf16 precision twice over) for j < r, and 0 for r <= j < rp.
+// P(j, k) = p[j * K + k] if p_rows_are_r else p[k * r + j].
+hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* p,
+                            bool p_rows_are_r, int64_t r, float scale, float* u_out,
+                            uint16_t* u_pad, int64_t rp, hipStream_t s);
+// G(j, c) = scale * sum_t P[t][j] * Q[t][c], fp32, j < r, c < C.
+// Stored at out[j * C + c] (out_jc) or out[c * r + j].
+hipError_t launch_lora_grad(const float* P, const uint16_t* Q, int64_t T, int64_t r, int64_t C,
+                            float scale, float* out, bool out_jc, hipStream_t s);
+// dst[i][j] = dst[i][Cp + j] (R x 2Cp, bf16) = src(i, j) for j < C, else 0, where
+// src(i, j) = src[i * C + j] (!transpose) or src[j * R + i] (transpose).
+hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
+                           int64_t Cp, hipStream_t s);
+hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
+
+// C[M][N] (bf16, ldc) = sum over the two K segments of act_i[m][k] * wt_i[n][k]
+// (bf16, K-contiguous, leading dims lda_i / ldw_i).  K0, K1 multiples of 64
+// (K1 may be 0).  N % 64 == 0.
+hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
+                          const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
+                          int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
+                          int64_t ldc, hipStream_t s);
+
+}  // namespace qlora

@@ -1,0 +1,186 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) NF4 / QLoRA linear library.
+ *
+ * What the library computes (the pages it follows are named per call):
+ *   - NF4 quantization of a frozen fp32 weight: one absmax per 64 consecutive
+ *     weights, nearest of 16 normal-quantile levels per weight, and double
+ *     quantization of the absmax values to 8 bits with one fp32 scale per 256
+ *     blocks (ultralytics glossary "QLoRA", "Como funciona a QLoRA": NF4 and
+ *     double-quantization bullets; paperclase lesson "QLoRA", Partes 1-3).
+ *   - dequantization of that weight to bfloat16 (same pages; paperclase
+ *     Parte 2, w_hat = NF4[c] * absmax).
+ *   - the QLoRA linear, forward h = W_hat x + (alpha/r) B A x and backward
+ *     (dX through W_hat and the LoRA path; gradients for A and B only)
+ *     (paperclase "QLoRA", Parte 4, "El gradiente atraviesa la base de 4
+ *     bits").
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major data on
+ *     the current HIP device, 16-byte aligned.  The caller owns every buffer,
+ *     including the workspace; the library allocates no device memory and
+ *     keeps no pointer after returning.  Its only global state is a
+ *     per-device cache of the architecture check (thread-safe).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Each call checks
+ *     its arguments on the host, enqueues its kernels on `stream` and
+ *     returns; nothing is synchronised.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Return value: QLORA_OK (0) or a negative qlora_status.  A call that
+ *     fails validation enqueues nothing and leaves every output untouched.
+ *     Validation happens before any HIP call, so it can be exercised on a
+ *     machine without a GPU.  No call aborts or throws.
+ *   - Outputs must not alias inputs (not checked).
+ *   - bfloat16 values are passed as raw 16-bit patterns (qlora_bf16).
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t qlora_bf16;   /* raw bfloat16 bits */
+typedef void* qlora_stream;    /* hipStream_t */
+
+enum qlora_status {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,      /* a required pointer is NULL */
+  QLORA_ERR_SHAPE = -2,     /* a size is negative, not a multiple of 64, or out of range */
+  QLORA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
+  QLORA_ERR_WORKSPACE = -4, /* workspace missing or smaller than qlora_workspace_bytes() */
+  QLORA_ERR_LAUNCH = -5,    /* a kernel launch failed (hipGetLastError) */
+  QLORA_ERR_DEVICE = -6,    /* no HIP device, or the current device is not gfx950 */
+  QLORA_ERR_VALUE = -7      /* a scalar argument is not finite */
+};
+
+/* Block and group sizes of the format (fixed). */
+#define QLORA_NF4_BLOCK 64      /* weights per absmax block */
+#define QLORA_NF4_GROUP 256     /* blocks per double-quantization scale */
+#define QLORA_MAX_RANK 256      /* largest LoRA rank r accepted */
+
+/*
+ * A frozen NF4 weight W_hat [rows = out_features, cols = in_features].
+ * Blocks are 64 consecutive weights of the row-major flattening, so with
+ * cols % 64 == 0 a block never crosses a row; double-quantization groups are
+ * 256 consecutive blocks of the same flattening and may cross rows.
+ *   codes        [rows*cols/2]  packed 4-bit codes; element 2i in bits 0-3,
+ *                               element 2i+1 in bits 4-7 of byte i
+ *   absmax_q     [rows*cols/64] 8-bit double-quantized absmax, one per block
+ *   absmax_scale [ceil(rows*cols/16384)] fp32 scale per group of 256 blocks
+ * Code c selects level L[c] of the 16-entry codebook (nf4_codebook), with
+ * L ascending and L[7] = +0.0.
+ */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* absmax_q;
+  const float* absmax_scale;
+  int64_t rows;
+  int64_t cols;
+} qlora_nf4_weight;
+
+/*
+ * Sizes in bytes of the three NF4 buffers for `numel` weights
+ * (numel >= 0, numel % 64 == 0): codes numel/2, absmax_q numel/64,
+ * absmax_scale 4*ceil(numel/16384).  That is 4 + 8/64 + 32/16384 bits per
+ * weight, the double-quantization budget of paperclase "QLoRA", Parte 3,
+ * "Bits por parametro".  Host only; any output pointer may be NULL.
+ * Errors: QLORA_ERR_SHAPE.
+ */
+int nf4_storage_bytes(int64_t numel, size_t* codes_bytes, size_t* absmax_q_bytes,
+                      size_t* scale_bytes);
+
+/*
+ * nf4_quantize -- Q1..Q4: fp32 weight -> NF4 codes + double-quantized absmax.
+ * Follows ultralytics glossary "QLoRA", "Como funciona a QLoRA" (one absmax
+ * per 64 weights, nearest of the 16 quantile levels, absmax values quantized
+ * to 8 bits in blocks of 256) and paperclase "QLoRA", Parte 4 (codes by argmin
+ * of the distance to the levels; two codes per byte).  Per block b of 64
+ * weights: a_b = max |w|; per weight x = fl32(w / a_b) and code = the first
+ * index j minimising |fl32(x - L[j])|.  Per group g of 256 blocks:
+ * s_g = max a_b, q_b = round_half_even(fl32(fl32(a_b / s_g) * 255)).  A zero
+ * block gets codes 7 and q 0; a zero group gets s 0.  The last group may be
+ * partial.  The codes use the exact fp32 a_b.
+ *   w            [numel] fp32, finite (non-finite input: outputs unspecified)
+ *   numel        >= 0, multiple of 64; 0 is a no-op
+ *   codes        [numel/2] out;  absmax_q [numel/64] out;
+ *   absmax_scale [ceil(numel/16384)] out
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
+ */
+int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
+                 float* absmax_scale, qlora_stream stream);
+
+/*
+ * nf4_dequantize -- D1: NF4 storage -> bfloat16 weight.
+ * a_hat_b = fl32(fl32(q_b / 255) * s_g);  w_hat = bf16_rne(fl32(L[c] * a_hat_b))
+ * (paperclase "QLoRA", Parte 2: w_hat = NF4[c] * absmax; ultralytics "QLoRA":
+ * weights are dequantized to bfloat16 right before the matmul).
+ *   codes, absmax_q, absmax_scale as produced by nf4_quantize for numel
+ *   w_out [numel] bf16 out (row-major, same order as the quantized input)
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
+ */
+int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_scale,
+                   int64_t numel, qlora_bf16* w_out, qlora_stream stream);
+
+/*
+ * Workspace bytes needed by qlora_linear_fwd (backward = 0) or
+ * qlora_linear_bwd (backward = 1) for T tokens, in/out features and rank r.
+ * Returns 0 for invalid shapes.  Host only.
+ */
+size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
+                             int backward);
+
+/*
+ * qlora_linear_fwd -- F1 + F2: Y = X W_hat^T + (alpha/r) (X A^T) B^T.
+ * paperclase "QLoRA", Parte 4, h = W_hat x + (alpha/r) B A x, with
+ * W_hat = dq(codes, absmax) rebuilt inside the matmul and never stored.
+ * bf16 inputs, fp32 accumulation, one rounding of Y to bf16 at the end.
+ *   W   NF4 weight [out, in]; in % 64 == 0, out % 64 == 0
+ *   X   [T, in] bf16;  T >= 0 (0 is a no-op; X and Y may then be NULL)
+ *   A   [r, in] bf16;  B [out, r] bf16;  1 <= r <= 256;  alpha finite
+ *   Y   [T, out] bf16 out
+ *   ws  workspace of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 0)
+ * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE, LAUNCH.
+ */
+int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
+                     const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
+                     qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream);
+
+/*
+ * qlora_linear_bwd -- B1..B3 for the forward above, with s = alpha/r:
+ *   dX = dY W_hat + s (dY B) A        [T, in]  bf16 (one rounding)
+ *   dA = s (dY B)^T X                 [r, in]  fp32
+ *   dB = s dY^T (X A^T)               [out, r] fp32
+ * paperclase "QLoRA", Parte 4: dL/dx = (W_hat + (alpha/r) B A)^T dL/dh; no
+ * gradient for W_hat (the codes are not parameters); A and B are the only
+ * trained tensors.  dA and dB are overwritten, not accumulated.
+ *   dY [T, out] bf16; other arguments as in qlora_linear_fwd;
+ *   ws of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1)
+ * T == 0 writes zeros to dA and dB and nothing else (X, dY, dX may be NULL).
+ * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE, LAUNCH.
+ */
+int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora_bf16* dY,
+                     int64_t T, const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
+                     qlora_bf16* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                     qlora_stream stream);
+
+/* Host copy of the 16 fp32 levels the kernels use (ascending, L[7] = +0.0). */
+void nf4_codebook(float out[16]);
+
+/*
+ * Host copy of the 15 fp32 code thresholds the quantize kernel uses:
+ * code(x) = number of j with x > t[j], for x = fl32(w / a).  Exposed so the
+ * threshold rule can be checked exhaustively against the argmin definition
+ * on the CPU.
+ */
+void nf4_code_thresholds(float out[15]);
+
+/* Static description of a status code. */
+const char* qlora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,188 @@
+"""GPU parity of qlora_linear_fwd / qlora_linear_bwd against the fp64 oracle.
+
+Acceptance: relative Frobenius error <= 2e-3 for Y, dX, dA, dB separately;
+bit-exact where the result is a single product (one-hot activations select a
+column of W_hat, which pins the dequantization inside the fused kernels)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dense as odense
+from oracle import native as onative
+from oracle import nf4 as onf4
+
+from gpu_util import TOL, banner, dev_bf16, dev_f32, host, host_bits, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _make(wid, proj, T, n_out, n_in, r, seed_shift=0, w_scale=None):
+    """Seeded inputs of one projection; returns host arrays and device tensors."""
+    w = synth.normal_f32(synth.seed_for(wid, proj, "W") + seed_shift, (n_out, n_in), synth.W_STD)
+    if w_scale is not None:
+        w = w * np.float32(w_scale)
+    X = synth.bf16_bits(synth.normal_f32(synth.seed_for(wid, proj, "X") + seed_shift, (T, n_in), 1.0))
+    A = synth.bf16_bits(synth.normal_f32(synth.seed_for(wid, proj, "A") + seed_shift, (r, n_in), 1.0 / n_in))
+    B = synth.bf16_bits(synth.normal_f32(synth.seed_for(wid, proj, "B") + seed_shift, (n_out, r), synth.B_STD))
+    dY = synth.bf16_bits(synth.normal_f32(synth.seed_for(wid, proj, "dY") + seed_shift, (T, n_out), 1.0))
+    return dict(w=w, X=X, A=A, B=B, dY=dY)
+
+
+def _quantize(q, w_host):
+    W = q.nf4_quantize_weight(dev_f32(w_host))
+    packed, aq, sc = onf4.quantize(w_host, nearest=onative.nearest_level)
+    w_hat = onf4.dequantize(packed, aq, sc).reshape(w_host.shape)
+    return W, w_hat
+
+
+def _fwd(q, W, h, r, alpha):
+    return q.qlora_linear_fwd(W, dev_bf16(h["X"]), dev_bf16(h["A"]), dev_bf16(h["B"]), r, alpha)
+
+
+def _bwd(q, W, h, r, alpha):
+    return q.qlora_linear_bwd(W, dev_bf16(h["X"]), dev_bf16(h["dY"]), dev_bf16(h["A"]),
+                              dev_bf16(h["B"]), r, alpha)
+
+
+def _check_fwd(Y, w_hat, h, r, alpha, what):
+    ref = odense.linear_fwd(w_hat, h["X"], h["A"], h["B"], alpha, r)
+    got = onf4.bf16_bits_to_f32(host_bits(Y)).astype(np.float64)
+    err = odense.rel_frobenius(got, ref)
+    print(f"  {what}: Y rel_frob={err:.3e}", flush=True)
+    assert err <= TOL, (what, err)
+
+
+def _check_bwd(res, w_hat, h, r, alpha, what):
+    dX, dA, dB = res
+    rdX, rdA, rdB = odense.linear_bwd(w_hat, h["X"], h["dY"], h["A"], h["B"], alpha, r)
+    e1 = odense.rel_frobenius(onf4.bf16_bits_to_f32(host_bits(dX)).astype(np.float64), rdX)
+    e2 = odense.rel_frobenius(host(dA).astype(np.float64), rdA)
+    e3 = odense.rel_frobenius(host(dB).astype(np.float64), rdB)
+    print(f"  {what}: dX={e1:.3e} dA={e2:.3e} dB={e3:.3e}", flush=True)
+    assert e1 <= TOL and e2 <= TOL and e3 <= TOL, (what, e1, e2, e3)
+
+
+# ------------------------------------------------------------------ configs
+
+def test_single_linear_256_T16_r8():
+    # single QLoRA linear: W 256x256, 16 tokens, r = 8, alpha = 16, fwd + bwd
+    q = require_gpu()
+    wl = synth.WORKLOADS[1]
+    banner("linear 256x256 T=16 r=8")
+    h = _make(1, 0, 16, 256, 256, wl.r)
+    W, w_hat = _quantize(q, h["w"])
+    _check_fwd(_fwd(q, W, h, wl.r, wl.alpha), w_hat, h, wl.r, wl.alpha, "cfg1")
+    _check_bwd(_bwd(q, W, h, wl.r, wl.alpha), w_hat, h, wl.r, wl.alpha, "cfg1")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_decode_q_proj_4096(T):
+    # decode-shaped q_proj 4096x4096, r = 16, alpha = 32, forward
+    q = require_gpu()
+    wl = synth.WORKLOADS[2]
+    banner(f"q_proj 4096x4096 fwd T={T}")
+    h = _make(2, 0, T, 4096, 4096, wl.r)
+    W, w_hat = _quantize(q, h["w"])
+    _check_fwd(_fwd(q, W, h, wl.r, wl.alpha), w_hat, h, wl.r, wl.alpha, f"q_proj T={T}")
+
+
+@pytest.mark.parametrize("T,n_out,n_in,r,alpha", [
+    (37, 320, 192, 12, 24.0),     # ragged T, r not a multiple of 8, several tiles
+    (200, 128, 512, 64, 16.0),    # ragged tail of a 128-row tile, r = 64
+    (129, 64, 64, 1, 1.0),        # smallest shapes, rank 1
+    (5, 192, 256, 256, 8.0),      # largest rank
+    (16, 512, 320, 16, 32.0),     # T at the small-token boundary
+    (17, 512, 320, 16, 32.0),     # just above it
+])
+def test_shapes_fwd_bwd(T, n_out, n_in, r, alpha):
+    q = require_gpu()
+    banner(f"shape T={T} out={n_out} in={n_in} r={r}")
+    h = _make(7, T % 10, T, n_out, n_in, r)
+    W, w_hat = _quantize(q, h["w"])
+    _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, "fwd")
+    _check_bwd(_bwd(q, W, h, r, alpha), w_hat, h, r, alpha, "bwd")
+
+
+# ------------------------------------------------------------------ exact pins
+
+@pytest.mark.parametrize("T", [3, 16, 40, 300])
+def test_one_hot_rows_select_columns_bit_exact(T):
+    # X rows one-hot (value 1) and B = 0: Y[t, :] = W_hat[:, i_t] exactly
+    q = require_gpu()
+    banner(f"one-hot fwd T={T}")
+    n_out, n_in, r = 192, 320, 8
+    h = _make(8, 1, T, n_out, n_in, r)
+    W, w_hat = _quantize(q, h["w"])
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, n_in, T)
+    X = np.zeros((T, n_in), dtype=np.uint16)
+    X[np.arange(T), idx] = 0x3F80
+    h["X"] = X
+    h["B"] = np.zeros_like(h["B"])
+    Y = host_bits(_fwd(q, W, h, r, 16.0))
+    assert np.array_equal(Y, w_hat[:, idx].T)
+
+
+@pytest.mark.parametrize("T", [4, 16, 70])
+def test_one_hot_grad_rows_select_weight_rows_bit_exact(T):
+    # dY rows one-hot and A = 0: dX[t, :] = W_hat[n_t, :] exactly; U = X A^T = 0
+    # so dB = s dY^T U = 0
+    q = require_gpu()
+    banner(f"one-hot bwd T={T}")
+    n_out, n_in, r = 192, 320, 8
+    h = _make(8, 2, T, n_out, n_in, r)
+    W, w_hat = _quantize(q, h["w"])
+    rng = np.random.default_rng(100 + T)
+    idx = rng.integers(0, n_out, T)
+    dY = np.zeros((T, n_out), dtype=np.uint16)
+    dY[np.arange(T), idx] = 0x3F80
+    h["dY"] = dY
+    h["A"] = np.zeros_like(h["A"])
+    dX, dA, dB = _bwd(q, W, h, r, 16.0)
+    assert np.array_equal(host_bits(dX), w_hat[idx, :])
+    assert np.all(host(dB) == 0)
+
+
+def test_zero_weight_isolates_lora():
+    # W = 0 (all codes 7): Y = s U B^T and dX = s V A
+    q = require_gpu()
+    banner("zero weight")
+    T, n_out, n_in, r, alpha = 48, 256, 192, 16, 32.0
+    h = _make(9, 0, T, n_out, n_in, r)
+    h["w"] = np.zeros_like(h["w"])
+    W, w_hat = _quantize(q, h["w"])
+    assert np.all(w_hat == 0)
+    _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, "W=0 fwd")
+    _check_bwd(_bwd(q, W, h, r, alpha), w_hat, h, r, alpha, "W=0 bwd")
+
+
+def test_zero_tokens():
+    q = require_gpu()
+    banner("T = 0")
+    n_out, n_in, r = 128, 128, 8
+    h = _make(9, 1, 1, n_out, n_in, r)
+    W, _ = _quantize(q, h["w"])
+    X = torch.empty(0, n_in, dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty(0, n_out, dtype=torch.bfloat16, device="cuda")
+    Y = q.qlora_linear_fwd(W, X, dev_bf16(h["A"]), dev_bf16(h["B"]), r, 16.0)
+    assert Y.shape == (0, n_out)
+    dA = torch.full((r, n_in), 7.0, device="cuda")
+    dB = torch.full((n_out, r), 7.0, device="cuda")
+    q.qlora_linear_bwd(W, X, dY, dev_bf16(h["A"]), dev_bf16(h["B"]), r, 16.0, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert torch.all(dA == 0) and torch.all(dB == 0)
+
+
+def test_gradients_overwrite_not_accumulate():
+    q = require_gpu()
+    banner("overwrite semantics")
+    T, n_out, n_in, r, alpha = 33, 128, 192, 8, 16.0
+    h = _make(9, 2, T, n_out, n_in, r)
+    W, w_hat = _quantize(q, h["w"])
+    dA = torch.full((r, n_in), 123.0, device="cuda")
+    dB = torch.full((n_out, r), -5.0, device="cuda")
+    res = q.qlora_linear_bwd(W, dev_bf16(h["X"]), dev_bf16(h["dY"]), dev_bf16(h["A"]),
+                             dev_bf16(h["B"]), r, alpha, dA=dA, dB=dB)
+    _check_bwd(res, w_hat, h, r, alpha, "overwrite")

@@ -1,0 +1,135 @@
+"""GPU parity of nf4_quantize / nf4_dequantize against the oracle: codes,
+8-bit absmax codes, group scales and the dequantized bf16 weight must match
+bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import native as onative
+from oracle import nf4 as onf4
+from oracle.codebook import nf4_levels
+
+from gpu_util import banner, dev_f32, host, host_bits, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_both(q, w_host: np.ndarray):
+    w = dev_f32(w_host)
+    codes, aq, sc = q.nf4_quantize(w)
+    torch.cuda.synchronize()
+    ref = onf4.quantize(w_host, nearest=onative.nearest_level)
+    return (host(codes), host(aq), host(sc)), ref, (codes, aq, sc)
+
+
+def _assert_bits_equal(got, ref, what):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if got.dtype == np.float32:
+        got, ref = got.view(np.uint32), ref.view(np.uint32)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}: {got[bad[:5]]} vs {ref[bad[:5]]}"
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (4096, 4096), (64,), (64 * (256 * 3 + 37),)])
+def test_quantize_dequantize_bit_exact(shape):
+    q = require_gpu()
+    banner(f"quantize/dequantize shape={shape}")
+    w_host = synth.normal_f32(11, shape, synth.W_STD)
+    (codes, aq, sc), (rc, raq, rsc), dev = _quant_both(q, w_host)
+    _assert_bits_equal(codes, rc, "codes")
+    _assert_bits_equal(aq, raq, "absmax_q")
+    _assert_bits_equal(sc, rsc, "scale")
+    n = int(np.prod(shape))
+    back = q.nf4_dequantize(*dev, n)
+    torch.cuda.synchronize()
+    _assert_bits_equal(host_bits(back), onf4.dequantize(rc, raq, rsc), "dequant")
+
+
+def test_edge_blocks():
+    # zero blocks, a zero group, tiny (subnormal) blocks, huge and exact-level values
+    q = require_gpu()
+    banner("quantize edge blocks")
+    w = synth.normal_f32(12, (64 * 256 * 4,), synth.W_STD)
+    w[0:64] = 0.0                                        # zero block
+    w[64 * 256:64 * 512] = 0.0                           # zero group
+    w[64 * 5:64 * 6] *= np.float32(1e-37)                # subnormal-range values
+    w[64 * 7:64 * 8] = np.float32(3e37) * np.sign(w[64 * 7:64 * 8])  # huge, equal magnitude
+    w[64 * 9:64 * 9 + 16] = nf4_levels() * np.float32(0.37)  # exact levels * a
+    w[64 * 9 + 16] = np.float32(0.37)
+    w[64 * 600 + 3] = -np.float32(5.0)                   # one large outlier in group 2
+    (codes, aq, sc), (rc, raq, rsc), dev = _quant_both(q, w)
+    _assert_bits_equal(codes, rc, "codes")
+    _assert_bits_equal(aq, raq, "absmax_q")
+    _assert_bits_equal(sc, rsc, "scale")
+    back = q.nf4_dequantize(*dev, w.size)
+    torch.cuda.synchronize()
+    _assert_bits_equal(host_bits(back), onf4.dequantize(rc, raq, rsc), "dequant")
+
+
+def test_tiny_absmax_block_gives_signed_zero():
+    # a block whose 8-bit absmax code rounds to 0 dequantizes to +-0 (sign of
+    # the level), bit-exactly as IEEE multiplication gives it
+    q = require_gpu()
+    banner("tiny absmax block")
+    w = synth.normal_f32(13, (64 * 256,), synth.W_STD)
+    w[0:64] *= np.float32(1e-4)
+    (codes, aq, sc), (rc, raq, rsc), dev = _quant_both(q, w)
+    assert raq[0] == 0
+    _assert_bits_equal(codes, rc, "codes")
+    back = host_bits(q.nf4_dequantize(*dev, w.size))
+    ref = onf4.dequantize(rc, raq, rsc)
+    assert np.any(ref[:64] == 0x8000)
+    _assert_bits_equal(back, ref, "dequant")
+
+
+def test_empty_is_noop():
+    q = require_gpu()
+    w = torch.empty(0, dtype=torch.float32, device="cuda")
+    c, a, s = q.nf4_quantize(w)
+    assert c.numel() == 0 and a.numel() == 0 and s.numel() == 0
+
+
+@pytest.mark.parametrize("proj", [0, 2])
+def test_mlp_weight_full_buffers(proj):
+    # 8B-MLP-shaped weights (gate 14336x4096 / down 4096x14336), full buffers
+    q = require_gpu()
+    p = synth.WORKLOADS[3].projections[proj]
+    banner(f"quantize {p.name} {p.out_features}x{p.in_features}")
+    w_host = synth.weight(3, proj, p.out_features, p.in_features)
+    (codes, aq, sc), (rc, raq, rsc), dev = _quant_both(q, w_host)
+    _assert_bits_equal(codes, rc, "codes")
+    _assert_bits_equal(aq, raq, "absmax_q")
+    _assert_bits_equal(sc, rsc, "scale")
+    back = host_bits(q.nf4_dequantize(*dev, w_host.size))
+    _assert_bits_equal(back, onf4.dequantize(rc, raq, rsc), "dequant")
+
+
+def test_flat_2pow30_sampled_groups():
+    # the 2^30-element flat quantize workload: every group is independent, so
+    # the oracle checks a sample of whole groups (first, last, and random)
+    q = require_gpu()
+    n = synth.FLAT_QUANTIZE_NUMEL
+    banner(f"quantize flat n={n}")
+    w_host = synth.normal_f32(synth.FLAT_QUANTIZE_SEED, (n,), synth.W_STD)
+    w = dev_f32(w_host)
+    codes, aq, sc = q.nf4_quantize(w)
+    back = q.nf4_dequantize(codes, aq, sc, n)
+    torch.cuda.synchronize()
+    del w
+    G = 16384
+    ng = n // G
+    rng = np.random.default_rng(0)
+    groups = sorted(set([0, 1, ng - 1] + rng.integers(0, ng, 61).tolist()))
+    codes_h, aq_h, sc_h = host(codes), host(aq), host(sc)
+    for g in groups:
+        seg = w_host[g * G:(g + 1) * G]
+        rc, raq, rsc = onf4.quantize(seg, nearest=onative.nearest_level)
+        _assert_bits_equal(codes_h[g * G // 2:(g + 1) * G // 2], rc, f"codes g={g}")
+        _assert_bits_equal(aq_h[g * 256:(g + 1) * 256], raq, f"absmax_q g={g}")
+        _assert_bits_equal(sc_h[g:g + 1], rsc, f"scale g={g}")
+        got = host_bits(back[g * G:(g + 1) * G])
+        _assert_bits_equal(got, onf4.dequantize(rc, raq, rsc), f"dequant g={g}")
