@@ -1,0 +1,305 @@
+"""Benchmark of the NF4 / QLoRA linear path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-train]
+
+Prints ONE JSON line.  Workload (the decode-shaped 8B q_proj): a 4096 x 4096
+NF4 weight (blocks of 64, absmax double-quantized in groups of 256, weights
+N(0, 0.02)), LoRA r = 16, alpha = 32, forward at 1 and at 16 tokens of
+N(0, 1) bf16 activations.  A step is one forward at T = 1 plus one at T = 16,
+each on a different weight of a pool of 64 quantized copies (554 MB, more
+than the 256 MB Infinity Cache), so every step streams its weights from HBM.
+
+value = NF4 weight-stream throughput of the step, in GB/s of algorithmic
+bytes (packed codes + 8-bit absmax + group scales + X + Y + A + B per call).
+
+Also reported ("extra"): nf4_quantize of the 4096 x 4096 fp32 weight and
+fwd+bwd TFLOP/s of the 8B-MLP gate projection (14336 x 4096, T = 4096,
+r = 64) -- the large-token half of the metric; skipped with --no-train.
+
+The roofline entry is for the dominant kernel, the fused small-token forward
+(one launch per call); its average duration comes from HIP events on the
+stream the library launches on (torch's current stream).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s and NF4 weight-stream GB/s (% of roofline)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+NF4_BYTES_PER_WEIGHT = 0.515869140625
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pool", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
+    return ap.parse_args()
+
+
+def decode_call_bytes(n_out, n_in, T, r):
+    """Algorithmic HBM bytes of one small-token forward call."""
+    weight = n_out * n_in * NF4_BYTES_PER_WEIGHT
+    return int(weight + 2 * T * (n_in + n_out) + 2 * r * (n_in + n_out))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_nf4_quantized_20_amd as q
+    import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[2]
+    proj = wl.projections[0]
+    n_out, n_in, r, alpha = proj.out_features, proj.in_features, wl.r, wl.alpha
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---------------------------------------------------------------- inputs
+    w_host = synth.weight(2, 0, n_out, n_in)
+    w_dev = torch.from_numpy(w_host).to(dev)
+    pool = [q.nf4_quantize_weight(w_dev) for _ in range(args.pool)]
+    A = bf(synth.lora_A(2, 0, r, n_in))
+    B = bf(synth.lora_B(2, 0, n_out, r))
+    X1 = bf(synth.activations(2, 0, 1, n_in))
+    X16 = bf(synth.activations(2, 0, 16, n_in))
+    Y1 = torch.empty(1, n_out, dtype=torch.bfloat16, device=dev)
+    Y16 = torch.empty(16, n_out, dtype=torch.bfloat16, device=dev)
+    ws = q.make_workspace(q.qlora_workspace_bytes(16, n_in, n_out, r, False), dev)
+    torch.cuda.synchronize()
+
+    b1 = decode_call_bytes(n_out, n_in, 1, r)
+    b16 = decode_call_bytes(n_out, n_in, 16, r)
+    P = len(pool)
+
+    def step(i):
+        q.qlora_linear_fwd(pool[(2 * i) % P], X1, A, B, r, alpha, Y=Y1, ws=ws)
+        q.qlora_linear_fwd(pool[(2 * i + 1) % P], X16, A, B, r, alpha, Y=Y16, ws=ws)
+
+    # The timed step is captured once as a HIP graph (the way a decode loop
+    # drives it: one launch per call, no host launch cost in the loop) and
+    # replayed; steps cycle through the weight pool inside the graph.
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    value = (b1 + b16) * args.steps / (ms_total * 1e-3) / 1e9
+
+    # ------------------------------------------------ dominant kernel alone
+    # the small-token forward is one kernel launch per call; its average
+    # launch duration from events around a graph of n back-to-back launches
+    def per_launch_us(X, Y, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                q.qlora_linear_fwd(pool[i % P], X, A, B, r, alpha, Y=Y, ws=ws)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def eager_us(X, Y, n):
+        for i in range(10):
+            q.qlora_linear_fwd(pool[i % P], X, A, B, r, alpha, Y=Y, ws=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            q.qlora_linear_fwd(pool[i % P], X, A, B, r, alpha, Y=Y, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    us16 = per_launch_us(X16, Y16, 400)
+    us1 = per_launch_us(X1, Y1, 400)
+    ach16 = b16 / (us16 * 1e-6) / 1e9
+
+    extra = {
+        "fwd_T1": {"us_per_call": round(us1, 3), "GB_per_s": round(b1 / (us1 * 1e-6) / 1e9, 1),
+                   "algorithmic_bytes": b1},
+        "fwd_T16": {"us_per_call": round(us16, 3), "GB_per_s": round(ach16, 1),
+                    "algorithmic_bytes": b16},
+        "eager_us_per_call": {"T1": round(eager_us(X1, Y1, 200), 2),
+                              "T16": round(eager_us(X16, Y16, 200), 2)},
+        "timing": "HIP graph replay of back-to-back calls (events on the library's stream)",
+        "weight_pool_bytes": int(P * n_out * n_in * NF4_BYTES_PER_WEIGHT),
+    }
+
+    # ------------------------------------------------------------ quantize
+    codes, aq, sc = pool[0].codes, pool[0].absmax_q, pool[0].absmax_scale
+    for _ in range(3):
+        q.nf4_quantize(w_dev, codes, aq, sc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    nq = 50
+    for _ in range(nq):
+        q.nf4_quantize(w_dev, codes, aq, sc)
+    e1.record()
+    torch.cuda.synchronize()
+    us_q = e0.elapsed_time(e1) * 1e3 / nq
+    qbytes = int(n_out * n_in * (4 + NF4_BYTES_PER_WEIGHT))
+    extra["quantize_4096x4096"] = {"us_per_call": round(us_q, 2),
+                                   "GB_per_s": round(qbytes / (us_q * 1e-6) / 1e9, 1)}
+
+    # ------------------------------------------- large-token fwd + bwd
+    if not args.no_train:
+        extra["mlp8b_gate_fwd_bwd"] = train_leg(q, synth, dev, bf)
+
+    # --------------------------------------------------------- cpu baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w_host, pool[0], n_out, n_in, r, alpha, X1, X16, A, B, b1 + b16)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": "decode-shaped 8B q_proj: NF4 W 4096x4096 (block 64, double-quant "
+                               "256), fwd at T=1 and T=16, LoRA r=16 alpha=32, 64-weight pool",
+                   "out_features": n_out, "in_features": n_in, "tokens": [1, 16], "r": r,
+                   "alpha": alpha, "weight_pool": P},
+        "roofline": {"bound": "hbm", "kernel": "k_decode_fwd (T=16)", "achieved": round(ach16, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach16 / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "wall_s_timed_region": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def train_leg(q, synth, dev, bf):
+    """fwd + bwd of the 8B-MLP gate projection (14336 x 4096, T = 4096, r = 64)."""
+    import torch
+    wl = synth.WORKLOADS[3]
+    p = wl.projections[0]
+    T, r, alpha = wl.tokens[0], wl.r, wl.alpha
+    n_out, n_in = p.out_features, p.in_features
+    w = torch.from_numpy(synth.weight(3, 0, n_out, n_in)).to(dev)
+    W = q.nf4_quantize_weight(w)
+    del w
+    X = bf(synth.activations(3, 0, T, n_in))
+    dY = bf(synth.activations(3, 0, T, n_out, "dY"))
+    A = bf(synth.lora_A(3, 0, r, n_in))
+    B = bf(synth.lora_B(3, 0, n_out, r))
+    Y = torch.empty(T, n_out, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
+    dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
+    wsf = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, False), dev)
+    wsb = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
+
+    def fwd():
+        q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=wsf)
+
+    def bwd():
+        q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX=dX, dA=dA, dB=dB, ws=wsb)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_f = timed(fwd, 10)
+    ms_b = timed(bwd, 10)
+    flop_f = 2 * T * n_in * n_out + 2 * T * r * (n_in + n_out)
+    flop_b = 2 * T * n_in * n_out + 4 * T * r * (n_in + n_out)
+    tf = (flop_f + flop_b) / ((ms_f + ms_b) * 1e-3) / 1e12
+    return {"T": T, "out": n_out, "in": n_in, "r": r, "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
+            "fwd_TFLOPs": round(flop_f / (ms_f * 1e-3) / 1e12, 1),
+            "bwd_TFLOPs": round(flop_b / (ms_b * 1e-3) / 1e12, 1),
+            "fwd_bwd_TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+def cpu_baseline(w_host, W, n_out, n_in, r, alpha, X1, X16, A, B, step_bytes):
+    """The oracle (NumPy, fp64 BLAS) doing the same step: dequantize one NF4
+    weight and run the T=1 and T=16 forwards; repeated for ~10 s."""
+    import numpy as np
+    import torch
+    from oracle import dense, nf4
+
+    def bits(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    codes = W.codes.cpu().numpy()
+    aq = W.absmax_q.cpu().numpy()
+    sc = W.absmax_scale.cpu().numpy()
+    hx1, hx16, ha, hb = bits(X1), bits(X16), bits(A), bits(B)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        w_hat = nf4.dequantize(codes, aq, sc).reshape(n_out, n_in)
+        dense.linear_fwd(w_hat, hx1, ha, hb, alpha, r)
+        w_hat = nf4.dequantize(codes, aq, sc).reshape(n_out, n_in)
+        dense.linear_fwd(w_hat, hx16, ha, hb, alpha, r)
+        n += 1
+        if time.perf_counter() - t0 > 10.0 or n >= 50:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(step_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"{n} steps (dequantize + T=1 and T=16 forward, fp64 BLAS) of the same "
+                      f"workload on one weight, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -160,10 +160,25 @@ def qlora_workspace_bytes(T: int, in_features: int, out_features: int, r: int, b
     return int(_lib.qlora_workspace_bytes(T, in_features, out_features, r, 1 if backward else 0))
 
 
+_WS_CACHE = {}
+
+
+def make_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace satisfying the library's contract (zero-filled once)."""
+    return torch.zeros(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
+
+
 def _workspace(ws, T, n_in, n_out, r, backward, device):
+    """Caller's workspace, or a cached zero-filled one per (device, stream)
+    that grows as needed (calls leave its counter region zero, so reuse is
+    valid; concurrent streams get separate buffers)."""
     need = qlora_workspace_bytes(T, n_in, n_out, r, backward)
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+        ws = _WS_CACHE.get(key)
+        if ws is None or ws.numel() < need:
+            ws = make_workspace(need, device)
+            _WS_CACHE[key] = ws
     return ws, ws.numel() * ws.element_size()
 
 

@@ -49,17 +49,20 @@ hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t*
                                             const float* scale, int64_t rows, int64_t cols,
                                             uint16_t* out, hipStream_t s);
 
-// U[t][j] = sum_k in[t][k] * P(j, k), j < r, fp32; optionally also the
-// bf16 pair u_pad[t][j] = hi, u_pad[t][rp + j] = lo with hi + lo = scale*U
-// (to bf16 precision twice over) for j < r, and 0 for r <= j < rp.
-// P(j, k) = p[j * K + k] if p_rows_are_r else p[k * r + j].
-hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* p,
-                            bool p_rows_are_r, int64_t r, float scale, float* u_out,
-                            uint16_t* u_pad, int64_t rp, hipStream_t s);
-// G(j, c) = scale * sum_t P[t][j] * Q[t][c], fp32, j < r, c < C.
-// Stored at out[j * C + c] (out_jc) or out[c * r + j].
-hipError_t launch_lora_grad(const float* P, const uint16_t* Q, int64_t T, int64_t r, int64_t C,
-                            float scale, float* out, bool out_jc, hipStream_t s);
+// sU[t][j] = scale * sum_k in[t][k] P[j][k] for j < r (P rows K-contiguous),
+// 0 for r <= j < rp, as bf16 pairs hi + lo.  Written to (either may be null)
+//   pad    [T][2*rp]   hi in columns [0, rp), lo in [rp, 2*rp)
+//   hilo_t [2*rp][ldt] transposed: hi rows [0, rp), lo rows [rp, 2*rp)
+hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* P, int64_t r,
+                            float scale, uint16_t* pad, uint16_t* hilo_t, int64_t ldt, int64_t rp,
+                            hipStream_t s);
+// out(j, c) += sum_t (Pt[j][t] + Pt[rp + j][t]) Q[t][c] for j < r, c < C (C % 64
+// == 0), atomically into out[j * C + c] (out_jc) or out[c * r + j].
+hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
+                            int64_t C, int64_t r, float* out, bool out_jc, hipStream_t s);
+// dst[c][r] = src[r][c] for src [R][C]
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
+                                 hipStream_t s);
 // dst[i][j] = dst[i][Cp + j] (R x 2Cp, bf16) = src(i, j) for j < C, else 0, where
 // src(i, j) = src[i * C + j] (!transpose) or src[j * R + i] (transpose).
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
@@ -73,5 +76,25 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
                           int64_t ldc, hipStream_t s);
+
+// Same, with the main segment's weight given as NF4 storage of W_hat [N][K0]
+// (dequantized while staged into LDS).
+hipError_t launch_gemm_nf4(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
+                           const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
+                           int64_t K0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
+                           int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);
+
+// Fused small-token forward (T <= 16, r <= 64): Y = X W_hat^T + s (X A^T) B^T
+// in one launch.  `ws` (decode_workspace_bytes) holds per-slice fp32 partials
+// and needs no initialisation; `counters` (decode_counter_count uint32) must
+// be zero when the kernel starts and are zero again when it ends.
+constexpr int64_t kDecodeMaxT = 16;
+constexpr int64_t kDecodeMaxRank = 64;
+size_t decode_workspace_bytes(int64_t in, int64_t out, int64_t r);
+int64_t decode_counter_count(int64_t out);
+hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
+                             int64_t in, int64_t out, const uint16_t* X, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                             uint16_t* Y, void* ws, uint32_t* counters, hipStream_t st);
 
 }  // namespace qlora

@@ -1,15 +1,20 @@
 // k_gemm.hip -- bf16 MFMA GEMM for gfx950 with fp32 accumulation and one
 // rounding to bf16 at the end:
 //   C[M][N] = sum_k act0[m][k] wt0[n][k]  +  sum_k act1[m][k] wt1[n][k]
+// The main segment's weight operand is either a bf16 matrix or an NF4 weight
+// (codes + double-quantized absmax) that is dequantized while it is staged
+// into LDS: each thread turns 32 or 64 packed codes of one block into bf16
+// with the block's v_perm table and writes them straight into the swizzled
+// LDS tile, so W_hat never exists in HBM (ultralytics glossary "QLoRA": the
+// frozen weight is dequantized to bfloat16 right before the matmul;
+// paperclase lesson "QLoRA", Parte 4: W_hat is built, used and discarded).
 // The second segment carries the LoRA term as extra K-steps (act1 = s*U or
-// s*V zero-padded to a multiple of 64 ranks, wt1 = B or A^T padded the same
-// way), so the base product and the adapter product share one accumulator
-// and Y / dX are rounded once (paperclase lesson "QLoRA", Parte 4: the layer
-// adds the scaled adapter output to the linear output).
+// s*V as a bf16 hi/lo pair, wt1 = B or A^T padded to match), so base and
+// adapter products share one fp32 accumulator and Y / dX are rounded once.
 //
 // Tile: BM x BN per workgroup of 4 waves (2 x 2), K-step 64, operands staged
 // through LDS with a 16-byte-chunk XOR swizzle, v_mfma_f32_32x32x16_bf16.
-// The MFMA's A operand is the weight tile (rows n), its B operand the
+// The MFMA A operand is the weight tile (rows n), its B operand the
 // activation tile (rows m), so each lane ends up holding 4 consecutive n of
 // one output row m and stores them as one 8-byte write.
 #include "common.hpp"
@@ -23,10 +28,10 @@ constexpr int kBK = 64;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)); }
 
+// bf16 rows [ROWS][64] from a K-contiguous matrix
 template <int ROWS>
-struct TileLoader {
-  // ROWS x 64 bf16 = ROWS*8 chunks of 16 B, spread over 256 threads
-  static constexpr int kPer = ROWS * 8 / 256;
+struct Bf16Loader {
+  static constexpr int kPer = ROWS * 8 / 256;  // 16-byte chunks per thread
   u32x4 v[kPer];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int64_t row0,
@@ -51,20 +56,78 @@ struct TileLoader {
   }
 };
 
+// NF4 rows [ROWS][64]: one 64-weight block per row per K-step.  256/ROWS
+// threads share a row; each loads its share of the 32 code bytes plus the
+// block's 8-bit absmax and group scale, and expands them at store time.
+template <int ROWS>
+struct Nf4Loader {
+  static constexpr int kTPR = 256 / ROWS;  // threads per row
+  static constexpr int kDw = 8 / kTPR;     // code dwords (8 weights each) per thread
+  static_assert(kTPR == 1 || kTPR == 2, "ROWS must be 128 or 256");
+  uint32_t cw[kDw];
+  uint32_t q;
+  float sg;
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ codes,
+                                       const uint8_t* __restrict__ absmax_q,
+                                       const float* __restrict__ scale, int64_t in, int64_t row0,
+                                       int64_t nrows, int64_t k0, int tid) {
+    const int row = tid / kTPR, part = tid % kTPR;
+    const int64_t grow = row0 + row;
+    if (grow < nrows) {
+      const int64_t e = grow * in + k0;  // first weight of the block
+      const u32x4* src = reinterpret_cast<const u32x4*>(codes + (e >> 1) + part * kDw * 4);
+#pragma unroll
+      for (int i = 0; i < kDw / 4; ++i) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        cw[4 * i + 0] = v[0]; cw[4 * i + 1] = v[1]; cw[4 * i + 2] = v[2]; cw[4 * i + 3] = v[3];
+      }
+      const int64_t bi = e >> 6;
+      q = absmax_q[bi];
+      sg = scale[bi >> 8];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDw; ++i) cw[i] = 0u;
+      q = 0u;
+      sg = 0.f;
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+    const int row = tid / kTPR, part = tid % kTPR;
+    const Nf4Table tab = make_table(dq_absmax(q, sg));
+#pragma unroll
+    for (int d = 0; d < kDw; ++d) {
+      uint32_t o[4];
+      lookup8(tab, cw[d], o);
+      const int chunk = part * kDw + d;
+      *reinterpret_cast<u32x4*>(lds + row * kBK + swz(row, chunk) * 8) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+};
+
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chunk) {
   const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kBK + swz(row, chunk) * 8);
   return __builtin_bit_cast(bf16x8, v);
 }
 
+struct GemmArgs {
+  int64_t M, N;
+  // main segment activation and weight (bf16 weight, or NF4 when codes != nullptr)
+  const uint16_t* act0; int64_t lda0;
+  const uint16_t* wt0; int64_t ldw0;
+  const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
+  int64_t K0;
+  // LoRA extension segment
+  const uint16_t* act1; int64_t lda1;
+  const uint16_t* wt1; int64_t ldw1;
+  int64_t K1;
+  uint16_t* C; int64_t ldc;
+};
+
 }  // namespace
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_gemm_nt(int64_t M, int64_t N, const uint16_t* __restrict__ act0,
-                                                 int64_t lda0, const uint16_t* __restrict__ wt0,
-                                                 int64_t ldw0, int64_t K0,
-                                                 const uint16_t* __restrict__ act1, int64_t lda1,
-                                                 const uint16_t* __restrict__ wt1, int64_t ldw1,
-                                                 int64_t K1, uint16_t* __restrict__ C, int64_t ldc) {
+template <int BM, int BN, bool kNf4>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   __shared__ __attribute__((aligned(16))) uint16_t s_act[BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t s_wt[BN * kBK];
@@ -83,24 +146,34 @@ __global__ __launch_bounds__(256) void k_gemm_nt(int64_t M, int64_t N, const uin
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  const int64_t s0 = K0 / kBK, steps = s0 + K1 / kBK;
-  TileLoader<BM> la;
-  TileLoader<BN> lw;
+  const int64_t s0 = p.K0 / kBK, steps = s0 + p.K1 / kBK;
+  Bf16Loader<BM> la;
+  Bf16Loader<BN> lw;
+  Nf4Loader<BN> lq;
   auto fetch = [&](int64_t st) {
     if (st < s0) {
-      la.load(act0, lda0, m0, M, st * kBK, tid);
-      lw.load(wt0, ldw0, n0, N, st * kBK, tid);
+      la.load(p.act0, p.lda0, m0, p.M, st * kBK, tid);
+      if constexpr (kNf4)
+        lq.load(p.codes, p.absmax_q, p.scale, p.K0, n0, p.N, st * kBK, tid);
+      else
+        lw.load(p.wt0, p.ldw0, n0, p.N, st * kBK, tid);
     } else {
-      la.load(act1, lda1, m0, M, (st - s0) * kBK, tid);
-      lw.load(wt1, ldw1, n0, N, (st - s0) * kBK, tid);
+      la.load(p.act1, p.lda1, m0, p.M, (st - s0) * kBK, tid);
+      lw.load(p.wt1, p.ldw1, n0, p.N, (st - s0) * kBK, tid);
     }
+  };
+  auto stash = [&](int64_t st) {
+    la.store(s_act, tid);
+    if constexpr (kNf4) {
+      if (st < s0) { lq.store(s_wt, tid); return; }
+    }
+    lw.store(s_wt, tid);
   };
 
   if (steps > 0) fetch(0);
   for (int64_t st = 0; st < steps; ++st) {
     __syncthreads();
-    la.store(s_act, tid);
-    lw.store(s_wt, tid);
+    stash(st);
     __syncthreads();
     if (st + 1 < steps) fetch(st + 1);
 #pragma unroll
@@ -123,31 +196,54 @@ __global__ __launch_bounds__(256) void k_gemm_nt(int64_t M, int64_t N, const uin
 #pragma unroll
   for (int b = 0; b < FM; ++b) {
     const int64_t m = m0 + wm * WM + b * 32 + r32;
-    if (m >= M) continue;
+    if (m >= p.M) continue;
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t n = n0 + wn * WN + a * 32 + 8 * g + 4 * half;
-        if (n < N) {
+        if (n < p.N) {
           const uint32_t p0 = pack_bf16x2(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1]);
           const uint32_t p1 = pack_bf16x2(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(C + m * ldc + n) = u32x2{p0, p1};
+          *reinterpret_cast<u32x2*>(p.C + m * p.ldc + n) = u32x2{p0, p1};
         }
       }
     }
   }
 }
 
+namespace {
+template <bool kNf4>
+hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
+  // 256 x 256 tiles when they give at least one full wave of workgroups
+  const int64_t big = ceil_div(a.M, 256) * ceil_div(a.N, 256);
+  if (big >= 256) {
+    dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 256)), static_cast<uint32_t>(ceil_div(a.N, 256)));
+    hipLaunchKernelGGL((k_gemm<256, 256, kNf4>), grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 128)), static_cast<uint32_t>(ceil_div(a.N, 128)));
+    hipLaunchKernelGGL((k_gemm<128, 128, kNf4>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
                           int64_t ldc, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
-  dim3 grid(static_cast<uint32_t>(ceil_div(M, BM)), static_cast<uint32_t>(ceil_div(N, BN)));
-  hipLaunchKernelGGL((k_gemm_nt<BM, BN>), grid, dim3(256), 0, s, M, N, act0, lda0, wt0, ldw0, K0,
-                     act1, lda1, wt1, ldw1, K1, C, ldc);
-  return hipGetLastError();
+  GemmArgs a{M, N, act0, lda0, wt0, ldw0, nullptr, nullptr, nullptr, K0,
+             act1, lda1, wt1, ldw1, K1, C, ldc};
+  return launch_tiles<false>(a, s);
+}
+
+hipError_t launch_gemm_nf4(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
+                           const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
+                           int64_t K0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
+                           int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s) {
+  GemmArgs a{M, N, act0, lda0, nullptr, 0, codes, absmax_q, scale, K0,
+             act1, lda1, wt1, ldw1, K1, C, ldc};
+  return launch_tiles<true>(a, s);
 }
 
 }  // namespace qlora

@@ -40,8 +40,14 @@ int launched(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNC
 // ---------------------------------------------------------------------------
 // Workspace layout.  Segments are 256-byte aligned.
 // ---------------------------------------------------------------------------
+// Every layout starts with the same counter region (split-K tickets of the
+// small-token forward).  It must be zero when a call starts; every call
+// leaves it zero, and no other segment overlaps it, so a workspace that was
+// zero-filled once can serve any sequence of calls.
+constexpr size_t kCounterRegion = 4096;
+
 struct Carve {
-  size_t off = 0;
+  size_t off = kCounterRegion;
   size_t take(size_t bytes) {
     const size_t at = off;
     off += (bytes + 255) & ~static_cast<size_t>(255);
@@ -50,32 +56,41 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t u_pad, b_pad, w_dq, total;
+  size_t counters, partials, u_pad, b_pad, total;
 };
 struct BwdLayout {
-  size_t u, v, v_pad, a_t_pad, w_dq_t, total;
+  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, total;
 };
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
 
+bool fwd_uses_decode(int64_t T, int64_t r) { return T <= kDecodeMaxT && r <= kDecodeMaxRank; }
+
 FwdLayout fwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
-  const int64_t rp = padded_rank(r);
+  FwdLayout l{0, 0, 0, 0, 0};
   Carve c;
-  FwdLayout l;
+  if (fwd_uses_decode(T, r)) {  // split-K partials of the fused small-token kernel
+    l.partials = c.take(decode_workspace_bytes(in, out, r));
+    l.total = c.off;
+    return l;
+  }
+  const int64_t rp = padded_rank(r);
   l.u_pad = c.take(static_cast<size_t>(T * rp * 4));
   l.b_pad = c.take(static_cast<size_t>(out * rp * 4));
-  l.w_dq = c.take(static_cast<size_t>(out * in * 2));
   l.total = c.off;
   return l;
 }
+
+int64_t token_pitch(int64_t T) { return round_up(T, 8); }
 
 BwdLayout bwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
   const int64_t rp = padded_rank(r);
   Carve c;
   BwdLayout l;
-  l.u = c.take(static_cast<size_t>(T * r * 4));
-  l.v = c.take(static_cast<size_t>(T * r * 4));
+  l.ut = c.take(static_cast<size_t>(2 * rp * token_pitch(T) * 2));
+  l.vt = c.take(static_cast<size_t>(2 * rp * token_pitch(T) * 2));
   l.v_pad = c.take(static_cast<size_t>(T * rp * 4));
+  l.b_t = c.take(static_cast<size_t>(r * out * 2));
   l.a_t_pad = c.take(static_cast<size_t>(in * rp * 4));
   l.w_dq_t = c.take(static_cast<size_t>(in * out * 2));
   l.total = c.off;
@@ -84,6 +99,7 @@ BwdLayout bwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
 
 bool linear_shapes_ok(int64_t T, int64_t in, int64_t out, int64_t r) {
   if (T < 0 || in < 64 || out < 64 || (in % 64) != 0 || (out % 64) != 0) return false;
+  if (decode_counter_count(out) * 4 > static_cast<int64_t>(kCounterRegion)) return false;
   if (r < 1 || r > QLORA_MAX_RANK) return false;
   if (in > (int64_t(1) << 31) || out > (int64_t(1) << 31) || T > (int64_t(1) << 31)) return false;
   return true;
@@ -155,23 +171,26 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
   if (T == 0) return QLORA_OK;
   const FwdLayout lay = fwd_layout(T, in, out, r);
-  if (ws == nullptr || ws_bytes < lay.total) return QLORA_ERR_WORKSPACE;
+  if (lay.total > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = alpha / static_cast<float>(r);
+  if (fwd_uses_decode(T, r))
+    return launched(launch_decode_fwd(W->codes, W->absmax_q, W->absmax_scale, in, out, X, T, A, B,
+                                      r, scale, Y, static_cast<uint8_t*>(ws) + lay.partials,
+                                      static_cast<uint32_t*>(ws), s));
+
   const int64_t rp = padded_rank(r);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* u_pad = reinterpret_cast<uint16_t*>(base + lay.u_pad);
   uint16_t* b_pad = reinterpret_cast<uint16_t*>(base + lay.b_pad);
-  uint16_t* w_dq = reinterpret_cast<uint16_t*>(base + lay.w_dq);
-
-  hipError_t e = launch_lora_down(X, T, in, A, true, r, scale, nullptr, u_pad, rp, s);
+  hipError_t e = launch_lora_down(X, T, in, A, r, scale, u_pad, nullptr, 0, rp, s);  // s X A^T
   if (e == hipSuccess) e = launch_pad_bf16(B, out, r, false, b_pad, rp, s);
-  if (e == hipSuccess) e = launch_nf4_dequantize(W->codes, W->absmax_q, W->absmax_scale, out * in, w_dq, s);
   if (e == hipSuccess)
-    e = launch_gemm_nt(T, out, X, in, w_dq, in, in, u_pad, 2 * rp, b_pad, 2 * rp, 2 * rp, Y, out, s);
+    e = launch_gemm_nf4(T, out, X, in, W->codes, W->absmax_q, W->absmax_scale, in, u_pad, 2 * rp,
+                        b_pad, 2 * rp, 2 * rp, Y, out, s);
   return launched(e);
 }
 
@@ -199,23 +218,25 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora
   if (T == 0 || e != hipSuccess) return launched(e);
 
   const float scale = alpha / static_cast<float>(r);
-  const int64_t rp = padded_rank(r);
+  const int64_t rp = padded_rank(r), tp = token_pitch(T);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  float* U = reinterpret_cast<float*>(base + lay.u);
-  float* V = reinterpret_cast<float*>(base + lay.v);
+  uint16_t* ut = reinterpret_cast<uint16_t*>(base + lay.ut);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(base + lay.vt);
   uint16_t* v_pad = reinterpret_cast<uint16_t*>(base + lay.v_pad);
+  uint16_t* b_t = reinterpret_cast<uint16_t*>(base + lay.b_t);
   uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(base + lay.a_t_pad);
   uint16_t* w_dq_t = reinterpret_cast<uint16_t*>(base + lay.w_dq_t);
 
-  e = launch_lora_down(X, T, in, A, true, r, scale, U, nullptr, rp, s);                // U = X A^T
-  if (e == hipSuccess) e = launch_lora_down(dY, T, out, B, false, r, scale, V, v_pad, rp, s);  // V = dY B
-  if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, s);             // A^T padded
+  e = launch_lora_down(X, T, in, A, r, scale, nullptr, ut, tp, rp, s);                 // (sU)^T
+  if (e == hipSuccess) e = launch_transpose_bf16(B, out, r, b_t, s);                  // B^T [r][out]
+  if (e == hipSuccess) e = launch_lora_down(dY, T, out, b_t, r, scale, v_pad, vt, tp, rp, s);  // sV
+  if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, s);           // A^T padded
   if (e == hipSuccess)
     e = launch_nf4_dequantize_transposed(W->codes, W->absmax_q, W->absmax_scale, out, in, w_dq_t, s);
   if (e == hipSuccess)
     e = launch_gemm_nt(T, in, dY, out, w_dq_t, out, out, v_pad, 2 * rp, a_t_pad, 2 * rp, 2 * rp, dX, in, s);
-  if (e == hipSuccess) e = launch_lora_grad(V, X, T, r, in, scale, dA, true, s);   // dA = s V^T X
-  if (e == hipSuccess) e = launch_lora_grad(U, dY, T, r, out, scale, dB, false, s);  // dB = s dY^T U
+  if (e == hipSuccess) e = launch_lora_grad(vt, T, tp, rp, X, in, r, dA, true, s);    // dA = (sV)^T X
+  if (e == hipSuccess) e = launch_lora_grad(ut, T, tp, rp, dY, out, r, dB, false, s); // dB = dY^T (sU)
   return launched(e);
 }
 

@@ -154,10 +154,14 @@ def test_linear_validation():
     lib = _api(_lib())
     F = _FAKE
     W = _W(F, F, F, 128, 256)
-    ws = lib.qlora_workspace_bytes(16, 256, 128, 8, 0)
+    # both forward paths (small-token split-K partials, large-token LoRA
+    # factors) use the workspace
+    assert lib.qlora_workspace_bytes(16, 256, 128, 8, 0) > 0
+    assert lib.qlora_workspace_bytes(16, 256, 128, 65, 0) > 0
+    ws = lib.qlora_workspace_bytes(32, 256, 128, 8, 0)
     wsb = lib.qlora_workspace_bytes(16, 256, 128, 8, 1)
     assert ws > 0 and wsb > 0
-    fwd = lambda **k: lib.qlora_linear_fwd(ctypes.byref(k.get("W", W)), k.get("X", F), k.get("T", 16),
+    fwd = lambda **k: lib.qlora_linear_fwd(ctypes.byref(k.get("W", W)), k.get("X", F), k.get("T", 32),
                                            F, F, k.get("r", 8), k.get("alpha", 16.0), k.get("Y", F),
                                            k.get("ws", F), k.get("wsb", ws), None)
     assert fwd(W=_W(F, F, F, 128, 100)) == -2      # in % 64

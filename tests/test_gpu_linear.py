@@ -95,6 +95,9 @@ def test_decode_q_proj_4096(T):
     (5, 192, 256, 256, 8.0),      # largest rank
     (16, 512, 320, 16, 32.0),     # T at the small-token boundary
     (17, 512, 320, 16, 32.0),     # just above it
+    (2, 256, 192, 24, 48.0),      # small-token path, two rank tiles
+    (9, 128, 448, 40, 10.0),      # small-token path, four rank tiles, K not a multiple of 256
+    (1, 64, 64, 64, 64.0),        # small-token path, largest rank it takes
 ])
 def test_shapes_fwd_bwd(T, n_out, n_in, r, alpha):
     q = require_gpu()
@@ -186,3 +189,66 @@ def test_gradients_overwrite_not_accumulate():
     res = q.qlora_linear_bwd(W, dev_bf16(h["X"]), dev_bf16(h["dY"]), dev_bf16(h["A"]),
                              dev_bf16(h["B"]), r, alpha, dA=dA, dB=dB)
     _check_bwd(res, w_hat, h, r, alpha, "overwrite")
+
+
+def test_small_token_forward_under_graph_replay():
+    # The small-token forward reduces its split-K partials with per-call
+    # (epoch, count) counters in the workspace.  A captured graph repeats its
+    # epoch on every replay; eager calls on the same workspace in between use
+    # fresh epochs.  Every replay must equal the eager result bit for bit.
+    q = require_gpu()
+    banner("graph replay of the small-token forward")
+    n_out, n_in, r, alpha = 512, 768, 16, 32.0
+    hs = [_make(10, p, T, n_out, n_in, r) for p, T in ((0, 1), (1, 16), (2, 7))]
+    W, w_hat = _quantize(q, hs[0]["w"])
+    ins = [(dev_bf16(h["X"]), dev_bf16(h["A"]), dev_bf16(h["B"])) for h in hs]
+    ws = q.make_workspace(max(q.qlora_workspace_bytes(T, n_in, n_out, r, False) for T in (1, 7, 16)),
+                          "cuda")
+    outs = [torch.empty(X.shape[0], n_out, dtype=torch.bfloat16, device="cuda") for X, _, _ in ins]
+    eager = []
+    for (X, A, B), Y in zip(ins, outs):
+        eager.append(host_bits(q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=ws)).copy())
+    for h, ref_bits in zip(hs, eager):
+        ref = odense.linear_fwd(w_hat, h["X"], h["A"], h["B"], alpha, r)
+        assert odense.rel_frobenius(onf4.bf16_bits_to_f32(ref_bits), ref) <= TOL
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (X, A, B), Y in zip(ins, outs):
+            q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=ws)
+    for rep in range(4):
+        for Y in outs:
+            Y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, Y in enumerate(outs):
+            assert np.array_equal(host_bits(Y), eager[i]), (rep, i)
+        # eager work on the same workspace between replays
+        scratch = torch.empty_like(outs[1])
+        X, A, B = ins[1]
+        q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=scratch, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(scratch), eager[1])
+
+
+def test_workspace_counters_return_to_zero():
+    # the contract: a call leaves the first 4096 bytes of its workspace zero,
+    # whichever path it takes, and one zero-filled workspace serves a mix of
+    # small- and large-token forwards and backwards
+    q = require_gpu()
+    banner("workspace counter region")
+    n_out, n_in, r, alpha = 384, 512, 16, 32.0
+    hs = {T: _make(11, T % 7, T, n_out, n_in, r) for T in (3, 16, 40)}
+    W, w_hat = _quantize(q, hs[3]["w"])
+    need = max(q.qlora_workspace_bytes(T, n_in, n_out, r, b) for T in hs for b in (False, True))
+    ws = q.make_workspace(need, "cuda")
+    for rep in range(2):
+        for T, h in hs.items():
+            Y = q.qlora_linear_fwd(W, dev_bf16(h["X"]), dev_bf16(h["A"]), dev_bf16(h["B"]), r, alpha, ws=ws)
+            _check_fwd(Y, w_hat, h, r, alpha, f"T={T} rep={rep}")
+            res = q.qlora_linear_bwd(W, dev_bf16(h["X"]), dev_bf16(h["dY"]), dev_bf16(h["A"]),
+                                     dev_bf16(h["B"]), r, alpha, ws=ws)
+            _check_bwd(res, w_hat, h, r, alpha, f"T={T} rep={rep}")
+            torch.cuda.synchronize()
+            assert int(ws[:4096].count_nonzero()) == 0
