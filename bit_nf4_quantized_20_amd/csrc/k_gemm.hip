@@ -26,19 +26,37 @@ namespace {
 
 constexpr int kBK = 64;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)); }
+// 16-byte chunk swizzle of a 128-byte LDS row.  A fragment read has 32
+// lanes on 32 consecutive rows at one chunk; the key (row & 7) ^ (row >> 3 & 1)
+// gives every 8 consecutive rows distinct chunks (32-bank view) and every 16
+// consecutive rows distinct (row parity, chunk) pairs (64-bank view), so the
+// reads are conflict-free either way.  Writes cover whole rows, so any
+// per-row permutation is conflict-free for them.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+}
 
-// bf16 rows [ROWS][64] from a K-contiguous matrix
-template <int ROWS>
+// bf16 rows [ROWS][64] from a K-contiguous matrix, staged through registers
+// by NT threads
+template <int ROWS, int NT>
 struct Bf16Loader {
-  static constexpr int kPer = ROWS * 8 / 256;  // 16-byte chunks per thread
+  static constexpr int kPer = ROWS * 8 / NT;  // 16-byte chunks per thread
   u32x4 v[kPer];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int64_t row0,
                                        int64_t nrows, int64_t k0, int tid) {
+    if (row0 + ROWS <= nrows) {  // whole tile in range (uniform): no per-row branches
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int id = tid + NT * i;
+        const int row = id >> 3, q = id & 7;
+        v[i] = *reinterpret_cast<const u32x4*>(src + (row0 + row) * ld + k0 + q * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int id = tid + 256 * i;
+      const int id = tid + NT * i;
       const int row = id >> 3, q = id & 7;
       if (row0 + row < nrows)
         v[i] = *reinterpret_cast<const u32x4*>(src + (row0 + row) * ld + k0 + q * 8);
@@ -49,21 +67,21 @@ struct Bf16Loader {
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int id = tid + 256 * i;
+      const int id = tid + NT * i;
       const int row = id >> 3, q = id & 7;
       *reinterpret_cast<u32x4*>(lds + row * kBK + swz(row, q) * 8) = v[i];
     }
   }
 };
 
-// NF4 rows [ROWS][64]: one 64-weight block per row per K-step.  256/ROWS
+// NF4 rows [ROWS][64]: one 64-weight block per row per K-step.  NT/ROWS
 // threads share a row; each loads its share of the 32 code bytes plus the
 // block's 8-bit absmax and group scale, and expands them at store time.
-template <int ROWS>
+template <int ROWS, int NT>
 struct Nf4Loader {
-  static constexpr int kTPR = 256 / ROWS;  // threads per row
+  static constexpr int kTPR = NT / ROWS;   // threads per row
   static constexpr int kDw = 8 / kTPR;     // code dwords (8 weights each) per thread
-  static_assert(kTPR == 1 || kTPR == 2, "ROWS must be 128 or 256");
+  static_assert(kTPR == 1 || kTPR == 2 || kTPR == 4, "unsupported tile");
   uint32_t cw[kDw];
   uint32_t q;
   float sg;
@@ -76,11 +94,16 @@ struct Nf4Loader {
     const int64_t grow = row0 + row;
     if (grow < nrows) {
       const int64_t e = grow * in + k0;  // first weight of the block
-      const u32x4* src = reinterpret_cast<const u32x4*>(codes + (e >> 1) + part * kDw * 4);
+      const uint8_t* src = codes + (e >> 1) + part * kDw * 4;
+      if constexpr (kDw >= 4) {
 #pragma unroll
-      for (int i = 0; i < kDw / 4; ++i) {
-        const u32x4 v = __builtin_nontemporal_load(src + i);
-        cw[4 * i + 0] = v[0]; cw[4 * i + 1] = v[1]; cw[4 * i + 2] = v[2]; cw[4 * i + 3] = v[3];
+        for (int i = 0; i < kDw / 4; ++i) {
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
+          cw[4 * i + 0] = v[0]; cw[4 * i + 1] = v[1]; cw[4 * i + 2] = v[2]; cw[4 * i + 3] = v[3];
+        }
+      } else {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+        cw[0] = v[0]; cw[1] = v[1];
       }
       const int64_t bi = e >> 6;
       q = absmax_q[bi];
@@ -110,6 +133,27 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chu
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
+// XCDs (linear id % 8), and each XCD has its own L2.  The tiles are renumbered
+// so that XCD x runs a contiguous stretch of the tile sequence, and the
+// sequence walks groups of 8 M-tiles column by column, so the ~32 workgroups an
+// XCD runs at once cover a compact block of C and share A and B panels in
+// that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void xcd_tile(int64_t gm, int64_t gn, int64_t& mt, int64_t& nt) {
+  const int64_t total = gm * gn;
+  const int64_t lin = static_cast<int64_t>(blockIdx.y) * gm + blockIdx.x;
+  int64_t t = lin;
+  if (total % kXcds == 0) t = (lin % kXcds) * (total / kXcds) + lin / kXcds;
+  const int64_t per_group = kGroupM * gn;
+  const int64_t g = t / per_group;
+  const int64_t gm_g = (gm - g * kGroupM) < kGroupM ? (gm - g * kGroupM) : kGroupM;
+  const int64_t in_g = t - g * per_group;
+  mt = g * kGroupM + in_g % gm_g;
+  nt = in_g / gm_g;
+}
+
 struct GemmArgs {
   int64_t M, N;
   // main segment activation and weight (bf16 weight, or NF4 when codes != nullptr)
@@ -126,16 +170,24 @@ struct GemmArgs {
 
 }  // namespace
 
-template <int BM, int BN, bool kNf4>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t s_act[BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_wt[BN * kBK];
+// WAVES_M x WAVES_N waves; each wave computes a (BM/WAVES_M) x (BN/WAVES_N)
+// sub-tile.  With 8 waves two share each SIMD, so one wave's loads and LDS
+// traffic overlap the other's MFMAs.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kNf4>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / 32, FN = WN / 32;
+  // two LDS stages: while the waves compute on one, the next tile is written
+  // into the other, so each K-step needs a single barrier
+  __shared__ __attribute__((aligned(16))) uint16_t s_act[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_wt[2][BN * kBK];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  const int wm = wv % WAVES_M, wn = wv / WAVES_M;
+  int64_t mt, nt;
+  xcd_tile(gridDim.x, gridDim.y, mt, nt);
+  const int64_t m0 = mt * BM;
+  const int64_t n0 = nt * BN;
   const int r32 = lane & 31, half = lane >> 5;
 
   f32x16 acc[FN][FM];
@@ -147,9 +199,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
   const int64_t s0 = p.K0 / kBK, steps = s0 + p.K1 / kBK;
-  Bf16Loader<BM> la;
-  Bf16Loader<BN> lw;
-  Nf4Loader<BN> lq;
+  Bf16Loader<BM, NT> la;
+  Bf16Loader<BN, NT> lw;
+  Nf4Loader<BN, NT> lq;
   auto fetch = [&](int64_t st) {
     if (st < s0) {
       la.load(p.act0, p.lda0, m0, p.M, st * kBK, tid);
@@ -162,28 +214,36 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       lw.load(p.wt1, p.ldw1, n0, p.N, (st - s0) * kBK, tid);
     }
   };
-  auto stash = [&](int64_t st) {
-    la.store(s_act, tid);
+  auto stash = [&](int64_t st, int buf) {
+    la.store(s_act[buf], tid);
     if constexpr (kNf4) {
-      if (st < s0) { lq.store(s_wt, tid); return; }
+      if (st < s0) { lq.store(s_wt[buf], tid); return; }
     }
-    lw.store(s_wt, tid);
+    lw.store(s_wt[buf], tid);
   };
 
-  if (steps > 0) fetch(0);
+  if (steps > 0) {
+    fetch(0);
+    stash(0, 0);
+    if (steps > 1) fetch(1);
+  }
   for (int64_t st = 0; st < steps; ++st) {
-    __syncthreads();
-    stash(st);
-    __syncthreads();
-    if (st + 1 < steps) fetch(st + 1);
+    const int buf = static_cast<int>(st & 1);
+    __syncthreads();  // stage buf complete; stage buf^1 free
+    if (st + 1 < steps) {
+      stash(st + 1, buf ^ 1);
+      if (st + 2 < steps) fetch(st + 2);
+    }
+    const uint16_t* sa = s_act[buf];
+    const uint16_t* sw = s_wt[buf];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int chunk = 2 * j + half;
       bf16x8 fw[FN], fa[FM];
 #pragma unroll
-      for (int a = 0; a < FN; ++a) fw[a] = lds_frag(s_wt, wn * WN + a * 32 + r32, chunk);
+      for (int a = 0; a < FN; ++a) fw[a] = lds_frag(sw, wn * WN + a * 32 + r32, chunk);
 #pragma unroll
-      for (int b = 0; b < FM; ++b) fa[b] = lds_frag(s_act, wm * WM + b * 32 + r32, chunk);
+      for (int b = 0; b < FM; ++b) fa[b] = lds_frag(sa, wm * WM + b * 32 + r32, chunk);
 #pragma unroll
       for (int a = 0; a < FN; ++a)
 #pragma unroll
@@ -215,14 +275,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
 namespace {
 template <bool kNf4>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
-  // 256 x 256 tiles when they give at least one full wave of workgroups
+  // 256 x 256 tiles (8 waves) when they give at least one full wave of
+  // workgroups, else 128 x 128 (4 waves)
   const int64_t big = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   if (big >= 256) {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 256)), static_cast<uint32_t>(ceil_div(a.N, 256)));
-    hipLaunchKernelGGL((k_gemm<256, 256, kNf4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<256, 256, 2, 4, kNf4>), grid, dim3(512), 0, s, a);
   } else {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 128)), static_cast<uint32_t>(ceil_div(a.N, 128)));
-    hipLaunchKernelGGL((k_gemm<128, 128, kNf4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<128, 128, 2, 2, kNf4>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
