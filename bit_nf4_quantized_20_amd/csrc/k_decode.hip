@@ -1,272 +1,301 @@
 // k_decode.hip -- fused QLoRA linear forward for small token counts
-// (T <= 16), HBM-bound on the packed-nibble weight stream.
+// (T <= 16, r <= 64), bound by the packed-nibble weight stream.
 //
 //   Y = X W_hat^T + s (X A^T) B^T     (paperclase lesson "QLoRA", Parte 4)
 //
-// Decomposition.  Workgroup (g, k) owns R = 128 output rows (8 tiles of 16)
-// and one K slice of whole 256-wide units; the slices of a row group are
-// spread over workgroups so the grid fills the chip while each workgroup
-// reads only its slice of X and A (the activation traffic is what limits a
-// small-token GEMV, not the 0.52 B/weight of codes).  Because the LoRA term
-// is linear in U = X A^T, each slice adds s * U_slice B^T to its own partial,
-// and the row group's result is the sum of its slices' partials.
+// Decomposition.  Workgroup b owns the 16 output rows [16b, 16b + 16) over
+// the whole reduction dimension, so its part of Y is finished inside the
+// workgroup: no partial sums and no synchronisation cross workgroups, and the
+// kernel needs no workspace.  With out = 4096 the grid is 256 workgroups, one
+// per CU, each streaming 16 rows x in of codes.  Every workgroup computes the
+// small U = X A^T itself from X and A, which stay resident in L2.
 //
-// Inside a workgroup: the X slice [T][KS] and A slice [r][KS] are staged in
-// LDS once, already in MFMA-fragment order.  Wave w owns row tile w; in unit
-// u its lane (n = l%16, g = l/16) owns block 4u+g of row n: 32 code bytes, the
-// block's 16-entry bf16 table, then 8 dwords of codes through the v_perm
-// lookup straight into the A operand of v_mfma_f32_16x16x32_bf16 (16 rows x
-// 16 tokens x 32 k) with the activation fragment as B operand.  Waves
-// 0..units-1 also compute the unit's U partial (A rows as MFMA A operand).
+// Eight waves split the 64-weight blocks of the 16 rows into contiguous
+// ranges, walked in chunks of four blocks (256 k).  In a chunk, lane
+// (n = l%16, g = l/16) owns block 4c+g of row n: 32 code bytes, the block's
+// 16-entry bf16 table, then 8 dwords of codes through the v_perm lookup into
+// the A operand of v_mfma_f32_16x16x32_bf16 (16 rows x 16 tokens x 32 k).
+// The B operand is token n's matching 8 activations.  The same activation
+// fragments also meet A's rows in a second MFMA (16 ranks x 16 tokens),
+// which accumulates this wave's share of U.
 //
-// Cross-workgroup reduction, deterministic: each workgroup stores its fp32
-// partial [T][R] to the workspace slot of its slice (device-coherent stores),
-// then takes a ticket from the row group's counter with one fetch-add.  The
-// workgroup holding the last ticket sums the slices in slice order, rounds to
-// bf16 once, writes Y and returns the counter to zero, so the counter region
-// must be zero when a call starts and is zero again when it ends.
+// Activations and A rows are 16 rows at a large stride; loading MFMA
+// fragments straight from memory puts 16 rows at one offset into every
+// instruction, which the memory pipeline serves several times slower than
+// contiguous requests.  So each wave loads its chunk of X (T tokens x 512 B)
+// and of A (16 ranks x 512 B) contiguously, two rows per instruction, into
+// a private LDS tile, then reads the fragments back.  The tile stores piece
+// p (16 B) of row t at slot 32 t + (p ^ t): writes are contiguous and the
+// fragment reads of 16 rows fall on 16 distinct 4-bank groups.  Rank tiles
+// beyond the first reuse the same A tile in turn (a wave's LDS operations run
+// in order).  For r <= 16 two chunks' global loads (codes, X, A) are in
+// flight at a time.
+//
+// Epilogue: the eight waves' fp32 accumulators of the base product and of U
+// meet in LDS; Y = base + s U B^T is rounded to bf16 once.
 #include "common.hpp"
 #include "nf4_format.hpp"
 
 namespace qlora {
 
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-
 namespace {
 constexpr int kWaves = 8;
-constexpr int kR = 128;           // rows per row group (8 tiles of 16)
-// 256-wide units per slice, bounded so the staged A fragments fit in LDS
-constexpr int max_ups(int rt) { return rt <= 1 ? 4 : (rt == 2 ? 2 : 1); }
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 16;
+constexpr int kTileSlots = 16 * 32;  // 16 rows x 32 pieces of 16 B (8 KB)
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+constexpr int kStream = 2;               // cache policy nt: streamed once
+constexpr uint32_t kPastEnd = 0x80000000u;  // past every buffer (all < 2^31 bytes)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-struct DecodeGeom {
-  int64_t units;      // ceil(in / 256)
-  int ups;            // units per slice
-  int slices;         // slices per row group
-};
+__device__ __forceinline__ int tile_slot(int row, int piece) { return 32 * row + (piece ^ row); }
 
-DecodeGeom decode_geom(int64_t in, int64_t out, int64_t r) {
-  DecodeGeom d;
-  d.units = ceil_div(in, 256);
-  const int kMaxUps = max_ups(static_cast<int>(ceil_div(r, 16)));
-  const int64_t groups = ceil_div(out, kR);
-  int64_t want = ceil_div(256, groups);  // slices per group for ~256 workgroups
-  if (want < 1) want = 1;
-  int64_t ups = ceil_div(d.units, want);
-  if (ups > kMaxUps) ups = kMaxUps;
-  if (ups < 1) ups = 1;
-  d.ups = static_cast<int>(ups);
-  d.slices = static_cast<int>(ceil_div(d.units, ups));
-  return d;
-}
+// This lane's block of codes in one chunk, with its absmax code and scale.
+struct CodeStage {
+  u32x4 c0, c1;
+  uint32_t q;
+  float sc;
+};
 }  // namespace
 
-size_t decode_workspace_bytes(int64_t in, int64_t out, int64_t r) {
-  const DecodeGeom d = decode_geom(in, out, r);
-  return static_cast<size_t>(d.slices) * 16 * static_cast<size_t>(out) * 4;  // fp32 partials
-}
-
-int64_t decode_counter_count(int64_t out) { return ceil_div(out, kR); }
-
 template <int RT>  // rank tiles of 16 (r <= 16 * RT)
-__global__ __launch_bounds__(kWaves * 64) void k_decode_fwd(
+__global__ __launch_bounds__(kThreads) void k_decode_fwd(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
-    uint16_t* __restrict__ Y, int64_t out, int ups, int slices, float* __restrict__ partials,
-    uint32_t* __restrict__ counters) {
-  constexpr int kMaxUps = max_ups(RT);
-  // activation / A fragments: [unit][step j][lane] x 16 B
-  __shared__ u32x4 s_x[kMaxUps][8][64];
-  __shared__ u32x4 s_a[kMaxUps][RT][8][64];
-  __shared__ f32x4v s_u[kMaxUps][RT][64];
-  __shared__ float s_uf[RT * 16][17];        // U_slice^T [j][t]
-  __shared__ float s_b[kR][RT * 16 + 1];     // B rows of the group, fp32
-  __shared__ int s_last;
+    uint16_t* __restrict__ Y, int64_t out) {
+  // staging tiles during the main loop; reused for the epilogue afterwards
+  __shared__ u32x4 s_tiles[kWaves][2][kTileSlots];
+  __shared__ float s_b[kRows][RT * 16 + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: everything derived from it (the wave's block
+  // range, chunk count, partial-chunk test) stays in scalar registers and
+  // branches
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int64_t grp = blockIdx.x, slc = blockIdx.y;
-  const int64_t r0 = grp * kR;
-  const int64_t units = ceil_div(in, 256);
-  const int64_t u0 = slc * ups;
-  const int nu = static_cast<int>(u0 + ups <= units ? ups : units - u0);
-  const int64_t kblocks = in / 64;
+  const int half = lane >> 5, piece = lane & 31;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int64_t nb = in / 64;  // blocks per row
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  // the last row group may hold only 64 rows (out % 128 == 64)
-  const int rows_valid = static_cast<int>(out - r0 < kR ? out - r0 : kR);
-  const bool tile_ok = 16 * wv < rows_valid;
 
-  // -- 1. the HBM stream first: this wave's codes for all units of the slice
-  const int64_t row = r0 + 16 * wv + n;
-  u32x4 c[kMaxUps][2];
-  uint32_t qv[kMaxUps];
-  float sv[kMaxUps];
-  bool okv[kMaxUps];
+  const int bw0 = static_cast<int>(nb * wv / kWaves), bw1 = static_cast<int>(nb * (wv + 1) / kWaves);
+  const int nch = (bw1 - bw0 + 3) / 4;
+  const uint32_t row = static_cast<uint32_t>(r0) + n;
+  const uint32_t inu = static_cast<uint32_t>(in), nbu = static_cast<uint32_t>(nb);
+  const int xpairs = (T + 1) / 2;
+
+  // Buffer resources: a load whose offset lies past the end returns zeros
+  // without a branch.  This zero-fills token rows >= T, rank rows >= r and
+  // block indices past the last row (sizes are checked on the host to fit
+  // 32-bit offsets).
+  const uint32_t wbytes = static_cast<uint32_t>(static_cast<uint64_t>(out) * in / 2);
+  const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes), 0, static_cast<int>(wbytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(absmax_q), 0, static_cast<int>(wbytes / 32), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scale), 0, static_cast<int>((wbytes + 8191) / 8192 * 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X), 0, static_cast<int>(static_cast<uint32_t>(T) * inu * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(r) * inu * 2), kBufferWord3);
+
+  // B rows of this workgroup: raw bits loaded now (nothing waits for them),
+  // converted and written to LDS in the epilogue
+  constexpr int kBPer = (kRows * RT * 16 + kThreads - 1) / kThreads;
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(out) * r * 2), kBufferWord3);
+  uint32_t braw[kBPer];
 #pragma unroll
-  for (int i = 0; i < kMaxUps; ++i) {
-    const int64_t kb = 4 * (u0 + i) + g;
-    okv[i] = tile_ok && i < nu && kb < kblocks;
-    if (okv[i]) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(codes + ((row * in + kb * 64) >> 1));
-      c[i][0] = __builtin_nontemporal_load(src);
-      c[i][1] = __builtin_nontemporal_load(src + 1);
-      const int64_t bi = (row * in) / 64 + kb;
-      qv[i] = absmax_q[bi];
-      sv[i] = scale[bi >> 8];
-    } else {
-      c[i][0] = c[i][1] = zero4;
-      qv[i] = 0u;
-      sv[i] = 0.f;
-    }
-  }
-
-  // -- 2. stage X and A slices in fragment order, and the group's B rows.
-  // Fragment (u, j, lane l) = 8 bf16 at k = 256u + 64*(l/16) + 8j of token /
-  // rank row l%16.
-  for (int idx = tid; idx < nu * 8 * 64; idx += kWaves * 64) {
-    const int u = idx / 512, rem = idx % 512, j = rem / 64, l = rem % 64;
-    const int t = l & 15;
-    const int64_t k = (u0 + u) * 256 + 64 * (l >> 4) + 8 * j;
-    u32x4 v = zero4;
-    if (t < T && k < in) v = *reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(t) * in + k);
-    s_x[u][j][l] = v;
-  }
-  for (int idx = tid; idx < nu * RT * 8 * 64; idx += kWaves * 64) {
-    const int u = idx / (RT * 512), rem = idx % (RT * 512);
-    const int rt = rem / 512, rem2 = rem % 512, j = rem2 / 64, l = rem2 % 64;
-    const int jr = rt * 16 + (l & 15);
-    const int64_t k = (u0 + u) * 256 + 64 * (l >> 4) + 8 * j;
-    u32x4 v = zero4;
-    if (jr < r && k < in) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(jr) * in + k);
-    s_a[u][rt][j][l] = v;
-  }
-  for (int idx = tid; idx < kR * RT * 16; idx += kWaves * 64) {
+  for (int e = 0; e < kBPer; ++e) {
+    const int idx = tid + e * kThreads;
     const int rr = idx / (RT * 16), j = idx % (RT * 16);
-    float v = 0.f;
-    if (j < r && rr < rows_valid)
-      v = __builtin_bit_cast(float, static_cast<uint32_t>(B[(r0 + rr) * r + j]) << 16);
-    s_b[rr][j] = v;
+    const uint32_t off = (rr < kRows && j < r) ? ((static_cast<uint32_t>(r0) + rr) * r + j) * 2 : kPastEnd;
+    braw[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
   }
-  __syncthreads();
 
-  // -- 3. base product of this wave's row tile, and U of unit wv
-  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  // Lanes whose block lies past the wave's range read a neighbouring block
+  // (or zeros past the end): finite values that meet zero activations.
+  auto load_codes = [&](CodeStage& cs, int c) {
+    const uint32_t blk = static_cast<uint32_t>(bw0 + 4 * c + g);
+    const uint32_t off = row * (inu / 2) + blk * 32;
+    cs.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, off, 0, kStream));
+    cs.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, off + 16, 0, kStream));
+    const uint32_t bi = row * nbu + blk;
+    cs.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi, 0, 0);
+    cs.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (bi >> 8) * 4, 0, 0));
+  };
+  // Rows 2i + l/32 (first row `row0`) of a chunk (256 k), piece (l%32) ^ row:
+  // contiguous 512 B per row.  Pieces past the wave's block range (only in
+  // its last chunk) are redirected past the end and read as zero.
+  auto load_rows = [&](u32x4 (&reg)[8], const __amdgpu_buffer_rsrc_t& rs, uint32_t row0, int c) {
+    const uint32_t k0 = static_cast<uint32_t>(bw0 + 4 * c) * 64;
+    const int kvalid = (bw1 - bw0 - 4 * c) * 64;
+    if (kvalid >= 256) {
 #pragma unroll
-  for (int i = 0; i < kMaxUps; ++i) {
-    if (i >= nu) break;
-    const float ahat = okv[i] ? dq_absmax(qv[i], sv[i]) : 0.f;
-    const Nf4Table tab = make_table(ahat);
+      for (int i = 0; i < 8; ++i) {
+        const int t = 2 * i + half, p = piece ^ t;
+        const uint32_t off = ((row0 + t) * inu + k0 + 8 * p) * 2;
+        reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 2 * i + half, p = piece ^ t;
+        const uint32_t off = 8 * p < kvalid ? ((row0 + t) * inu + k0 + 8 * p) * 2 : kPastEnd;
+        reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      }
+    }
+  };
+  auto load_x = [&](u32x4 (&reg)[8], int c) { load_rows(reg, rs_x, 0, c); };
+  auto load_a = [&](u32x4 (&reg)[8], int c, int rt) { load_rows(reg, rs_a, 16 * rt, c); };
+
+  u32x4* tx = s_tiles[wv][0];
+  u32x4* ta = s_tiles[wv][1];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 au[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One chunk from registers: xr holds X(c), a0 holds A(c, tile 0).  Tiles
+  // 1.. of A are loaded here into a1 / a0 in turn (r > 16 only).
+  auto chunk = [&](int c, const CodeStage& cs, const u32x4 (&xr)[8], u32x4 (&a0)[8],
+                   u32x4 (&a1)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < xpairs) tx[64 * i + lane] = xr[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ta[64 * i + lane] = a0[i];
+    if constexpr (RT > 1) load_a(a1, c, 1);
+    // base product
+    const Nf4Table tab = make_table(dq_absmax(cs.q, cs.sc));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t cw = j < 4 ? c[i][0][j] : c[i][1][j - 4];
+      const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
+      const uint32_t cw = j < 4 ? cs.c0[j] : cs.c1[j - 4];
       uint32_t w[4];
       lookup8(tab, cw, w);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
-                                                    as_bf16x8(s_x[i][j][lane]), acc, 0, 0, 0);
+                                                    as_bf16x8(xf), acc, 0, 0, 0);
     }
-  }
-  if (wv < nu) {
-    f32x4v au[RT];
+    // this wave's share of U, rank tile by rank tile through the A tile
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) au[rt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) {
+      if (rt > 0) {
+        u32x4 (&cur)[8] = (rt & 1) ? a1 : a0;
+        u32x4 (&nxt)[8] = (rt & 1) ? a0 : a1;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8 xb = as_bf16x8(s_x[wv][j][lane]);
+        for (int i = 0; i < 8; ++i) ta[64 * i + lane] = cur[i];
+        if (rt + 1 < RT) load_a(nxt, c, rt + 1);
+      }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        au[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s_a[wv][rt][j][lane]), xb, au[rt],
-                                                         0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
+        const u32x4 af = ta[tile_slot(n, 8 * g + j)];
+        au[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), au[rt], 0, 0,
+                                                         0);
+      }
     }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) s_u[wv][rt][lane] = au[rt];
-  }
-  __syncthreads();
-  // U_slice^T[j][t] = sum over the slice's units; lane holds D[4g+i][n]
-  if (wv < RT) {
-    f32x4v su = {0.f, 0.f, 0.f, 0.f};
-    for (int u = 0; u < nu; ++u) su += s_u[u][wv][lane];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_uf[wv * 16 + 4 * g + i][n] = su[i];
-  }
-  __syncthreads();
+  };
 
-  // -- 4. partial of this slice: base + s * U_slice B^T, rows 16*wv + 4g + i
-  const int t = n;
-  float y[4];
+  // For r <= 16, two register sets by chunk parity: codes, X and A of chunk
+  // c + 2 are loaded as soon as chunk c has been computed, so two chunks'
+  // loads are always in flight.  Larger ranks need the registers for their
+  // further A tiles and keep one chunk in flight.
+  CodeStage cs0, cs1;
+  u32x4 x0[8], x1[8], p0[8], p1[8], q0[8];
+  auto load_all = [&](CodeStage& cs, u32x4 (&xr)[8], u32x4 (&a)[8], int c) {
+    load_codes(cs, c);
+    load_x(xr, c);
+    load_a(a, c, 0);
+  };
+  // token rows of the X tile that no chunk writes (>= 2 * xpairs) stay zero
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = 16 * wv + 4 * g + i;
-    float lora = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < RT * 16; ++j) lora += s_uf[j][t] * s_b[rr][j];
-    y[i] = acc[i] + s * lora;
-  }
-  if (t < T && tile_ok) {
-    // device-coherent stores (written through to the coherence point shared
-    // by all XCDs), so the reducing workgroup can read them without any
-    // cache-wide writeback or invalidate
-    uint64_t* dst = reinterpret_cast<uint64_t*>(partials + (slc * 16 + t) * out + r0 + 16 * wv + 4 * g);
-    const uint64_t v01 = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, y[0])) |
-                         (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, y[1])) << 32);
-    const uint64_t v23 = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, y[2])) |
-                         (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, y[3])) << 32);
-    __hip_atomic_store(dst, v01, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, v23, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < 8; ++i) tx[64 * i + lane] = zero4;
+  if constexpr (RT == 1) {
+    if (nch > 0) load_all(cs0, x0, p0, 0);
+    if (nch > 1) load_all(cs1, x1, p1, 1);
+    for (int c = 0; c < nch; c += 2) {
+      chunk(c, cs0, x0, p0, q0);
+      if (c + 2 < nch) load_all(cs0, x0, p0, c + 2);
+      if (c + 1 < nch) {
+        chunk(c + 1, cs1, x1, p1, q0);
+        if (c + 3 < nch) load_all(cs1, x1, p1, c + 3);
+      }
+    }
+  } else {
+    for (int c = 0; c < nch; ++c) {
+      load_all(cs0, x0, p0, c);
+      chunk(c, cs0, x0, p0, q0);
+    }
   }
 
-  // -- 5. the last slice to finish reduces the row group.  The stores above
-  // are acknowledged (vmcnt 0) before the barrier, hence before the counter
-  // update; the reducer reads the partials with device-coherent loads.
-  __builtin_amdgcn_s_waitcnt(0);
+  // ---------------- epilogue (tiles reused): per-wave accumulators
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t ticket = __hip_atomic_fetch_add(counters + grp, 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ticket == static_cast<uint32_t>(slices - 1);
+  f32x4* s_acc = reinterpret_cast<f32x4*>(&s_tiles[0][0][0]);  // [wave][1 + RT][64]
+  s_acc[(wv * (1 + RT)) * 64 + lane] = acc;                     // D[row 4g+i][token n]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) s_acc[(wv * (1 + RT) + 1 + rt) * 64 + lane] = au[rt];  // D[rank][token]
+#pragma unroll
+  for (int e = 0; e < kBPer; ++e) {
+    const int idx = tid + e * kThreads;
+    if (idx < kRows * RT * 16)
+      s_b[idx / (RT * 16)][idx % (RT * 16)] = __builtin_bit_cast(float, braw[e] << 16);
   }
   __syncthreads();
-  if (!s_last) return;
-  // T x 128 outputs, 4 consecutive rows per thread
-  const int tt = tid >> 5, rq = (tid & 31) * 4;
-  if (tt < T && rq < rows_valid) {
-    f32x4v sum = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < slices; ++k) {
-      uint64_t* src = reinterpret_cast<uint64_t*>(
-          partials + (static_cast<int64_t>(k) * 16 + tt) * out + r0 + rq);
-      const uint64_t v01 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t v23 = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sum += f32x4v{__builtin_bit_cast(float, static_cast<uint32_t>(v01)),
-                    __builtin_bit_cast(float, static_cast<uint32_t>(v01 >> 32)),
-                    __builtin_bit_cast(float, static_cast<uint32_t>(v23)),
-                    __builtin_bit_cast(float, static_cast<uint32_t>(v23 >> 32))};
+  // U [t][j] summed over the waves, placed after the accumulators
+  float* s_u = reinterpret_cast<float*>(s_acc + kWaves * (1 + RT) * 64);  // [16][RT*16 + 1]
+  constexpr int kUP = RT * 16 + 1;
+  for (int idx = tid; idx < 16 * RT * 16; idx += kThreads) {
+    const int t = idx / (RT * 16), j = idx % (RT * 16);
+    const int rt = j >> 4, m = j & 15;  // lane 16 (m/4) + t, element m % 4
+    float u = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) u += s_acc[(w * (1 + RT) + 1 + rt) * 64 + 16 * (m >> 2) + t][m & 3];
+    s_u[t * kUP + j] = u;
+  }
+  __syncthreads();
+  // T x 16 outputs, two adjacent rows per thread
+  if (tid < T * (kRows / 2)) {
+    const int t = tid / (kRows / 2), rr = 2 * (tid % (kRows / 2));
+    float y[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int m = rr + e;
+      float base = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) base += s_acc[(w * (1 + RT)) * 64 + 16 * (m >> 2) + t][m & 3];
+      float lora = 0.f;
+      for (int j = 0; j < r; ++j) lora += s_u[t * kUP + j] * s_b[m][j];
+      y[e] = base + s * lora;
     }
-    const uint32_t p0 = pack_bf16x2(sum[0], sum[1]);
-    const uint32_t p1 = pack_bf16x2(sum[2], sum[3]);
-    *reinterpret_cast<u32x2*>(Y + static_cast<int64_t>(tt) * out + r0 + rq) = u32x2{p0, p1};
+    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * out + r0 + rr) = pack_bf16x2(y[0], y[1]);
   }
-  // every slice of this group has taken its ticket: reset for the next call
-  if (tid == 0) __hip_atomic_store(counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r) {
+  // 32-bit buffer offsets: codes and every row of X and A stay below 2^31 bytes
+  return T >= 1 && T <= kDecodeMaxT && r >= 1 && r <= kDecodeMaxRank && out % kRows == 0 &&
+         in % 64 == 0 && in <= (int64_t(1) << 24) && out * in < (int64_t(1) << 32);
 }
 
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                              int64_t in, int64_t out, const uint16_t* X, int64_t T,
                              const uint16_t* A, const uint16_t* B, int64_t r, float s,
-                             uint16_t* Y, void* ws, uint32_t* counters, hipStream_t st) {
-  const DecodeGeom d = decode_geom(in, out, r);
-  const dim3 grid(static_cast<uint32_t>(ceil_div(out, kR)), static_cast<uint32_t>(d.slices));
-  const dim3 block(kWaves * 64);
-  float* partials = static_cast<float*>(ws);
+                             uint16_t* Y, hipStream_t st) {
+  if (!decode_fits(T, in, out, r)) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(out / kRows));
+  const dim3 block(kThreads);
   const int rt = static_cast<int>(ceil_div(r, 16));
   const int iT = static_cast<int>(T), ir = static_cast<int>(r);
 #define QLORA_DEC(RTV)                                                                            \
   hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, codes, absmax_q, scale, in, X, iT, \
-                     A, B, ir, s, Y, out, d.ups, d.slices, partials, counters)
+                     A, B, ir, s, Y, out)
   if (rt <= 1) QLORA_DEC(1);
   else if (rt <= 2) QLORA_DEC(2);
-  else if (rt <= 4) QLORA_DEC(4);
-  else return hipErrorInvalidValue;
+  else QLORA_DEC(4);
 #undef QLORA_DEC
   return hipGetLastError();
 }

@@ -38,16 +38,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int launched(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
 
 // ---------------------------------------------------------------------------
-// Workspace layout.  Segments are 256-byte aligned.
+// Workspace layout.  Segments are 256-byte aligned; the workspace needs no
+// initialisation.
 // ---------------------------------------------------------------------------
-// Every layout starts with the same counter region (split-K tickets of the
-// small-token forward).  It must be zero when a call starts; every call
-// leaves it zero, and no other segment overlaps it, so a workspace that was
-// zero-filled once can serve any sequence of calls.
-constexpr size_t kCounterRegion = 4096;
+constexpr size_t kMinWorkspace = 256;
 
 struct Carve {
-  size_t off = kCounterRegion;
+  size_t off = 0;
   size_t take(size_t bytes) {
     const size_t at = off;
     off += (bytes + 255) & ~static_cast<size_t>(255);
@@ -56,7 +53,7 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t counters, partials, u_pad, b_pad, total;
+  size_t u_pad, b_pad, total;
 };
 struct BwdLayout {
   size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, total;
@@ -64,16 +61,12 @@ struct BwdLayout {
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
 
-bool fwd_uses_decode(int64_t T, int64_t r) { return T <= kDecodeMaxT && r <= kDecodeMaxRank; }
+bool fwd_uses_decode(int64_t T, int64_t in, int64_t out, int64_t r) { return decode_fits(T, in, out, r); }
 
 FwdLayout fwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
-  FwdLayout l{0, 0, 0, 0, 0};
+  FwdLayout l{0, 0, 0};
   Carve c;
-  if (fwd_uses_decode(T, r)) {  // split-K partials of the fused small-token kernel
-    l.partials = c.take(decode_workspace_bytes(in, out, r));
-    l.total = c.off;
-    return l;
-  }
+  if (fwd_uses_decode(T, in, out, r)) return l;  // the fused small-token kernel needs none
   const int64_t rp = padded_rank(r);
   l.u_pad = c.take(static_cast<size_t>(T * rp * 4));
   l.b_pad = c.take(static_cast<size_t>(out * rp * 4));
@@ -99,7 +92,6 @@ BwdLayout bwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
 
 bool linear_shapes_ok(int64_t T, int64_t in, int64_t out, int64_t r) {
   if (T < 0 || in < 64 || out < 64 || (in % 64) != 0 || (out % 64) != 0) return false;
-  if (decode_counter_count(out) * 4 > static_cast<int64_t>(kCounterRegion)) return false;
   if (r < 1 || r > QLORA_MAX_RANK) return false;
   if (in > (int64_t(1) << 31) || out > (int64_t(1) << 31) || T > (int64_t(1) << 31)) return false;
   return true;
@@ -155,8 +147,9 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
 size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                              int backward) {
   if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;
-  return backward ? bwd_layout(T, in_features, out_features, r).total
-                  : fwd_layout(T, in_features, out_features, r).total;
+  const size_t need = backward ? bwd_layout(T, in_features, out_features, r).total
+                               : fwd_layout(T, in_features, out_features, r).total;
+  return need > kMinWorkspace ? need : kMinWorkspace;
 }
 
 int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
@@ -177,10 +170,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = alpha / static_cast<float>(r);
-  if (fwd_uses_decode(T, r))
+  if (fwd_uses_decode(T, in, out, r))
     return launched(launch_decode_fwd(W->codes, W->absmax_q, W->absmax_scale, in, out, X, T, A, B,
-                                      r, scale, Y, static_cast<uint8_t*>(ws) + lay.partials,
-                                      static_cast<uint32_t*>(ws), s));
+                                      r, scale, Y, s));
 
   const int64_t rp = padded_rank(r);
   uint8_t* base = static_cast<uint8_t*>(ws);

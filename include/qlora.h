@@ -126,15 +126,13 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
 /*
  * Workspace bytes needed by qlora_linear_fwd (backward = 0) or
  * qlora_linear_bwd (backward = 1) for T tokens, in/out features and rank r.
- * Returns 0 for invalid shapes.  Host only.
+ * Returns 0 for invalid shapes and at least 256 otherwise.  Host only.
  *
- * Workspace contract (both linear calls): the first 4096 bytes hold the
- * tickets of the small-token forward's split-K reduction.  They must read as
- * zero when a call starts, and every call leaves them zero on completion, so
- * a workspace zero-filled once (e.g. hipMemset before first use) can serve
- * any sequence of calls of either entry point, of any shape that fits.  The
- * rest needs no initialisation.  Calls that overlap in time (different
- * streams) must not share a workspace.
+ * The workspace is scratch for intermediate products (padded LoRA factors,
+ * the transposed dequantized weight of the backward).  It needs no
+ * initialisation and keeps nothing between calls.  The small-token forward
+ * (T <= 16 and r <= 64) does not use it; ws may then be NULL.  Calls that
+ * overlap in time (different streams) must not share a workspace.
  */
 size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                              int backward);
