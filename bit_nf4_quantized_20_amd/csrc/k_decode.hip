@@ -43,6 +43,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 16;
 constexpr int kTileSlots = 16 * 32;  // 16 rows x 32 pieces of 16 B (8 KB)
+constexpr int kCodeSlots = 16 * 8;   // 16 rows x 8 pieces: one chunk of codes (2 KB)
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kStream = 2;               // cache policy nt: streamed once
 constexpr uint32_t kPastEnd = 0x80000000u;  // past every buffer (all < 2^31 bytes)
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
     uint16_t* __restrict__ Y, int64_t out) {
   // staging tiles during the main loop; reused for the epilogue afterwards
   __shared__ u32x4 s_tiles[kWaves][2][kTileSlots];
+  __shared__ u32x4 s_codes[kWaves][kCodeSlots];
   __shared__ float s_b[kRows][RT * 16 + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -116,13 +118,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
     braw[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
   }
 
-  // Lanes whose block lies past the wave's range read a neighbouring block
-  // (or zeros past the end): finite values that meet zero activations.
+  // The chunk's codes (16 rows x 128 B) are loaded contiguously, eight rows
+  // per instruction: lane l takes piece l%8 of row l/8 (c0) and of row
+  // 8 + l/8 (c1); the chunk routine moves them to their owners through LDS.
+  // Blocks past the wave's range read a neighbouring block (or zeros past
+  // the end): finite values that meet zero activations.
   auto load_codes = [&](CodeStage& cs, int c) {
+    const uint32_t base = static_cast<uint32_t>(bw0 + 4 * c) * 32 + 16 * (lane & 7);
+    const uint32_t rl = static_cast<uint32_t>(r0) + (lane >> 3);
+    cs.c0 = __builtin_bit_cast(u32x4,
+                               __builtin_amdgcn_raw_buffer_load_b128(rs_codes, rl * (inu / 2) + base, 0, kStream));
+    cs.c1 = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, (rl + 8) * (inu / 2) + base, 0, kStream));
     const uint32_t blk = static_cast<uint32_t>(bw0 + 4 * c + g);
-    const uint32_t off = row * (inu / 2) + blk * 32;
-    cs.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, off, 0, kStream));
-    cs.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, off + 16, 0, kStream));
     const uint32_t bi = row * nbu + blk;
     cs.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi, 0, 0);
     cs.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (bi >> 8) * 4, 0, 0));
@@ -130,12 +138,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
   // Rows 2i + l/32 (first row `row0`) of a chunk (256 k), piece (l%32) ^ row:
   // contiguous 512 B per row.  Pieces past the wave's block range (only in
   // its last chunk) are redirected past the end and read as zero.
-  auto load_rows = [&](u32x4 (&reg)[8], const __amdgpu_buffer_rsrc_t& rs, uint32_t row0, int c) {
+  // Only the npairs instructions that hold existing rows are issued: the
+  // address unit spends the same time on a lane whether or not it is in
+  // range.
+  auto load_rows = [&](u32x4 (&reg)[8], const __amdgpu_buffer_rsrc_t& rs, uint32_t row0, int npairs,
+                       int c) {
     const uint32_t k0 = static_cast<uint32_t>(bw0 + 4 * c) * 64;
     const int kvalid = (bw1 - bw0 - 4 * c) * 64;
     if (kvalid >= 256) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        if (i >= npairs) break;
         const int t = 2 * i + half, p = piece ^ t;
         const uint32_t off = ((row0 + t) * inu + k0 + 8 * p) * 2;
         reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
@@ -143,14 +156,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        if (i >= npairs) break;
         const int t = 2 * i + half, p = piece ^ t;
         const uint32_t off = 8 * p < kvalid ? ((row0 + t) * inu + k0 + 8 * p) * 2 : kPastEnd;
         reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
       }
     }
   };
-  auto load_x = [&](u32x4 (&reg)[8], int c) { load_rows(reg, rs_x, 0, c); };
-  auto load_a = [&](u32x4 (&reg)[8], int c, int rt) { load_rows(reg, rs_a, 16 * rt, c); };
+  auto a_pairs = [&](int rt) {
+    const int rows = r - 16 * rt;
+    return rows >= 16 ? 8 : (rows + 1) / 2;
+  };
+  auto load_x = [&](u32x4 (&reg)[8], int c) { load_rows(reg, rs_x, 0, xpairs, c); };
+  auto load_a = [&](u32x4 (&reg)[8], int c, int rt) { load_rows(reg, rs_a, 16 * rt, a_pairs(rt), c); };
 
   u32x4* tx = s_tiles[wv][0];
   u32x4* ta = s_tiles[wv][1];
@@ -159,6 +177,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A tile from registers; rows of ranks >= r are zero
+  auto write_a = [&](const u32x4 (&a)[8], int ap) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < ap) ta[64 * i + lane] = a[i];
+      else ta[64 * i + lane] = zero4;
+    }
+  };
+
   // One chunk from registers: xr holds X(c), a0 holds A(c, tile 0).  Tiles
   // 1.. of A are loaded here into a1 / a0 in turn (r > 16 only).
   auto chunk = [&](int c, const CodeStage& cs, const u32x4 (&xr)[8], u32x4 (&a0)[8],
@@ -166,15 +193,25 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (i < xpairs) tx[64 * i + lane] = xr[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ta[64 * i + lane] = a0[i];
+    write_a(a0, a_pairs(0));
     if constexpr (RT > 1) load_a(a1, c, 1);
+    // codes to their owners: row n, block g = pieces 2g, 2g + 1.  Piece p
+    // of row m sits at slot 8m + (p ^ ((m >> 1) & 7)), so the owners' reads
+    // of 16 rows fall on 16 distinct 4-bank groups.
+    u32x4* tc = s_codes[wv];
+    {
+      const int m = lane >> 3, pc = lane & 7;
+      tc[8 * m + (pc ^ ((m >> 1) & 7))] = cs.c0;
+      tc[8 * (m + 8) + (pc ^ (((m + 8) >> 1) & 7))] = cs.c1;
+    }
+    const u32x4 cc0 = tc[8 * n + ((2 * g) ^ ((n >> 1) & 7))];
+    const u32x4 cc1 = tc[8 * n + ((2 * g + 1) ^ ((n >> 1) & 7))];
     // base product
     const Nf4Table tab = make_table(dq_absmax(cs.q, cs.sc));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
-      const uint32_t cw = j < 4 ? cs.c0[j] : cs.c1[j - 4];
+      const uint32_t cw = j < 4 ? cc0[j] : cc1[j - 4];
       uint32_t w[4];
       lookup8(tab, cw, w);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
@@ -186,8 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
       if (rt > 0) {
         u32x4 (&cur)[8] = (rt & 1) ? a1 : a0;
         u32x4 (&nxt)[8] = (rt & 1) ? a0 : a1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ta[64 * i + lane] = cur[i];
+        write_a(cur, a_pairs(rt));
         if (rt + 1 < RT) load_a(nxt, c, rt + 1);
       }
 #pragma unroll
@@ -206,10 +242,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
   // further A tiles and keep one chunk in flight.
   CodeStage cs0, cs1;
   u32x4 x0[8], x1[8], p0[8], p1[8], q0[8];
+  // activations and A first: their L2 round trip then overlaps the codes'
+  // longer HBM one
   auto load_all = [&](CodeStage& cs, u32x4 (&xr)[8], u32x4 (&a)[8], int c) {
-    load_codes(cs, c);
     load_x(xr, c);
     load_a(a, c, 0);
+    load_codes(cs, c);
   };
   // token rows of the X tile that no chunk writes (>= 2 * xpairs) stay zero
 #pragma unroll
@@ -275,6 +313,211 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
   }
 }
 
+// ---------------------------------------------------------------------------
+// r <= 16: the same decomposition with the two kinds of work on different
+// waves.  Waves 0-3 stream codes and run the dequantize + base MFMA (vector
+// ALU bound); waves 4-7 load X and A and run the U MFMA (bound by the
+// load-address unit).  Wave w and wave w + 4 share a quarter of the blocks
+// of each row and sit on the same SIMD, so the hardware overlaps one pair
+// member's address-unit stalls with the other's vector arithmetic.  The X
+// tile of a chunk is written by the U wave and read by both, double-buffered
+// by chunk parity with one workgroup barrier per chunk.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
+    const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
+    uint16_t* __restrict__ Y, int64_t out) {
+  constexpr int kPairs = kWaves / 2;
+  __shared__ u32x4 s_x[kPairs][2][kTileSlots];   // X tiles by chunk parity
+  __shared__ u32x4 s_a[kPairs][kTileSlots];      // A tile of each U wave
+  __shared__ u32x4 s_codes[kPairs][kCodeSlots];  // codes of each dequantize wave
+  __shared__ f32x4 s_acc[kWaves][64];
+  __shared__ float s_b[kRows][17];
+  __shared__ float s_u[16][17];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar wave index
+  const bool dq_wave = wv < kPairs;
+  const int qtr = dq_wave ? wv : wv - kPairs;
+  const int n = lane & 15, g = lane >> 4;
+  const int half = lane >> 5, piece = lane & 31;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int64_t nb = in / 64;
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+
+  const int bw0 = static_cast<int>(nb * qtr / kPairs), bw1 = static_cast<int>(nb * (qtr + 1) / kPairs);
+  const int nch = (bw1 - bw0 + 3) / 4;
+  const int nch_all = static_cast<int>((ceil_div(nb, kPairs) + 3) / 4);  // same for every wave
+  const uint32_t row = static_cast<uint32_t>(r0) + n;
+  const uint32_t inu = static_cast<uint32_t>(in), nbu = static_cast<uint32_t>(nb);
+  const int xpairs = (T + 1) / 2;
+  const int apairs = (r + 1) / 2;
+
+  const uint32_t wbytes = static_cast<uint32_t>(static_cast<uint64_t>(out) * in / 2);
+  const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes), 0, static_cast<int>(wbytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(absmax_q), 0, static_cast<int>(wbytes / 32), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scale), 0, static_cast<int>((wbytes + 8191) / 8192 * 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X), 0, static_cast<int>(static_cast<uint32_t>(T) * inu * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(r) * inu * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(out) * r * 2), kBufferWord3);
+
+  // B rows of this workgroup (16 x r <= 256 values), converted in the epilogue
+  uint32_t braw;
+  {
+    const int rr = tid >> 4, j = tid & 15;
+    const uint32_t off = (rr < kRows && j < r) ? ((static_cast<uint32_t>(r0) + rr) * r + j) * 2 : kPastEnd;
+    braw = tid < kRows * 16 ? __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0) : 0u;
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  if (dq_wave) {
+    // ------------------------------------------------ dequantize waves
+    u32x4* tc = s_codes[qtr];
+    auto load_codes = [&](CodeStage& cs, int c) {
+      const uint32_t base = static_cast<uint32_t>(bw0 + 4 * c) * 32 + 16 * (lane & 7);
+      const uint32_t rl = static_cast<uint32_t>(r0) + (lane >> 3);
+      cs.c0 = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, rl * (inu / 2) + base, 0, kStream));
+      cs.c1 = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, (rl + 8) * (inu / 2) + base, 0, kStream));
+      const uint32_t bi = row * nbu + static_cast<uint32_t>(bw0 + 4 * c + g);
+      cs.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi, 0, 0);
+      cs.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (bi >> 8) * 4, 0, 0));
+    };
+    auto step = [&](int c, CodeStage& cs, const u32x4* tx) {
+      const bool live = c < nch;
+      u32x4 cc0 = zero4, cc1 = zero4;
+      uint32_t qv = 0u;
+      float sv = 0.f;
+      if (live) {
+        const int m = lane >> 3, pc = lane & 7;
+        tc[8 * m + (pc ^ ((m >> 1) & 7))] = cs.c0;
+        tc[8 * (m + 8) + (pc ^ (((m + 8) >> 1) & 7))] = cs.c1;
+        cc0 = tc[8 * n + ((2 * g) ^ ((n >> 1) & 7))];
+        cc1 = tc[8 * n + ((2 * g + 1) ^ ((n >> 1) & 7))];
+        qv = cs.q;
+        sv = cs.sc;
+        if (c + 2 < nch) load_codes(cs, c + 2);
+      }
+      __syncthreads();  // X(c) is in tx
+      if (live) {
+        const Nf4Table tab = make_table(dq_absmax(qv, sv));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
+          const uint32_t cw = j < 4 ? cc0[j] : cc1[j - 4];
+          uint32_t w[4];
+          lookup8(tab, cw, w);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
+                                                        as_bf16x8(xf), acc, 0, 0, 0);
+        }
+      }
+    };
+    CodeStage cs0, cs1;
+    if (nch > 0) load_codes(cs0, 0);
+    if (nch > 1) load_codes(cs1, 1);
+    for (int c = 0; c < nch_all; c += 2) {
+      step(c, cs0, s_x[qtr][0]);
+      if (c + 1 < nch_all) step(c + 1, cs1, s_x[qtr][1]);
+    }
+  } else {
+    // ------------------------------------------------ U waves
+    u32x4* ta = s_a[qtr];
+    auto load_rows = [&](u32x4 (&reg)[8], const __amdgpu_buffer_rsrc_t& rs, int npairs, int c) {
+      const uint32_t k0 = static_cast<uint32_t>(bw0 + 4 * c) * 64;
+      const int kvalid = (bw1 - bw0 - 4 * c) * 64;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i >= npairs) break;
+        const int t = 2 * i + half, p = piece ^ t;
+        const uint32_t off = (kvalid >= 256 || 8 * p < kvalid) ? ((t * inu) + k0 + 8 * p) * 2 : kPastEnd;
+        reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      }
+    };
+    // token / rank rows that no chunk writes stay zero in both X tiles and the A tile
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i >= xpairs) {
+        s_x[qtr][0][64 * i + lane] = zero4;
+        s_x[qtr][1][64 * i + lane] = zero4;
+      }
+      if (i >= apairs) ta[64 * i + lane] = zero4;
+    }
+    auto step = [&](int c, u32x4 (&xr)[8], u32x4 (&ar)[8], u32x4* tx) {
+      const bool live = c < nch;
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < xpairs) tx[64 * i + lane] = xr[i];
+          if (i < apairs) ta[64 * i + lane] = ar[i];
+        }
+        if (c + 2 < nch) {
+          load_rows(xr, rs_x, xpairs, c + 2);
+          load_rows(ar, rs_a, apairs, c + 2);
+        }
+      }
+      __syncthreads();  // X(c) is in tx for the partner
+      if (live) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
+          const u32x4 af = ta[tile_slot(n, 8 * g + j)];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc, 0, 0, 0);
+        }
+      }
+    };
+    u32x4 x0[8], x1[8], a0[8], a1[8];
+    if (nch > 0) {
+      load_rows(x0, rs_x, xpairs, 0);
+      load_rows(a0, rs_a, apairs, 0);
+    }
+    if (nch > 1) {
+      load_rows(x1, rs_x, xpairs, 1);
+      load_rows(a1, rs_a, apairs, 1);
+    }
+    for (int c = 0; c < nch_all; c += 2) {
+      step(c, x0, a0, s_x[qtr][0]);
+      if (c + 1 < nch_all) step(c + 1, x1, a1, s_x[qtr][1]);
+    }
+  }
+
+  // ---------------- epilogue: waves 0-3 hold D[row][token], 4-7 D[rank][token]
+  s_acc[wv][lane] = acc;
+  if (tid < kRows * 16) s_b[tid >> 4][tid & 15] = __builtin_bit_cast(float, braw << 16);
+  __syncthreads();
+  if (tid < 256) {
+    const int t = tid >> 4, j = tid & 15;  // U[t][j]: lane 16 (j/4) + t, element j % 4
+    float u = 0.f;
+#pragma unroll
+    for (int w = kPairs; w < kWaves; ++w) u += s_acc[w][16 * (j >> 2) + t][j & 3];
+    s_u[t][j] = u;
+  }
+  __syncthreads();
+  if (tid < T * (kRows / 2)) {
+    const int t = tid / (kRows / 2), rr = 2 * (tid % (kRows / 2));
+    float y[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int m = rr + e;
+      float base = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPairs; ++w) base += s_acc[w][16 * (m >> 2) + t][m & 3];
+      float lora = 0.f;
+      for (int j = 0; j < r; ++j) lora += s_u[t][j] * s_b[m][j];
+      y[e] = base + s * lora;
+    }
+    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * out + r0 + rr) = pack_bf16x2(y[0], y[1]);
+  }
+}
+
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r) {
   // 32-bit buffer offsets: codes and every row of X and A stay below 2^31 bytes
   return T >= 1 && T <= kDecodeMaxT && r >= 1 && r <= kDecodeMaxRank && out % kRows == 0 &&
@@ -293,7 +536,9 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, cons
 #define QLORA_DEC(RTV)                                                                            \
   hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, codes, absmax_q, scale, in, X, iT, \
                      A, B, ir, s, Y, out)
-  if (rt <= 1) QLORA_DEC(1);
+  if (rt <= 1)
+    hipLaunchKernelGGL(k_decode_fwd_split, grid, block, 0, st, codes, absmax_q, scale, in, X, iT, A, B,
+                       ir, s, Y, out);
   else if (rt <= 2) QLORA_DEC(2);
   else QLORA_DEC(4);
 #undef QLORA_DEC
