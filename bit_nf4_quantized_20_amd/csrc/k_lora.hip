@@ -81,7 +81,14 @@ __global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ 
   // thread -> (token tt = tid % 16, rank j = tid / 16 + 16 * m)
   const int tt = tid & 15;
   const int64_t t = t0 + tt;
-  if (t >= T) return;
+  if (t >= T) {  // padding tokens of the transposed copy read as zero
+    if (hilo_t != nullptr && t < ldt)
+      for (int j = tid >> 4; j < rp; j += 16) {
+        hilo_t[static_cast<int64_t>(j) * ldt + t] = 0;
+        hilo_t[static_cast<int64_t>(rp + j) * ldt + t] = 0;
+      }
+    return;
+  }
   for (int j = tid >> 4; j < rp; j += 16) {
     float v = 0.f;
     if (j < 16 * RT) {
@@ -123,105 +130,156 @@ hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint
 
 // ---------------------------------------------------------------------------
 // lora_grad: G[j][c] = sum_t Pt[j][t] Q[t][c] + sum_t Pt[rp+j][t] Q[t][c]
-// (the hi and lo halves of the transposed rank factor), for 64 columns per
-// workgroup and a slice of tokens; partial sums over token slices go to the
-// zeroed fp32 output with atomics.  The Q tile [64 t][64 c] is transposed on
-// its way into LDS (pairs of token rows interleaved with v_perm, written as
-// dwords) so the MFMA B operand reads 8 consecutive tokens of one column.
-// Wave w owns the 32x32 output tiles (jt, ct) with jt*2 + ct = w (mod 4).
+// (the hi and lo halves of the transposed rank factor) for ranks
+// [j0, j0 + 32*JT), 128 columns per workgroup and a slice of tokens; slices
+// add into the zeroed fp32 output with atomics.  Bound by streaming Q (dY or
+// X) from HBM once.
+//
+// Per 64-token step the Q tile [64 t][128 c] and the Pt tile [64*JT rows][64 t]
+// are loaded contiguously into registers one step ahead and written into a
+// double-buffered LDS stage.  Q is transposed on the way: a thread holds two
+// token rows of 8 columns, pairs them with v_perm and writes one dword
+// (Q[2w][c], Q[2w+1][c]) per column; dword w of column c sits at
+// 36c + (w ^ 4((c >> 4) & 7)), which makes both these writes and the MFMA
+// fragment reads (8 tokens of one column) free of bank conflicts.  Wave w
+// owns columns [32w, 32w + 32) and all JT rank tiles:
+// v_mfma_f32_32x32x16_bf16 with Pt rows as A operand and Q columns as B.
 // ---------------------------------------------------------------------------
-constexpr int kGradSlice = 512;
-constexpr int kQPitch = 72;  // bf16 per LDS row (144 B, 16-byte aligned rows)
+constexpr int kGradCT = 128;    // columns per workgroup
+constexpr int kGradPitch = 36;  // dwords per LDS row: 64 tokens + 8 padding
+constexpr int kGradMaxJT = 4;   // rank tiles per launch (128 ranks)
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kPastEnd = 0x80000000u;
 
-template <int JT>  // rank tiles of 32
+namespace {
+__device__ __forceinline__ int grad_qslot(int c, int w) { return kGradPitch * c + (w ^ (4 * ((c >> 4) & 7))); }
+}  // namespace
+
+// kJC: output out[j*C + c] (else out[c*r + j]).  The MFMA orientation
+// follows it, so a wave's 32 lanes always add to 32 consecutive floats.
+template <int JT, bool kJC>
 __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ Pt, int64_t T,
-                                                   int64_t ldt, int rp,
-                                                   const uint16_t* __restrict__ Q, int64_t C, int r,
-                                                   float* __restrict__ out, int out_jc) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * kQPitch];
-  constexpr int kTiles = JT * 2;                 // (jt, ct) tiles
-  constexpr int kPerWave = (kTiles + 3) / 4;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+                                                   int64_t ldt, int rp, const uint16_t* __restrict__ Q,
+                                                   int64_t C, int r, int j0, float* __restrict__ out,
+                                                   int64_t TS) {
+  constexpr int kPRows = 64 * JT;  // hi rows [0, 32JT), lo rows [32JT, 64JT)
+  __shared__ uint32_t s_q[2][kGradCT * kGradPitch];
+  __shared__ uint32_t s_p[2][kPRows * kGradPitch];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, h = lane >> 5;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int64_t ts = static_cast<int64_t>(blockIdx.y) * kGradSlice;
-  const int64_t te = ts + kGradSlice < T ? ts + kGradSlice : T;
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kGradCT;
+  const int64_t ts = static_cast<int64_t>(blockIdx.y) * TS;
+  const int64_t te = ts + TS < T ? ts + TS : T;
+  const int nsteps = static_cast<int>((te - ts + 63) / 64);
 
-  f32x16 acc[kPerWave];
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  // Q resource starts at this slice and ends at row T (or 2^31 - 1 bytes;
+  // the host keeps a slice under 2^30 bytes)
+  const uint64_t q_bytes = static_cast<uint64_t>(T - ts) * C * 2;
+  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Q + ts * C), 0, static_cast<int>(q_bytes < 0x7fffffffu ? q_bytes : 0x7fffffffu),
+      kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Pt), 0, static_cast<int>(static_cast<uint64_t>(2 * rp) * ldt * 2), kBufferWord3);
 
-  // staging role: token pair tp, column group cg (8 columns)
-  const int tp = tid >> 3, cg = tid & 7;
-  for (int64_t tb = ts; tb < te; tb += 64) {
-    {
-      const int64_t ta = tb + 2 * tp, tb1 = ta + 1;
-      const u32x4 a = ta < te ? *reinterpret_cast<const u32x4*>(Q + ta * C + c0 + 8 * cg) : zero4;
-      const u32x4 b = tb1 < te ? *reinterpret_cast<const u32x4*>(Q + tb1 * C + c0 + 8 * cg) : zero4;
+  // Q staging items: column group cg (8 columns), token pairs tp and tp + 16
+  const int cg = tid & 15, tp0 = tid >> 4;
+  const bool col_ok = c0 + 8 * cg < C;
+  u32x4 qv[4];
+  u32x4 pv[2 * JT];
+  auto load = [&](int step) {
+    const int64_t t0 = ts + 64 * static_cast<int64_t>(step);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 - ts + 2 * (tp0 + 16 * (i >> 1)) + (i & 1);  // rows past T read as zero
+      const uint32_t off = col_ok ? static_cast<uint32_t>((t * C + c0 + 8 * cg) * 2) : kPastEnd;
+      qv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_q, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * JT; ++i) {
+      const int id = tid + 256 * i, prow = id >> 3, q = id & 7;
+      const int64_t grow = prow < 32 * JT ? j0 + prow : rp + j0 + (prow - 32 * JT);
+      const int64_t tk = t0 + 8 * q;  // tokens in [T, ldt) are zero in Pt
+      const uint32_t off = tk < ldt ? static_cast<uint32_t>((grow * ldt + tk) * 2) : kPastEnd;
+      pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, off, 0, 0));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 a = qv[2 * i], b = qv[2 * i + 1];
+      const int w = tp0 + 16 * i;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // columns 2e and 2e+1 of the group: (Q[ta][c], Q[tb1][c]) pairs
-        const uint32_t lo = perm(b[e], a[e], 0x05040100u);
-        const uint32_t hi = perm(b[e], a[e], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(s_q + (8 * cg + 2 * e) * kQPitch + 2 * tp) = lo;
-        *reinterpret_cast<uint32_t*>(s_q + (8 * cg + 2 * e + 1) * kQPitch + 2 * tp) = hi;
+        s_q[buf][grad_qslot(8 * cg + 2 * e, w)] = perm(b[e], a[e], 0x05040100u);
+        s_q[buf][grad_qslot(8 * cg + 2 * e + 1, w)] = perm(b[e], a[e], 0x07060302u);
       }
     }
-    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // 16 tokens per MFMA step
-      const int64_t tk = tb + 16 * s + 8 * h;
-#pragma unroll
-      for (int i = 0; i < kPerWave; ++i) {
-        const int tile = wv + 4 * i;
-        if (tile >= kTiles) continue;
-        const int jt = tile >> 1, ct = tile & 1;
-        const u32x4 qf = *reinterpret_cast<const u32x4*>(s_q + (32 * ct + r32) * kQPitch + 16 * s + 8 * h);
-        const int j = 32 * jt + r32;
-        u32x4 ph = zero4, pl = zero4;
-        if (tk < te && j < rp) {  // te - tk is a multiple of 8 except at the very end
-          const uint16_t* rh = Pt + static_cast<int64_t>(j) * ldt;
-          const uint16_t* rl = Pt + static_cast<int64_t>(rp + j) * ldt;
-          if (tk + 8 <= te) {
-            ph = *reinterpret_cast<const u32x4*>(rh + tk);
-            pl = *reinterpret_cast<const u32x4*>(rl + tk);
-          } else {
-            uint16_t hv[8], lv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const bool ok = tk + e < te;
-              hv[e] = ok ? rh[tk + e] : 0;
-              lv[e] = ok ? rl[tk + e] : 0;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ph[e] = hv[2 * e] | (static_cast<uint32_t>(hv[2 * e + 1]) << 16);
-              pl[e] = lv[2 * e] | (static_cast<uint32_t>(lv[2 * e + 1]) << 16);
-            }
-          }
-        }
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ph), as_bf16x8(qf), acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pl), as_bf16x8(qf), acc[i], 0, 0, 0);
-      }
+    for (int i = 0; i < 2 * JT; ++i) {
+      const int id = tid + 256 * i, prow = id >> 3, q = id & 7;
+      *reinterpret_cast<u32x4*>(&s_p[buf][kGradPitch * prow + 4 * q]) = pv[i];
     }
-    __syncthreads();
+  };
+
+  f32x16 acc[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[jt][e] = 0.f;
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+    if (nsteps > 1) load(1);
   }
-  // D[j][c]: lane holds column c = r32, rows j = 8*(e/4) + 4*h + e%4
+  const int c = 32 * wv + r32;
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    __syncthreads();  // stage buf complete, stage buf ^ 1 free
+    if (step + 1 < nsteps) {
+      store(buf ^ 1);
+      if (step + 2 < nsteps) load(step + 2);
+    }
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int tile = wv + 4 * i;
-    if (tile >= kTiles) continue;
-    const int jt = tile >> 1, ct = tile & 1;
-    const int64_t c = c0 + 32 * ct + r32;
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int w0 = 8 * s4 + 4 * h;
+      const u32x4 qf = *reinterpret_cast<const u32x4*>(&s_q[buf][grad_qslot(c, w0)]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = 32 * jt + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (j < r) {
-        float* dst = out_jc ? out + static_cast<int64_t>(j) * C + c : out + c * r + j;
-        atomicAdd(dst, acc[i][e]);
+      for (int jt = 0; jt < JT; ++jt) {
+        const u32x4 ph = *reinterpret_cast<const u32x4*>(&s_p[buf][kGradPitch * (32 * jt + r32) + w0]);
+        const u32x4 pl = *reinterpret_cast<const u32x4*>(&s_p[buf][kGradPitch * (32 * JT + 32 * jt + r32) + w0]);
+        if constexpr (kJC) {  // D[j][c]
+          acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ph), as_bf16x8(qf), acc[jt], 0, 0, 0);
+          acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pl), as_bf16x8(qf), acc[jt], 0, 0, 0);
+        } else {  // D[c][j]
+          acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qf), as_bf16x8(ph), acc[jt], 0, 0, 0);
+          acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qf), as_bf16x8(pl), acc[jt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if constexpr (kJC) {
+    // D[j][c]: lane holds column c, rows j = 8*(e/4) + 4*h + e%4
+    const int64_t cc = c0 + c;
+    if (cc >= C) return;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + 32 * jt + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (j < r) atomicAdd(out + static_cast<int64_t>(j) * C + cc, acc[jt][e]);
+      }
+  } else {
+    // D[c][j]: lane holds rank j, rows c = 8*(e/4) + 4*h + e%4 of the wave's tile
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const int j = j0 + 32 * jt + r32;
+      if (j >= r) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t cc = c0 + 32 * wv + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (cc < C) atomicAdd(out + cc * r + j, acc[jt][e]);
       }
     }
   }
@@ -229,16 +287,41 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
                             int64_t C, int64_t r, float* out, bool out_jc, hipStream_t s) {
-  const dim3 grid(static_cast<uint32_t>(C / 64), static_cast<uint32_t>(ceil_div(T, kGradSlice)));
-  const int jt = static_cast<int>(ceil_div(r, 32));
-  const int irp = static_cast<int>(rp), ir = static_cast<int>(r), jc = out_jc ? 1 : 0;
-#define QLORA_GRAD(JTV) hipLaunchKernelGGL((k_lora_grad<JTV>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ir, out, jc)
-  if (jt <= 1) QLORA_GRAD(1);
-  else if (jt <= 2) QLORA_GRAD(2);
-  else if (jt <= 4) QLORA_GRAD(4);
-  else QLORA_GRAD(8);
+  if (T <= 0) return hipSuccess;
+  // token slices (multiples of 64) for about 512 workgroups
+  const int64_t ctiles = ceil_div(C, kGradCT);
+  int64_t slices = ceil_div(512, ctiles);
+  const int64_t max_slices = ceil_div(T, 64);
+  if (slices > max_slices) slices = max_slices;
+  if (slices < 1) slices = 1;
+  // 32-bit buffer offsets: a slice of Q stays under 2^30 bytes, Pt under 2^31
+  const int64_t min_slices = ceil_div(T * C * 2, int64_t(1) << 30);
+  if (slices < min_slices) slices = min_slices;
+  if (2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int64_t TS = round_up(ceil_div(T, slices), 64);
+  slices = ceil_div(T, TS);
+  const dim3 grid(static_cast<uint32_t>(ctiles), static_cast<uint32_t>(slices));
+  const int irp = static_cast<int>(rp), ir = static_cast<int>(r);
+  for (int64_t j0 = 0; j0 < r; j0 += 32 * kGradMaxJT) {
+    const int64_t left = r - j0;
+    const int jt = static_cast<int>(ceil_div(left < 32 * kGradMaxJT ? left : 32 * kGradMaxJT, 32));
+    const int ij0 = static_cast<int>(j0);
+#define QLORA_GRAD(JTV, JC)                                                                          \
+  hipLaunchKernelGGL((k_lora_grad<JTV, JC>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ir, ij0, out, TS)
+    if (out_jc) {
+      if (jt <= 1) QLORA_GRAD(1, true);
+      else if (jt <= 2) QLORA_GRAD(2, true);
+      else QLORA_GRAD(4, true);
+    } else {
+      if (jt <= 1) QLORA_GRAD(1, false);
+      else if (jt <= 2) QLORA_GRAD(2, false);
+      else QLORA_GRAD(4, false);
+    }
 #undef QLORA_GRAD
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
