@@ -24,6 +24,7 @@ stream the library launches on (torch's current stream).
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,7 +45,48 @@ def parse():
     ap.add_argument("--pool", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--counters-probe", action="store_true",
+                    help="only run the T=16 small-token forward over the weight pool and a "
+                         "256 MiB copy (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
     return ap.parse_args()
+
+
+# Sources that define the small-token forward kernel; the HBM traffic recorded
+# from hardware counters is reported only while they are unchanged.
+DECODE_SOURCES = ("bit_nf4_quantized_20_amd/csrc/k_decode.hip",
+                  "bit_nf4_quantized_20_amd/csrc/nf4_format.hpp",
+                  "bit_nf4_quantized_20_amd/csrc/common.hpp",
+                  "bit_nf4_quantized_20_amd/build.py")
+TRAFFIC_RECORD = "profiles/k_decode_fwd_split_qproj4096x4096_T16_traffic.md"
+COPY_BYTES = 256 << 20
+
+
+def decode_fingerprint():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the T=16 small-token forward, from the counter
+    record in profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
+    counter reads for a copy of known size), or None when the record is
+    missing or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_RECORD)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256") != decode_fingerprint():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def decode_call_bytes(n_out, n_in, T, r):
@@ -86,6 +128,10 @@ def main():
     Y16 = torch.empty(16, n_out, dtype=torch.bfloat16, device=dev)
     ws = q.make_workspace(q.qlora_workspace_bytes(16, n_in, n_out, r, False), dev)
     torch.cuda.synchronize()
+
+    if args.counters_probe:
+        counters_probe(q, pool, X16, Y16, A, B, r, alpha, ws, dev)
+        return
 
     b1 = decode_call_bytes(n_out, n_in, 1, r)
     b16 = decode_call_bytes(n_out, n_in, 16, r)
@@ -207,12 +253,30 @@ def main():
                    "alpha": alpha, "weight_pool": P},
         "roofline": {"bound": "hbm", "kernel": "k_decode_fwd (T=16)", "achieved": round(ach16, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach16 / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
         "cpu_baseline": cpu,
         "extra": extra,
         "wall_s_timed_region": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def counters_probe(q, pool, X, Y, A, B, r, alpha, ws, dev):
+    """Workload of the counter passes: one T=16 forward on each pool weight
+    (64 launches, every one streaming its weight from HBM), then a plain
+    256 MiB fp32 copy (torch.neg into a second buffer: COPY_BYTES read and
+    COPY_BYTES written), whose counter readings calibrate the scale."""
+    import torch
+    for W in pool:
+        q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=ws)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "decode T=16 x %d, copy %d B x 4" % (len(pool), COPY_BYTES),
+                      "sources_sha256": decode_fingerprint()}), flush=True)
 
 
 def train_leg(q, synth, dev, bf):
