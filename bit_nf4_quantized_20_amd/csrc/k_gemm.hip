@@ -3,25 +3,39 @@
 //   C[M][N] = sum_k act0[m][k] wt0[n][k]  +  sum_k act1[m][k] wt1[n][k]
 // The main segment's weight operand is either a bf16 matrix or an NF4 weight
 // (codes + double-quantized absmax) that is dequantized while it is staged
-// into LDS: each thread turns 32 packed codes of one block into bf16 with the
-// block's v_perm table and writes them straight into the swizzled LDS tile,
-// so W_hat never exists in HBM (ultralytics glossary "QLoRA": the frozen
-// weight is dequantized to bfloat16 right before the matmul; paperclase
-// lesson "QLoRA", Parte 4: W_hat is built, used and discarded).
+// into LDS: each thread turns packed codes of one 64-weight block into bf16
+// with the block's v_perm table and writes them straight into the swizzled
+// LDS tile, so W_hat never exists in HBM (ultralytics glossary "QLoRA": the
+// frozen weight is dequantized to bfloat16 right before the matmul;
+// paperclase lesson "QLoRA", Parte 4: W_hat is built, used and discarded).
 // The second segment carries the LoRA term as extra K-steps (act1 = s*U or
 // s*V as a bf16 hi/lo pair, wt1 = B or A^T padded to match), so base and
 // adapter products share one fp32 accumulator and Y / dX are rounded once.
 //
-// Tile BM x BN, K-step 64 (whole 128-byte lines per tile row: half-line
-// steps measured markedly slower), two LDS stages and two register stages:
-// the tiles of step st + 3 are loaded into registers while step st is
-// computed and written into LDS two steps later, so ~128 KB of loads are in
-// flight per CU (the loads are latency bound; ordinary loads into registers
-// measured faster here than copies straight into LDS).  One barrier per
-// K-step.  v_mfma_f32_32x32x16_bf16; the MFMA A operand is the weight tile
-// (rows n), its B operand the activation tile (rows m), so each lane ends up
-// holding 4 consecutive n of one output row m and stores them as one 8-byte
-// write.
+// Two kernels, both v_mfma_f32_32x32x16_bf16 with the weight tile as the
+// MFMA A operand (rows n) and the activation tile as B (rows m), so each lane
+// ends up holding 4 consecutive n of one output row m (one 8-byte store):
+//
+// k_gemm_big (grids of >= 256 tiles): 256 x 256 x 64 tiles, 8 waves (2 x 4,
+// 128 x 64 each, two per SIMD).  bf16 tiles go from global memory straight
+// into LDS (buffer_load ... lds: one 1 KB block of 8 rows per wave
+// instruction, the swizzle applied on the global side), so they take no
+// registers and no LDS-write instructions.  Two LDS stages, each a separate
+// __shared__ array and the stage index a compile-time constant in the
+// unrolled loop, so the compiler can see that the copies into one stage do
+// not alias the fragment reads of the other and does not make every LDS
+// read wait for the copies in flight.  Step e: copy step e+1 into the other
+// stage, compute step e (fragments of sub-step j+1 read during sub-step j),
+// one barrier at the end.  An NF4 weight is loaded into registers three
+// steps ahead (three register sets) and dequantized into the other stage a
+// quarter per sub-step, between the MFMAs; the barrier waits only for the
+// copies, not for those code loads.
+//
+// k_gemm (smaller grids): 128 x 128 x 64 tiles, 4 waves, tiles staged
+// through two register sets (three K-steps of loads in flight) and two LDS
+// stages, one barrier per K-step.
+#include <type_traits>
+
 #include "common.hpp"
 #include "nf4_format.hpp"
 
@@ -95,7 +109,7 @@ template <int ROWS, int NT>
 struct Nf4Tile {
   static constexpr int kTPR = NT / ROWS;  // threads per row
   static constexpr int kDw = 8 / kTPR;    // code dwords (8 weights each) per thread
-  static_assert(kTPR == 2 || kTPR == 4, "unsupported tile");
+  static_assert(kTPR == 1 || kTPR == 2 || kTPR == 4, "unsupported tile");
   struct Regs {
     uint32_t cw[kDw];
     uint32_t q;
@@ -119,7 +133,12 @@ struct Nf4Tile {
     blk0 = g * (in / 64);
   }
   __device__ __forceinline__ void load(Regs& r, int64_t k0) const {
-    if constexpr (kDw == 4) {
+    if constexpr (kDw == 8) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff, static_cast<int>(k0 / 2), kStream));
+      const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff + 16, static_cast<int>(k0 / 2), kStream));
+      r.cw[0] = v[0]; r.cw[1] = v[1]; r.cw[2] = v[2]; r.cw[3] = v[3];
+      r.cw[4] = w[0]; r.cw[5] = w[1]; r.cw[6] = w[2]; r.cw[7] = w[3];
+    } else if constexpr (kDw == 4) {
       const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff, static_cast<int>(k0 / 2), kStream));
       r.cw[0] = v[0]; r.cw[1] = v[1]; r.cw[2] = v[2]; r.cw[3] = v[3];
     } else {
@@ -139,6 +158,43 @@ struct Nf4Tile {
       const int chunk = part * kDw + d;
       *reinterpret_cast<u32x4*>(lds + row * kBK + swz(row, chunk) * 8) = u32x4{o[0], o[1], o[2], o[3]};
     }
+  }
+  // The same in pieces: the block's table once, then code dword d -> one
+  // 16-byte chunk of the LDS tile.
+  __device__ __forceinline__ static Nf4Table table(const Regs& r) { return make_table(dq_absmax(r.q, r.sg)); }
+  __device__ __forceinline__ static void store_part(const Regs& r, const Nf4Table& tab, uint16_t* lds, int tid, int d) {
+    const int row = tid / kTPR, part = tid % kTPR;
+    uint32_t o[4];
+    lookup8(tab, r.cw[d], o);
+    const int chunk = part * kDw + d;
+    *reinterpret_cast<u32x4*>(lds + row * kBK + swz(row, chunk) * 8) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+};
+
+// bf16 tile rows [ROWS][64] of a K-contiguous matrix copied straight into
+// LDS by NW waves: ROWS/8 blocks of 1 KB, one wave instruction each.  Lane L
+// of a block lands at LDS byte 16 L of the block, i.e. row 8 blk + L/8,
+// position L % 8, so it loads the global chunk that the swizzle puts there
+// (the XOR swizzle is its own inverse).  Rows past the matrix read as zero.
+template <int ROWS, int NW>
+struct DtlTile {
+  static constexpr int kPerWave = ROWS / 8 / NW;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[kPerWave];
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t row0, int64_t nrows, int wv, int lane) {
+    rs = rows_rsrc(base, ld, row0, nrows, 2);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int row = (i * NW + wv) * 8 + (lane >> 3);
+      voff[i] = static_cast<uint32_t>((row * ld + swz(row, lane & 7) * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void load(uint16_t* lds, int wv, int64_t k0) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + (i * NW + wv) * 512), 16, voff[i],
+          static_cast<int>(k0 * 2), 0, 0);
   }
 };
 
@@ -343,16 +399,222 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   }
 }
 
+// 256 x 256 tiles, 8 waves (see the file comment).  Launch: 512 threads.
+template <bool kNf4>
+__global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
+  constexpr int NW = 8, NT = 64 * NW, BM = 256, BN = 256;
+  constexpr int FN = 2, WN = 64, FM = 4, WM = 128;  // wave tile 128 (m) x 64 (n)
+  __shared__ __attribute__((aligned(1024))) uint16_t s_act0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_act1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_wt0[BN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_wt1[BN * kBK];
+  uint16_t* const s_act[2] = {s_act0, s_act1};
+  uint16_t* const s_wt[2] = {s_wt0, s_wt1};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv & 1, wn = wv >> 1;
+  int64_t mt, nt;
+  xcd_tile(gridDim.x, gridDim.y, mt, nt);
+  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int r32 = lane & 31, half = lane >> 5;
+
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int c = 0; c < FM; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.f;
+
+  typedef bf16x8 Frags[FN + FM];  // [0, FN) weight rows, [FN, FN + FM) activation rows
+  auto read_frags = [&](Frags& f, const uint16_t* sw, const uint16_t* sa, int j) {
+    const int chunk = 2 * j + half;
+#pragma unroll
+    for (int a = 0; a < FN; ++a) f[a] = lds_frag(sw, wn * WN + a * 32 + r32, chunk);
+#pragma unroll
+    for (int c = 0; c < FM; ++c) f[FN + c] = lds_frag(sa, wm * WM + c * 32 + r32, chunk);
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int c = 0; c < FM; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[a], f[FN + c], acc[a][c], 0, 0, 0);
+  };
+  // scheduling hint for one sub-step: each MFMA followed by at most one LDS
+  // read, one LDS write, one global load and eight vector-ALU instructions
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < FN * FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+
+  // Main segment.  TW: DtlTile (bf16 weight) or Nf4Tile (codes in registers).
+  auto main_loop = [&](DtlTile<BM, NW>& ta, auto& tw, int64_t steps) {
+    using TW = std::remove_reference_t<decltype(tw)>;
+    constexpr bool kRegW = !std::is_same_v<TW, DtlTile<BN, NW>>;
+    struct NoRegs { };
+    using WRegs = std::conditional_t<kRegW, typename Nf4Tile<BN, NT>::Regs, NoRegs>;
+    const int64_t last = steps - 1;
+    WRegs wr[3];
+    auto wfetch = [&](WRegs& r, int64_t e) {  // steps past the end re-read the last one
+      if constexpr (kRegW) tw.load(r, (e < last ? e : last) * kBK);
+    };
+    auto copy = [&](int64_t e, uint16_t* sa, uint16_t* sw) {
+      const int64_t k = (e < last ? e : last) * kBK;
+      ta.load(sa, wv, k);
+      if constexpr (!kRegW) tw.load(sw, wv, k);
+    };
+    wfetch(wr[0], 0);
+    wfetch(wr[1], 1);
+    wfetch(wr[2], 2);
+    copy(0, s_act0, s_wt0);
+    if constexpr (kRegW) TW::store(wr[0], s_wt0, tid);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    Frags f0, f1;
+    read_frags(f0, s_wt0, s_act0, 0);
+    // Step e: stage B holds step e; code set (C + 1) % 3 holds step e + 1 and
+    // set C (step e's, consumed) takes step e + 3.
+    auto step = [&](int64_t e, auto bc, auto cc) {
+      constexpr int B = decltype(bc)::value, C = decltype(cc)::value;
+      uint16_t* const sa = s_act[B];
+      uint16_t* const sw = s_wt[B];
+      uint16_t* const na = s_act[B ^ 1];
+      uint16_t* const nw = s_wt[B ^ 1];
+      WRegs& nxt = wr[(C + 1) % 3];
+      Nf4Table tab{};
+      auto part = [&](int d) {  // a quarter of step e+1's weight tile
+        if constexpr (kRegW) {
+          if constexpr (TW::kDw == 4) {
+            TW::store_part(nxt, tab, nw, tid, d);
+          } else {
+            TW::store_part(nxt, tab, nw, tid, 2 * d);
+            TW::store_part(nxt, tab, nw, tid, 2 * d + 1);
+          }
+        }
+      };
+      copy(e + 1, na, nw);
+      wfetch(wr[C], e + 3);
+      if constexpr (kRegW) tab = TW::table(nxt);
+      part(0);
+      read_frags(f1, sw, sa, 1);
+      mfmas(f0);
+      interleave();
+      part(1);
+      read_frags(f0, sw, sa, 2);
+      mfmas(f1);
+      interleave();
+      part(2);
+      read_frags(f1, sw, sa, 3);
+      mfmas(f0);
+      interleave();
+      part(3);
+      mfmas(f1);
+      interleave();
+      // stage B^1 complete and stage B free: wait for this wave's copies and
+      // LDS writes (the code loads issued after the copies, 3 instructions,
+      // may stay in flight), then the barrier
+      if constexpr (kRegW) __builtin_amdgcn_s_waitcnt(0x73);  // vmcnt(3) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      read_frags(f0, nw, na, 0);
+    };
+    int64_t e = 0;
+    for (; e + 6 <= steps; e += 6) {
+      step(e, I0{}, I0{});
+      step(e + 1, I1{}, I1{});
+      step(e + 2, I0{}, I2{});
+      step(e + 3, I1{}, I0{});
+      step(e + 4, I0{}, I1{});
+      step(e + 5, I1{}, I2{});
+    }
+    const int64_t rem = steps - e;
+    if (rem > 0) step(e, I0{}, I0{});
+    if (rem > 1) step(e + 1, I1{}, I1{});
+    if (rem > 2) step(e + 2, I0{}, I2{});
+    if (rem > 3) step(e + 3, I1{}, I0{});
+    if (rem > 4) step(e + 4, I0{}, I1{});
+  };
+
+  const int64_t s0 = p.K0 / kBK, s1 = p.K1 / kBK;
+  DtlTile<BM, NW> ta;
+  ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
+  if constexpr (kNf4) {
+    Nf4Tile<BN, NT> tq;
+    tq.init(p.codes, p.absmax_q, p.scale, p.K0, n0, p.N, tid);
+    main_loop(ta, tq, s0);
+  } else {
+    DtlTile<BN, NW> tw;
+    tw.init(p.wt0, p.ldw0, n0, p.N, wv, lane);
+    main_loop(ta, tw, s0);
+  }
+
+  // LoRA extension segment (a few steps): copy, barrier, compute
+  if (s1 > 0) {
+    DtlTile<BM, NW> ta1;
+    DtlTile<BN, NW> tw1;
+    ta1.init(p.act1, p.lda1, m0, p.M, wv, lane);
+    tw1.init(p.wt1, p.ldw1, n0, p.N, wv, lane);
+    for (int64_t e = 0; e < s1; ++e) {
+      __syncthreads();  // every wave is done reading stage 0
+      ta1.load(s_act0, wv, e * kBK);
+      tw1.load(s_wt0, wv, e * kBK);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Frags f;
+        read_frags(f, s_wt0, s_act0, j);
+        mfmas(f);
+      }
+    }
+  }
+
+  // epilogue: D[n][m] -> C[m][n]; lane holds m = r32, n = 8*(e/4) + 4*half + e%4
+#pragma unroll
+  for (int c = 0; c < FM; ++c) {
+    const int64_t m = m0 + wm * WM + c * 32 + r32;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * WN + a * 32 + 8 * g + 4 * half;
+        if (n < p.N) {
+          const uint32_t p0 = pack_bf16x2(acc[a][c][4 * g + 0], acc[a][c][4 * g + 1]);
+          const uint32_t p1 = pack_bf16x2(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(p.C + m * p.ldc + n) = u32x2{p0, p1};
+        }
+      }
+    }
+  }
+}
+
+// (explicit instantiations: the host-side launch stubs of these templates are
+// otherwise not always emitted)
+template __global__ void k_gemm_big<false>(GemmArgs);
+template __global__ void k_gemm_big<true>(GemmArgs);
+
 namespace {
 template <bool kNf4>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
-
   // 256 x 256 tiles (8 waves) when they give at least one full wave of
   // workgroups, else 128 x 128 (4 waves)
   const int64_t big = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   if (big >= 256) {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 256)), static_cast<uint32_t>(ceil_div(a.N, 256)));
-    hipLaunchKernelGGL((k_gemm<256, 256, 2, 4, kNf4>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_big<kNf4>), grid, dim3(512), 0, s, a);
   } else {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 128)), static_cast<uint32_t>(ceil_div(a.N, 128)));
     hipLaunchKernelGGL((k_gemm<128, 128, 2, 2, kNf4>), grid, dim3(256), 0, s, a);
