@@ -53,9 +53,11 @@ hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t*
 // 0 for r <= j < rp, as bf16 pairs hi + lo.  Written to (either may be null)
 //   pad    [T][2*rp]   hi in columns [0, rp), lo in [rp, 2*rp)
 //   hilo_t [2*rp][ldt] transposed: hi rows [0, rp), lo rows [rp, 2*rp)
+// `part` is fp32 scratch of lora_down_part_bytes(T, K, rp) bytes.  K % 64 == 0.
+size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t rp);
 hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* P, int64_t r,
                             float scale, uint16_t* pad, uint16_t* hilo_t, int64_t ldt, int64_t rp,
-                            hipStream_t s);
+                            float* part, hipStream_t s);
 // out(j, c) += sum_t (Pt[j][t] + Pt[rp + j][t]) Q[t][c] for j < r, c < C (C % 64
 // == 0), atomically into out[j * C + c] (out_jc) or out[c * r + j].
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,

@@ -18,113 +18,228 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// lora_down: D[j][t] = sum_k P[j][k] in[t][k] for 16 tokens per workgroup and
-// all ranks.  4 waves split K in 32-wide slices (wave w takes slices w, w+4,
-// ...); per slice a lane (n = l%16, g = l/16) loads 8 activations of token
-// t0+n and 8 weights of rank row 16*rt+n, and each rank tile issues one
-// v_mfma_f32_16x16x32_bf16.  Partial tiles meet in LDS.
+// lora_down: sU = scale * in P^T for in [T][K] (X or dY) and P [r][K] (A or
+// B^T), written as bf16 hi/lo pairs.  A skinny GEMM (r <= 256 columns) bound
+// by streaming `in` once, so the work is split in two dimensions: a
+// workgroup takes 128 tokens x 64 ranks x one K-chunk, so P is re-read only
+// once per 128 tokens and the grid still has ~256 workgroups.  Each writes
+// its fp32 partial tile; k_lora_down_fin adds the K-chunks in a fixed order
+// (deterministic), scales, splits hi/lo and writes the padded / transposed
+// layouts.
+//
+// Partial kernel: 4 waves (2 x 2; 64 tokens x 32 ranks each), K-step 64,
+// tiles through registers into a double-buffered swizzled LDS stage (one
+// barrier per step), v_mfma_f32_32x32x16_bf16 with the rank rows as the A
+// operand, so a lane holds 16 ranks of one token and stores them as four
+// 16-byte writes.
 // ---------------------------------------------------------------------------
-template <int RT>
-__global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ in, int64_t T,
-                                                   int64_t K, const uint16_t* __restrict__ P,
-                                                   int r, float scale, uint16_t* __restrict__ pad,
-                                                   uint16_t* __restrict__ hilo_t, int64_t ldt,
-                                                   int rp) {
-  __shared__ f32x4v red[4][RT][64];
+constexpr int kDownTok = 128;   // tokens per workgroup
+constexpr int kDownRanks = 64;  // ranks per workgroup
+constexpr int kDownBufWord3 = 0x00020000;
+
+namespace {
+__device__ __forceinline__ int down_swz(int row, int chunk) { return chunk ^ ((row & 7) ^ ((row >> 3) & 1)); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t down_rsrc(const uint16_t* base, int64_t ld, int64_t row0,
+                                                            int64_t nrows) {
+  const uint64_t bytes = static_cast<uint64_t>(nrows > row0 ? nrows - row0 : 0) * ld * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + row0 * ld), 0,
+                                           static_cast<int>(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+                                           kDownBufWord3);
+}
+}  // namespace
+
+// part[kc][t][j] (fp32, [KC][T][rp]) = sum over chunk kc of in[t][k] P[j][k]
+__global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restrict__ in, int64_t T,
+                                                        int64_t K, const uint16_t* __restrict__ P,
+                                                        int r, int rp, int64_t kch,
+                                                        float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kDownTok * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[2][kDownRanks * 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const bool tok_ok = t0 + n < T;
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const int wm = wv & 1, wn = wv >> 1;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kDownTok;
+  const int64_t kc = blockIdx.y;
+  const int j0 = static_cast<int>(blockIdx.z) * kDownRanks;
+  const int64_t kbeg = kc * kch;
+  const int64_t kend = kbeg + kch < K ? kbeg + kch : K;
+  const int nsteps = static_cast<int>((kend - kbeg) / 64);
 
-  f32x4v acc[RT];
+  // rows past T (tokens) or r (ranks) read as zero
+  const __amdgpu_buffer_rsrc_t rs_x = down_rsrc(in, K, t0, T);
+  const __amdgpu_buffer_rsrc_t rs_p = down_rsrc(P, K, j0, r);
+  uint32_t xoff[4], poff[2];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t slices = K / 32;
-  const uint16_t* xrow = in + (t0 + n) * K + 8 * g;
-  int64_t sl = wv;
-  // two slices per iteration so the loads of both are in flight together
-  for (; sl + 4 < slices; sl += 8) {
-    const int64_t k0 = sl * 32, k1 = (sl + 4) * 32;
-    const u32x4 x0 = tok_ok ? *reinterpret_cast<const u32x4*>(xrow + k0) : zero4;
-    const u32x4 x1 = tok_ok ? *reinterpret_cast<const u32x4*>(xrow + k1) : zero4;
-    u32x4 p0[RT], p1[RT];
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i, row = id >> 3, q = id & 7;
+    xoff[i] = static_cast<uint32_t>((row * K + q * 8) * 2);
+  }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int j = rt * 16 + n;
-      const uint16_t* prow = P + static_cast<int64_t>(j) * K + 8 * g;
-      p0[rt] = j < r ? *reinterpret_cast<const u32x4*>(prow + k0) : zero4;
-      p1[rt] = j < r ? *reinterpret_cast<const u32x4*>(prow + k1) : zero4;
+  for (int i = 0; i < 2; ++i) {
+    const int id = tid + 256 * i, row = id >> 3, q = id & 7;
+    poff[i] = static_cast<uint32_t>((row * K + q * 8) * 2);
+  }
+  u32x4 xv[4], pv[2];
+  auto load = [&](int st) {
+    const int so = static_cast<int>((kbeg + 64 * static_cast<int64_t>(st)) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xoff[i], so, 0));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, poff[i], so, 0));
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + 256 * i, row = id >> 3, q = id & 7;
+      *reinterpret_cast<u32x4*>(&s_x[b][row * 64 + down_swz(row, q) * 8]) = xv[i];
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0[rt]), as_bf16x8(x0), acc[rt], 0, 0, 0);
-      acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1[rt]), as_bf16x8(x1), acc[rt], 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + 256 * i, row = id >> 3, q = id & 7;
+      *reinterpret_cast<u32x4*>(&s_p[b][row * 64 + down_swz(row, q) * 8]) = pv[i];
     }
-  }
-  for (; sl < slices; sl += 4) {
-    const int64_t k0 = sl * 32;
-    const u32x4 x0 = tok_ok ? *reinterpret_cast<const u32x4*>(xrow + k0) : zero4;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int j = rt * 16 + n;
-      const u32x4 p0 = j < r ? *reinterpret_cast<const u32x4*>(P + static_cast<int64_t>(j) * K + 8 * g + k0) : zero4;
-      acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), as_bf16x8(x0), acc[rt], 0, 0, 0);
-    }
-  }
+  };
+  auto frag = [&](const uint16_t* base, int row, int chunk) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(base + row * 64 + down_swz(row, chunk) * 8));
+  };
 
-  // lane holds D[16*rt + 4*g + i][n], i = 0..3
+  f32x16 acc[2];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) red[wv][rt][lane] = acc[rt];
-  __syncthreads();
-  // thread -> (token tt = tid % 16, rank j = tid / 16 + 16 * m)
-  const int tt = tid & 15;
-  const int64_t t = t0 + tt;
-  if (t >= T) {  // padding tokens of the transposed copy read as zero
-    if (hilo_t != nullptr && t < ldt)
-      for (int j = tid >> 4; j < rp; j += 16) {
-        hilo_t[static_cast<int64_t>(j) * ldt + t] = 0;
-        hilo_t[static_cast<int64_t>(rp + j) * ldt + t] = 0;
-      }
-    return;
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+    if (nsteps > 1) load(1);
   }
-  for (int j = tid >> 4; j < rp; j += 16) {
+  for (int st = 0; st < nsteps; ++st) {
+    const int b = st & 1;
+    __syncthreads();  // stage b complete, stage b ^ 1 free
+    if (st + 1 < nsteps) {
+      store(b ^ 1);
+      if (st + 2 < nsteps) load(st + 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int chunk = 2 * j + h;
+      const bf16x8 fp = frag(s_p[b], wn * 32 + r32, chunk);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp, frag(s_x[b], wm * 64 + c * 32 + r32, chunk), acc[c], 0, 0, 0);
+    }
+  }
+  // D[rank][token]: lane holds token r32 of tile c, ranks 8 (e/4) + 4 h + e%4
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int64_t t = t0 + wm * 64 + c * 32 + r32;
+    if (t >= T) continue;
+    float* dst = part + (kc * T + t) * rp + j0 + wn * 32 + 4 * h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if (j0 + wn * 32 + 8 * g + 4 * h < rp)
+        *reinterpret_cast<f32x4v*>(dst + 8 * g) =
+            f32x4v{acc[c][4 * g], acc[c][4 * g + 1], acc[c][4 * g + 2], acc[c][4 * g + 3]};
+  }
+}
+
+// Sums the KC (<= kDownMaxKC) partials in order, scales and writes sU as
+// bf16 hi/lo pairs:
+//   pad    [T][2 rp]      hi in columns [0, rp), lo in [rp, 2 rp)
+//   hilo_t [2 rp][ldt]    transposed; tokens [T, ldt) are zero
+// One workgroup per 16 tokens x 64 ranks (4 per thread, the KC loads of one
+// value issued together); the transposed copy goes through an LDS tile so
+// both stores are coalesced.
+constexpr int kDownMaxKC = 16;
+__global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__ part, int64_t T, int KC,
+                                                       int rp, float scale, uint16_t* __restrict__ pad,
+                                                       uint16_t* __restrict__ hilo_t, int64_t ldt) {
+  __shared__ uint32_t s_t[64][17];  // [rank][token] hi | lo << 16
+  const int tid = threadIdx.x;
+  const int64_t tb = static_cast<int64_t>(blockIdx.x) * 16;
+  const int jb = static_cast<int>(blockIdx.y) * 64;
+  // phase 1: thread -> rank jb + tid % 64, tokens tb + tid / 64 + 4 i
+  const int jl = tid & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tl = (tid >> 6) + 4 * i;
+    const int64_t t = tb + tl;
+    const bool ok = t < T && jb + jl < rp;
+    float pv[kDownMaxKC];
+#pragma unroll
+    for (int q = 0; q < kDownMaxKC; ++q)
+      pv[q] = (ok && q < KC) ? part[(static_cast<int64_t>(q) * T + t) * rp + jb + jl] : 0.f;
     float v = 0.f;
-    if (j < 16 * RT) {
-      const int rt = j >> 4, gi = (j & 15) >> 2, i = j & 3;
-      const int l = tt + 16 * gi;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += red[w][rt][l][i];
+    for (int q = 0; q < kDownMaxKC; ++q) v += pv[q];
+    v *= scale;
+    const uint32_t hb = pack_bf16x2(v, 0.f) & 0xffffu;
+    const float hi = __builtin_bit_cast(float, hb << 16);
+    const uint32_t lb = pack_bf16x2(v - hi, 0.f) & 0xffffu;
+    if (ok && pad != nullptr) {
+      pad[t * 2 * rp + jb + jl] = static_cast<uint16_t>(hb);
+      pad[t * 2 * rp + rp + jb + jl] = static_cast<uint16_t>(lb);
     }
-    v *= scale;  // zero for j >= r (rows of P beyond r are zero)
-    const float hi = __builtin_bit_cast(float, static_cast<uint32_t>(pack_bf16x2(v, 0.f)) << 16);
-    const uint16_t hb = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
-    const uint16_t lb = static_cast<uint16_t>(pack_bf16x2(v - hi, 0.f) & 0xffffu);
-    if (pad != nullptr) {
-      pad[t * 2 * rp + j] = hb;
-      pad[t * 2 * rp + rp + j] = lb;
-    }
-    if (hilo_t != nullptr) {
-      hilo_t[static_cast<int64_t>(j) * ldt + t] = hb;
-      hilo_t[static_cast<int64_t>(rp + j) * ldt + t] = lb;
-    }
+    s_t[jl][tl] = hb | (lb << 16);  // tokens >= T hold zero
   }
+  if (hilo_t == nullptr) return;
+  __syncthreads();
+  // phase 2: thread -> token tb + tid % 16, ranks jb + tid / 16 + 16 i
+  const int tl = tid & 15;
+  const int64_t t = tb + tl;
+  if (t >= ldt) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = (tid >> 4) + 16 * i;
+    if (jb + j >= rp) break;
+    const uint32_t v = s_t[j][tl];
+    hilo_t[static_cast<int64_t>(jb + j) * ldt + t] = static_cast<uint16_t>(v & 0xffffu);
+    hilo_t[static_cast<int64_t>(rp + jb + j) * ldt + t] = static_cast<uint16_t>(v >> 16);
+  }
+}
+
+namespace {
+// K-chunk length (a multiple of 64) for about 256 partial workgroups (at
+// most kDownMaxKC chunks)
+int64_t down_chunk(int64_t T, int64_t K, int64_t rp) {
+  const int64_t tiles = ceil_div(T, kDownTok) * ceil_div(rp, kDownRanks);
+  if (tiles <= 0 || K <= 0) return 64;  // no tokens: nothing is launched
+  int64_t kc = ceil_div(256, tiles);
+  const int64_t steps = K / 64;
+  if (kc > kDownMaxKC) kc = kDownMaxKC;
+  if (kc > steps) kc = steps;
+  if (kc < 1) kc = 1;
+  return ceil_div(steps, kc) * 64;
+}
+}  // namespace
+
+size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t rp) {
+  const int64_t kch = down_chunk(T, K, rp);
+  return static_cast<size_t>(ceil_div(K, kch) * T * rp * 4);
 }
 
 hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* P, int64_t r,
                             float scale, uint16_t* pad, uint16_t* hilo_t, int64_t ldt, int64_t rp,
-                            hipStream_t s) {
-  const dim3 grid(static_cast<uint32_t>(ceil_div(T, 16))), block(256);
-  const int rt = static_cast<int>(ceil_div(r, 16));
-  const int ir = static_cast<int>(r), irp = static_cast<int>(rp);
-#define QLORA_DOWN(RTV) hipLaunchKernelGGL((k_lora_down<RTV>), grid, block, 0, s, in, T, K, P, ir, scale, pad, hilo_t, ldt, irp)
-  if (rt <= 1) QLORA_DOWN(1);
-  else if (rt <= 2) QLORA_DOWN(2);
-  else if (rt <= 4) QLORA_DOWN(4);
-  else if (rt <= 8) QLORA_DOWN(8);
-  else QLORA_DOWN(16);
-#undef QLORA_DOWN
+                            float* part, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  // 32-bit buffer offsets: one tile's rows of `in` and P stay under 2^31 bytes
+  if (kDownTok * K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int64_t kch = down_chunk(T, K, rp);
+  const int64_t KC = ceil_div(K, kch);
+  const dim3 grid(static_cast<uint32_t>(ceil_div(T, kDownTok)), static_cast<uint32_t>(KC),
+                  static_cast<uint32_t>(ceil_div(rp, kDownRanks)));
+  hipLaunchKernelGGL(k_lora_down_part, grid, dim3(256), 0, s, in, T, K, P, static_cast<int>(r),
+                     static_cast<int>(rp), kch, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tt = hilo_t != nullptr ? (ldt > T ? ldt : T) : T;
+  const dim3 fgrid(static_cast<uint32_t>(ceil_div(tt, 16)), static_cast<uint32_t>(ceil_div(rp, 64)));
+  hipLaunchKernelGGL(k_lora_down_fin, fgrid, dim3(256), 0, s, part, T, static_cast<int>(KC),
+                     static_cast<int>(rp), scale, pad, hilo_t, ldt);
   return hipGetLastError();
 }
 

@@ -53,10 +53,10 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t u_pad, b_pad, total;
+  size_t u_pad, b_pad, part, total;
 };
 struct BwdLayout {
-  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, total;
+  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, total;
 };
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
@@ -64,12 +64,13 @@ int64_t padded_rank(int64_t r) { return round_up(r, 64); }
 bool fwd_uses_decode(int64_t T, int64_t in, int64_t out, int64_t r) { return decode_fits(T, in, out, r); }
 
 FwdLayout fwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
-  FwdLayout l{0, 0, 0};
+  FwdLayout l{0, 0, 0, 0};
   Carve c;
   if (fwd_uses_decode(T, in, out, r)) return l;  // the fused small-token kernel needs none
   const int64_t rp = padded_rank(r);
   l.u_pad = c.take(static_cast<size_t>(T * rp * 4));
   l.b_pad = c.take(static_cast<size_t>(out * rp * 4));
+  l.part = c.take(lora_down_part_bytes(T, in, rp));
   l.total = c.off;
   return l;
 }
@@ -86,6 +87,8 @@ BwdLayout bwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
   l.b_t = c.take(static_cast<size_t>(r * out * 2));
   l.a_t_pad = c.take(static_cast<size_t>(in * rp * 4));
   l.w_dq_t = c.take(static_cast<size_t>(in * out * 2));
+  const size_t pu = lora_down_part_bytes(T, in, rp), pv = lora_down_part_bytes(T, out, rp);
+  l.part = c.take(pu > pv ? pu : pv);
   l.total = c.off;
   return l;
 }
@@ -178,7 +181,8 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* u_pad = reinterpret_cast<uint16_t*>(base + lay.u_pad);
   uint16_t* b_pad = reinterpret_cast<uint16_t*>(base + lay.b_pad);
-  hipError_t e = launch_lora_down(X, T, in, A, r, scale, u_pad, nullptr, 0, rp, s);  // s X A^T
+  float* part = reinterpret_cast<float*>(base + lay.part);
+  hipError_t e = launch_lora_down(X, T, in, A, r, scale, u_pad, nullptr, 0, rp, part, s);  // s X A^T
   if (e == hipSuccess) e = launch_pad_bf16(B, out, r, false, b_pad, rp, s);
   if (e == hipSuccess)
     e = launch_gemm_nf4(T, out, X, in, W->codes, W->absmax_q, W->absmax_scale, in, u_pad, 2 * rp,
@@ -219,9 +223,10 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora
   uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(base + lay.a_t_pad);
   uint16_t* w_dq_t = reinterpret_cast<uint16_t*>(base + lay.w_dq_t);
 
-  e = launch_lora_down(X, T, in, A, r, scale, nullptr, ut, tp, rp, s);                 // (sU)^T
+  float* part = reinterpret_cast<float*>(base + lay.part);
+  e = launch_lora_down(X, T, in, A, r, scale, nullptr, ut, tp, rp, part, s);           // (sU)^T
   if (e == hipSuccess) e = launch_transpose_bf16(B, out, r, b_t, s);                  // B^T [r][out]
-  if (e == hipSuccess) e = launch_lora_down(dY, T, out, b_t, r, scale, v_pad, vt, tp, rp, s);  // sV
+  if (e == hipSuccess) e = launch_lora_down(dY, T, out, b_t, r, scale, v_pad, vt, tp, rp, part, s);  // sV
   if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, s);           // A^T padded
   if (e == hipSuccess)
     e = launch_nf4_dequantize_transposed(W->codes, W->absmax_q, W->absmax_scale, out, in, w_dq_t, s);

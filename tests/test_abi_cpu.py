@@ -154,9 +154,13 @@ def test_linear_validation():
     lib = _api(_lib())
     F = _FAKE
     W = _W(F, F, F, 128, 256)
-    # both forward paths (small-token split-K partials, large-token LoRA
-    # factors) use the workspace
+    # the large-token forward needs a workspace (LoRA factors, split-K
+    # partials of the rank-r product); the small-token one none, but every
+    # valid shape reports at least 256 bytes, T = 0 included
     assert lib.qlora_workspace_bytes(16, 256, 128, 8, 0) > 0
+    assert lib.qlora_workspace_bytes(0, 256, 128, 8, 0) >= 256
+    assert lib.qlora_workspace_bytes(0, 256, 128, 8, 1) >= 256
+    assert lib.qlora_workspace_bytes(4096, 4096, 14336, 64, 1) > 4096 * 14336 * 2
     assert lib.qlora_workspace_bytes(16, 256, 128, 65, 0) > 0
     ws = lib.qlora_workspace_bytes(32, 256, 128, 8, 0)
     wsb = lib.qlora_workspace_bytes(16, 256, 128, 8, 1)
