@@ -13,8 +13,9 @@ value = NF4 weight-stream throughput of the step, in GB/s of algorithmic
 bytes (packed codes + 8-bit absmax + group scales + X + Y + A + B per call).
 
 Also reported ("extra"): nf4_quantize of the 4096 x 4096 fp32 weight and
-fwd+bwd TFLOP/s of the 8B-MLP gate projection (14336 x 4096, T = 4096,
-r = 64) -- the large-token half of the metric; skipped with --no-train.
+fwd+bwd TFLOP/s of the 8B-MLP projections (gate, up 4096 -> 14336, down
+14336 -> 4096; T = 4096, r = 64) -- the large-token half of the metric;
+skipped with --no-train.
 
 The roofline entry is for the dominant kernel, the fused small-token forward
 (one launch per call); its average duration comes from HIP events on the
@@ -227,7 +228,7 @@ def main():
 
     # ------------------------------------------- large-token fwd + bwd
     if not args.no_train:
-        extra["mlp8b_gate_fwd_bwd"] = train_leg(q, synth, dev, bf)
+        extra["mlp8b_fwd_bwd"] = train_leg(q, synth, dev, bf)
 
     # --------------------------------------------------------- cpu baseline
     cpu = None
@@ -280,35 +281,16 @@ def counters_probe(q, pool, X, Y, A, B, r, alpha, ws, dev):
 
 
 def train_leg(q, synth, dev, bf):
-    """fwd + bwd of the 8B-MLP gate projection (14336 x 4096, T = 4096, r = 64)."""
+    """fwd + bwd of the 8B-MLP projections (gate and up 4096 -> 14336, down
+    14336 -> 4096; T = 4096, r = 64, alpha = 128): per projection and for the
+    three together.  Each call is warmed up, then timed over 20 calls."""
     import torch
     wl = synth.WORKLOADS[3]
-    p = wl.projections[0]
     T, r, alpha = wl.tokens[0], wl.r, wl.alpha
-    n_out, n_in = p.out_features, p.in_features
-    w = torch.from_numpy(synth.weight(3, 0, n_out, n_in)).to(dev)
-    W = q.nf4_quantize_weight(w)
-    del w
-    X = bf(synth.activations(3, 0, T, n_in))
-    dY = bf(synth.activations(3, 0, T, n_out, "dY"))
-    A = bf(synth.lora_A(3, 0, r, n_in))
-    B = bf(synth.lora_B(3, 0, n_out, r))
-    Y = torch.empty(T, n_out, dtype=torch.bfloat16, device=dev)
-    dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
-    dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
-    dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
-    wsf = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, False), dev)
-    wsb = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
-
-    def fwd():
-        q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=wsf)
-
-    def bwd():
-        q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX=dX, dA=dA, dB=dB, ws=wsb)
+    res = {"T": T, "r": r, "alpha": alpha}
+    tot_flop, tot_ms = 0.0, 0.0
 
     def timed(fn, n):
-        for _ in range(2):
-            fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -318,15 +300,47 @@ def train_leg(q, synth, dev, bf):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    ms_f = timed(fwd, 10)
-    ms_b = timed(bwd, 10)
-    flop_f = 2 * T * n_in * n_out + 2 * T * r * (n_in + n_out)
-    flop_b = 2 * T * n_in * n_out + 4 * T * r * (n_in + n_out)
-    tf = (flop_f + flop_b) / ((ms_f + ms_b) * 1e-3) / 1e12
-    return {"T": T, "out": n_out, "in": n_in, "r": r, "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
-            "fwd_TFLOPs": round(flop_f / (ms_f * 1e-3) / 1e12, 1),
-            "bwd_TFLOPs": round(flop_b / (ms_b * 1e-3) / 1e12, 1),
-            "fwd_bwd_TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    for pi, p in enumerate(wl.projections):
+        n_out, n_in = p.out_features, p.in_features
+        w = torch.from_numpy(synth.weight(3, pi, n_out, n_in)).to(dev)
+        W = q.nf4_quantize_weight(w)
+        del w
+        X = bf(synth.activations(3, pi, T, n_in))
+        dY = bf(synth.activations(3, pi, T, n_out, "dY"))
+        A = bf(synth.lora_A(3, pi, r, n_in))
+        B = bf(synth.lora_B(3, pi, n_out, r))
+        Y = torch.empty(T, n_out, dtype=torch.bfloat16, device=dev)
+        dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
+        dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
+        dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
+        wsf = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, False), dev)
+        wsb = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
+
+        def fwd():
+            q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=wsf)
+
+        def bwd():
+            q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX=dX, dA=dA, dB=dB, ws=wsb)
+
+        for _ in range(8):
+            fwd()
+            bwd()
+        ms_f = timed(fwd, 20)
+        ms_b = timed(bwd, 20)
+        flop_f = 2 * T * n_in * n_out + 2 * T * r * (n_in + n_out)
+        flop_b = 2 * T * n_in * n_out + 4 * T * r * (n_in + n_out)
+        res[p.name] = {"out": n_out, "in": n_in, "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
+                       "fwd_TFLOPs": round(flop_f / (ms_f * 1e-3) / 1e12, 1),
+                       "bwd_TFLOPs": round(flop_b / (ms_b * 1e-3) / 1e12, 1),
+                       "fwd_bwd_TFLOPs": round((flop_f + flop_b) / ((ms_f + ms_b) * 1e-3) / 1e12, 1)}
+        tot_flop += flop_f + flop_b
+        tot_ms += ms_f + ms_b
+        del W, X, dY, Y, dX, wsf, wsb
+    tf = tot_flop / (tot_ms * 1e-3) / 1e12
+    res["mlp_fwd_bwd_ms"] = round(tot_ms, 3)
+    res["mlp_fwd_bwd_TFLOPs"] = round(tf, 1)
+    res["frac_of_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+    return res
 
 
 def cpu_baseline(w_host, W, n_out, n_in, r, alpha, X1, X16, A, B, step_bytes):

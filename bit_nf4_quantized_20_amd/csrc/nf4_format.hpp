@@ -100,10 +100,19 @@ __device__ __forceinline__ float bf16_hi(uint32_t p) { return __builtin_bit_cast
 
 // ---------------------------------------------------------------------------
 // Double-quantized absmax: a_hat = fl32(fl32(q / 255) * s).
+// fl32(q / 255) without a division: r0 = fl32(q * c) with c = fl32(1/255),
+// then one FMA correction r0 + fl32(q - 255 r0) * c.  For every q in 0..255
+// this equals the correctly rounded quotient (checked exhaustively on the
+// host in the tests, and on the GPU by dequantizing all 256 codes); it costs
+// three instructions instead of the ~10 of an IEEE division.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float dq_absmax(uint32_t q, float s) {
-  const float ratio = static_cast<float>(q) / 255.0f;  // IEEE division (correctly rounded)
-  return ratio * s;
+  constexpr float kInv255 = 0x1.010102p-8f;  // fl32(1 / 255)
+  const float qf = static_cast<float>(q);
+  const float r0 = __fmul_rn(qf, kInv255);
+  const float e = __builtin_fmaf(-r0, 255.0f, qf);
+  const float ratio = __builtin_fmaf(e, kInv255, r0);
+  return __fmul_rn(ratio, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -49,6 +49,24 @@ def test_quantize_dequantize_bit_exact(shape):
     _assert_bits_equal(host_bits(back), onf4.dequantize(rc, raq, rsc), "dequant")
 
 
+def test_dequantize_every_absmax_code():
+    # 3 groups of 256 blocks whose absmax codes run through 0..255 and whose
+    # 64 codes cycle through the 16 levels, with an ordinary, a tiny and a
+    # huge group scale: the dequantized bf16 must match bit for bit
+    q = require_gpu()
+    banner("dequantize all 256 absmax codes x 16 levels")
+    nblk = 3 * 256
+    n = nblk * 64
+    levels = (np.arange(n) % 16).astype(np.uint8)
+    packed = (levels[0::2] | (levels[1::2] << 4)).astype(np.uint8)
+    aq = (np.arange(nblk) % 256).astype(np.uint8)
+    sc = np.array([0.0371, 1.0e-38, 3.0e38], dtype=np.float32)
+    back = q.nf4_dequantize(torch.from_numpy(packed).cuda(), torch.from_numpy(aq).cuda(),
+                            torch.from_numpy(sc).cuda(), n)
+    torch.cuda.synchronize()
+    _assert_bits_equal(host_bits(back), onf4.dequantize(packed, aq, sc), "dequant")
+
+
 def test_edge_blocks():
     # zero blocks, a zero group, tiny (subnormal) blocks, huge and exact-level values
     q = require_gpu()
