@@ -226,6 +226,9 @@ def main():
     extra["quantize_4096x4096"] = {"us_per_call": round(us_q, 2),
                                    "GB_per_s": round(qbytes / (us_q * 1e-6) / 1e9, 1)}
 
+    # ------------------------------------------------------ adapter merge
+    extra["merge_8b_gate"] = merge_leg(q, synth, dev, bf)
+
     # ------------------------------------------- large-token fwd + bwd
     if not args.no_train:
         extra["mlp8b_fwd_bwd"] = train_leg(q, synth, dev, bf)
@@ -260,6 +263,37 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def merge_leg(q, synth, dev, bf):
+    """qlora_merge of the 8B-MLP gate projection (14336 x 4096 NF4, r = 64):
+    W_merged = bf16(W_hat + (alpha/r) B A), HBM-bound (codes + absmax read,
+    2 B per weight written)."""
+    import torch
+    wl = synth.WORKLOADS[3]
+    p = wl.projections[0]
+    r, alpha = wl.r, wl.alpha
+    n_out, n_in = p.out_features, p.in_features
+    W = q.nf4_quantize_weight(torch.from_numpy(synth.weight(3, 0, n_out, n_in)).to(dev))
+    A = bf(synth.lora_A(3, 0, r, n_in))
+    B = bf(synth.lora_B(3, 0, n_out, r))
+    out = torch.empty(n_out, n_in, dtype=torch.bfloat16, device=dev)
+    ws = q.make_workspace(q.qlora_merge_workspace_bytes(n_in, n_out, r), dev)
+    for _ in range(3):
+        q.qlora_merge(W, A, B, r, alpha, out=out, ws=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    n = 20
+    for _ in range(n):
+        q.qlora_merge(W, A, B, r, alpha, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    nbytes = int(n_out * n_in * (NF4_BYTES_PER_WEIGHT + 2) + 2 * r * (n_in + n_out))
+    return {"out": n_out, "in": n_in, "r": r, "us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+            "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def counters_probe(q, pool, X, Y, A, B, r, alpha, ws, dev):

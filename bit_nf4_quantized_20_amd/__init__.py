@@ -7,8 +7,8 @@ library has not been built, importing this package raises.
 
 Names and semantics follow include/qlora.h:
     nf4_storage_bytes, nf4_quantize, nf4_dequantize, qlora_workspace_bytes,
-    qlora_linear_fwd, qlora_linear_bwd, nf4_codebook, nf4_code_thresholds,
-    qlora_status_string
+    qlora_linear_fwd, qlora_linear_bwd, qlora_merge_workspace_bytes, qlora_merge,
+    nf4_codebook, nf4_code_thresholds, qlora_status_string
 """
 
 import ctypes
@@ -32,7 +32,7 @@ class QloraError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_nf4_quantized_20_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python bit_nf4_quantized_20_amd/build.py` "
                       "(hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -60,6 +60,10 @@ _lib.qlora_linear_fwd.restype = ctypes.c_int
 _lib.qlora_linear_bwd.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, _p, _i64,
                                   ctypes.c_float, _p, _p, _p, _p, _sz, _p]
 _lib.qlora_linear_bwd.restype = ctypes.c_int
+_lib.qlora_merge_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.qlora_merge_workspace_bytes.restype = _sz
+_lib.qlora_merge.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, ctypes.c_float, _p, _p, _sz, _p]
+_lib.qlora_merge.restype = ctypes.c_int
 _lib.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
 _lib.nf4_codebook.restype = None
 _lib.nf4_code_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -221,6 +225,27 @@ def qlora_linear_bwd(W: NF4Weight, X, dY, A, B, r: int, alpha: float, dX=None, d
                                  float(alpha), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
                                  _stream(dev)), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+def qlora_merge_workspace_bytes(in_features: int, out_features: int, r: int) -> int:
+    return int(_lib.qlora_merge_workspace_bytes(in_features, out_features, r))
+
+
+def qlora_merge(W: NF4Weight, A, B, r: int, alpha: float, out=None, ws=None):
+    """W_merged [out, in] bf16 = bf16(W_hat + (alpha/r) B A)."""
+    _need(A, torch.bfloat16, "A", r * W.cols)
+    _need(B, torch.bfloat16, "B", W.rows * r)
+    dev = A.device
+    if out is None:
+        out = torch.empty(W.rows, W.cols, dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", W.rows * W.cols)
+    need = qlora_merge_workspace_bytes(W.cols, W.rows, r)
+    if ws is None:
+        ws = make_workspace(need, dev)
+    wc = W._c()
+    _check(_lib.qlora_merge(ctypes.byref(wc), _ptr(A), _ptr(B), r, float(alpha), _ptr(out), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(dev)), "qlora_merge")
+    return out
 
 
 def nf4_codebook():

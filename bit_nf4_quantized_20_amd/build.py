@@ -1,6 +1,6 @@
 """Builds libqlora.so (the HIP kernels + C ABI) in-tree for gfx950.
 
-    python -m bit_nf4_quantized_20_amd.build
+    python bit_nf4_quantized_20_amd/build.py
 
 hipcc cross-compiles for gfx950 without a GPU.  Every HIP source is compiled
 with packed fp32 instructions disabled (-Xclang -target-feature -Xclang

@@ -86,6 +86,13 @@ hipError_t launch_gemm_nf4(int64_t M, int64_t N, const uint16_t* act0, int64_t l
                            int64_t K0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);
 
+// W_merged[m][n] = bf16(W_hat[m][n] + s * sum_j Bp[m][j] Atp[n][j]) for the
+// NF4 weight [out][in] (out % 64 == 0, in % 64 == 0); Bp [out][ldp] and Atp
+// [in][ldp] hold B and A^T zero-padded to rp (a multiple of 16) columns.
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
+                        int64_t out, int64_t in, const uint16_t* Bp, const uint16_t* Atp,
+                        int64_t ldp, int64_t rp, float s, uint16_t* w_out, hipStream_t st);
+
 // Fused small-token forward (T <= 16, r <= 64): Y = X W_hat^T + s (X A^T) B^T
 // in one launch, no workspace.  decode_fits() lists the shapes it takes.
 constexpr int64_t kDecodeMaxT = 16;

@@ -237,6 +237,40 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora
   return launched(e);
 }
 
+size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, int64_t r) {
+  if (!linear_shapes_ok(0, in_features, out_features, r)) return 0;
+  const int64_t rp = padded_rank(r);
+  Carve c;
+  c.take(static_cast<size_t>(out_features * rp * 4));  // B padded [out][2 rp]
+  c.take(static_cast<size_t>(in_features * rp * 4));   // A^T padded [in][2 rp]
+  return c.off > kMinWorkspace ? c.off : kMinWorkspace;
+}
+
+int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16* B, int64_t r,
+                float alpha, qlora_bf16* W_out, void* ws, size_t ws_bytes, qlora_stream stream) {
+  if (int st = check_weight(W)) return st;
+  const int64_t out = W->rows, in = W->cols;
+  if (!linear_shapes_ok(0, in, out, r)) return QLORA_ERR_SHAPE;
+  if (!A || !B || !W_out) return QLORA_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(W_out)) return QLORA_ERR_ALIGN;
+  if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
+  const size_t need = qlora_merge_workspace_bytes(in, out, r);
+  if (ws == nullptr || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (int st = check_device()) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rp = padded_rank(r);
+  uint16_t* b_pad = static_cast<uint16_t*>(ws);
+  uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + round_up(out * rp * 4, 256));
+  hipError_t e = launch_pad_bf16(B, out, r, false, b_pad, rp, s);
+  if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, s);
+  if (e == hipSuccess)
+    e = launch_merge(W->codes, W->absmax_q, W->absmax_scale, out, in, b_pad, a_t_pad, 2 * rp, rp,
+                     alpha / static_cast<float>(r), W_out, s);
+  return launched(e);
+}
+
 void nf4_codebook(float out[16]) {
   for (int j = 0; j < 16; ++j) out[j] = level(j);
 }

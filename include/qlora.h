@@ -171,6 +171,29 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora
                      qlora_bf16* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
                      qlora_stream stream);
 
+/*
+ * Workspace bytes needed by qlora_merge: 0 for invalid shapes, at least 256
+ * otherwise.  Host only.  Scratch only; needs no initialisation.
+ */
+size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, int64_t r);
+
+/*
+ * qlora_merge -- folds the adapter into the frozen weight for serving:
+ *   W_out = bf16(W_hat + (alpha/r) B A)          [out, in] bf16
+ * (coddykit "LoRA y QLoRA": the adapter is merged into the base with
+ * merge_and_unload; ultralytics glossary "QLoRA", "Compromissos": the 4-bit
+ * base must be dequantized to 16 bits first).  Per element one rounding:
+ * bf16_rne(fl32(w_hat + fl32(s * sum_j B[m][j] A[j][n]))) with w_hat exactly
+ * as nf4_dequantize produces it and the rank-r sum accumulated in fp32.
+ *   W      NF4 weight [out, in]; in % 64 == 0, out % 64 == 0
+ *   A      [r, in] bf16;  B [out, r] bf16;  1 <= r <= 256;  alpha finite
+ *   W_out  [out, in] bf16 out (row-major)
+ *   ws     workspace of ws_bytes >= qlora_merge_workspace_bytes(in, out, r)
+ * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE, LAUNCH.
+ */
+int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16* B, int64_t r,
+                float alpha, qlora_bf16* W_out, void* ws, size_t ws_bytes, qlora_stream stream);
+
 /* Host copy of the 16 fp32 levels the kernels use (ascending, L[7] = +0.0). */
 void nf4_codebook(float out[16]);
 

@@ -61,6 +61,16 @@ def linear_bwd(W_hat, X, dY, A, B, alpha: float, r: int):
     return dX, dA, dB
 
 
+def merge(W_hat, A, B, alpha: float, r: int) -> np.ndarray:
+    """W_hat + (alpha/r) B A in fp64, unrounded: the adapter folded into the
+    dequantized base for serving (coddykit "LoRA y QLoRA": merge_and_unload;
+    ultralytics glossary "QLoRA", "Compromissos": the 4-bit base is
+    dequantized to 16 bits before the merge).  Serving the merged weight is
+    the same linear map as the forward above: X merge^T = X W_hat^T + s U B^T."""
+    s = float(alpha) / float(r)
+    return widen(W_hat) + s * (widen(B) @ widen(A))
+
+
 def rel_frobenius(got, ref) -> float:
     """||got - ref||_F / ||ref||_F in fp64 (the acceptance measure)."""
     g = np.asarray(got, dtype=np.float64)

@@ -191,6 +191,31 @@ def test_linear_validation():
         assert len(lib.qlora_status_string(s)) > 0
 
 
+def test_merge_validation():
+    lib = _lib()
+    i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.qlora_merge_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.qlora_merge_workspace_bytes.restype = sz
+    lib.qlora_merge.argtypes = [ctypes.POINTER(_W), vp, vp, i64, ctypes.c_float, vp, vp, sz, vp]
+    lib.qlora_merge.restype = ctypes.c_int
+    F = _FAKE
+    ws = lib.qlora_merge_workspace_bytes(256, 128, 8)
+    # B padded [out][2 rp] + A^T padded [in][2 rp], bf16, rp = 64
+    assert ws == 128 * 128 * 2 + 256 * 128 * 2
+    assert lib.qlora_merge_workspace_bytes(100, 128, 8) == 0
+    assert lib.qlora_merge_workspace_bytes(256, 128, 0) == 0
+    W = _W(F, F, F, 128, 256)
+    call = lambda **k: lib.qlora_merge(ctypes.byref(k.get("W", W)), k.get("A", F), F, k.get("r", 8),
+                                       k.get("alpha", 16.0), k.get("out", F), k.get("ws", F),
+                                       k.get("wsb", ws), None)
+    assert call(W=_W(F, F, F, 128, 100)) == -2
+    assert call(r=300) == -2
+    assert call(A=None) == -1 and call(out=None) == -1
+    assert call(out=_MISALIGNED) == -3
+    assert call(alpha=float("nan")) == -7
+    assert call(ws=None) == -4 and call(wsb=ws - 1) == -4
+
+
 def test_valid_call_without_gpu_reports_device_error():
     # with no HIP device the first HIP call fails and the call returns
     # ERR_DEVICE without launching anything (pointers are never touched)

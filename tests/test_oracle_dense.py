@@ -97,3 +97,31 @@ def test_special_cases():
 def test_rel_frobenius():
     assert dense.rel_frobenius([3.0, 4.0], [3.0, 4.0]) == 0.0
     assert abs(dense.rel_frobenius([3.0, 4.0], [0.0, 5.0]) - np.sqrt(10) / 5) < 1e-15
+
+
+def test_merge_against_loops():
+    W, _, A, B, _ = _problem(3, n_in=6, n_out=5, r=3)
+    alpha, r = 6.0, 3
+    Wd, Ad, Bd = _f(W), _f(A), _f(B)
+    M = dense.merge(W, A, B, alpha, r)
+    for o in range(Wd.shape[0]):
+        for k in range(Wd.shape[1]):
+            ref = Wd[o, k] + alpha / r * sum(Bd[o, j] * Ad[j, k] for j in range(r))
+            assert abs(M[o, k] - ref) < 1e-12
+
+
+def test_merged_weight_serves_the_same_linear():
+    # (W_hat + s B A) x = W_hat x + s B (A x): the merged weight reproduces
+    # the QLoRA forward for any input
+    W, X, A, B, _ = _problem(4, T=6, n_in=7, n_out=5, r=2)
+    alpha, r = 3.0, 2
+    Y = dense.linear_fwd(W, X, A, B, alpha, r)
+    Ym = _f(X) @ dense.merge(W, A, B, alpha, r).T
+    assert np.max(np.abs(Y - Ym)) < 1e-12 * max(1.0, np.max(np.abs(Y)))
+
+
+def test_merge_special_cases():
+    W, _, A, B, _ = _problem(5)
+    # B = 0: the base alone; W = 0: the adapter alone
+    assert np.array_equal(dense.merge(W, A, np.zeros_like(B), 4.0, 2), _f(W))
+    assert np.array_equal(dense.merge(np.zeros_like(W), A, B, 4.0, 2), 2.0 * (_f(B) @ _f(A)))
