@@ -226,6 +226,33 @@ def main():
     extra["quantize_4096x4096"] = {"us_per_call": round(us_q, 2),
                                    "GB_per_s": round(qbytes / (us_q * 1e-6) / 1e9, 1)}
 
+    # standalone dequantize (D1) and the format without double quantization
+    def per_call_us(fn, n=50):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    nw = n_out * n_in
+    wout = torch.empty(nw, dtype=torch.bfloat16, device=dev)
+    us_d = per_call_us(lambda: q.nf4_dequantize(codes, aq, sc, nw, out=wout))
+    dbytes = int(nw * (NF4_BYTES_PER_WEIGHT + 2))
+    extra["dequantize_4096x4096"] = {"us_per_call": round(us_d, 2),
+                                     "GB_per_s": round(dbytes / (us_d * 1e-6) / 1e9, 1)}
+    c2, a2 = q.nf4_quantize_nodq(w_dev)
+    us_qn = per_call_us(lambda: q.nf4_quantize_nodq(w_dev, codes=c2, absmax=a2))
+    us_dn = per_call_us(lambda: q.nf4_dequantize_nodq(c2, a2, nw, out=wout))
+    extra["nodq_4096x4096"] = {"quantize_us": round(us_qn, 2),
+                               "quantize_GB_per_s": round(nw * 4.5625 / (us_qn * 1e-6) / 1e9, 1),
+                               "dequantize_us": round(us_dn, 2),
+                               "dequantize_GB_per_s": round(nw * 2.5625 / (us_dn * 1e-6) / 1e9, 1)}
+
     # ------------------------------------------------------ adapter merge
     extra["merge_8b_gate"] = merge_leg(q, synth, dev, bf)
 

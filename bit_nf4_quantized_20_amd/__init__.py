@@ -7,6 +7,7 @@ library has not been built, importing this package raises.
 
 Names and semantics follow include/qlora.h:
     nf4_storage_bytes, nf4_quantize, nf4_dequantize, qlora_workspace_bytes,
+    nf4_quantize_nodq, nf4_dequantize_nodq,
     qlora_linear_fwd, qlora_linear_bwd, qlora_merge_workspace_bytes, qlora_merge,
     nf4_codebook, nf4_code_thresholds, qlora_status_string
 """
@@ -60,6 +61,10 @@ _lib.qlora_linear_fwd.restype = ctypes.c_int
 _lib.qlora_linear_bwd.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, _p, _i64,
                                   ctypes.c_float, _p, _p, _p, _p, _sz, _p]
 _lib.qlora_linear_bwd.restype = ctypes.c_int
+_lib.nf4_quantize_nodq.argtypes = [_p, _i64, _p, _p, _p]
+_lib.nf4_quantize_nodq.restype = ctypes.c_int
+_lib.nf4_dequantize_nodq.argtypes = [_p, _p, _i64, _p, _p]
+_lib.nf4_dequantize_nodq.restype = ctypes.c_int
 _lib.qlora_merge_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.qlora_merge_workspace_bytes.restype = _sz
 _lib.qlora_merge.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, ctypes.c_float, _p, _p, _sz, _p]
@@ -157,6 +162,32 @@ def nf4_dequantize(codes, absmax_q, absmax_scale, numel: int, out=None):
     _need(out, torch.bfloat16, "out", numel)
     _check(_lib.nf4_dequantize(_ptr(codes), _ptr(absmax_q), _ptr(absmax_scale), numel, _ptr(out),
                                _stream(codes.device)), "nf4_dequantize")
+    return out
+
+
+def nf4_quantize_nodq(w: torch.Tensor, codes=None, absmax=None):
+    """fp32 device tensor (numel % 64 == 0) -> (codes uint8 [numel/2], absmax fp32 [numel/64]),
+    no double quantization (4.5 bits per weight)."""
+    _need(w, torch.float32, "w")
+    n = w.numel()
+    if codes is None:
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=w.device)
+    if absmax is None:
+        absmax = torch.empty(n // 64, dtype=torch.float32, device=w.device)
+    _need(codes, torch.uint8, "codes", n // 2)
+    _need(absmax, torch.float32, "absmax", n // 64)
+    _check(_lib.nf4_quantize_nodq(_ptr(w), n, _ptr(codes), _ptr(absmax), _stream(w.device)),
+           "nf4_quantize_nodq")
+    return codes, absmax
+
+
+def nf4_dequantize_nodq(codes, absmax, numel: int, out=None):
+    """-> bf16 device tensor [numel] (fp32 block absmax, no double quantization)."""
+    if out is None:
+        out = torch.empty(numel, dtype=torch.bfloat16, device=codes.device)
+    _need(out, torch.bfloat16, "out", numel)
+    _check(_lib.nf4_dequantize_nodq(_ptr(codes), _ptr(absmax), numel, _ptr(out), _stream(codes.device)),
+           "nf4_dequantize_nodq")
     return out
 
 

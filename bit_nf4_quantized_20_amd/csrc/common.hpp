@@ -44,6 +44,11 @@ hipError_t launch_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, ui
                                float* scale, hipStream_t s);
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                                  int64_t numel, uint16_t* out, hipStream_t s);
+// Without double quantization: the exact fp32 block absmax [numel/64].
+hipError_t launch_nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
+                                    hipStream_t s);
+hipError_t launch_nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel,
+                                      uint16_t* out, hipStream_t s);
 // out[c][r] = W_hat[r][c] for W_hat [rows][cols]; rows % 64 == 0, cols % 64 == 0
 hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t* absmax_q,
                                             const float* scale, int64_t rows, int64_t cols,

@@ -18,10 +18,14 @@ namespace qlora {
 // wave, and the 16 chunks of one 64-weight block sit in 16 adjacent lanes,
 // so the block absmax is a 16-lane DPP max.
 // ---------------------------------------------------------------------------
+// kDQ = false: no double quantization; absmax_q and scale are unused and
+// the exact fp32 block absmax goes to absmax[numel/64] (4.5 bits per weight).
+template <bool kDQ>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ w, int64_t numel,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ absmax_q,
-                                                      float* __restrict__ scale) {
+                                                      float* __restrict__ scale,
+                                                      float* __restrict__ absmax) {
   __shared__ float wave_max[4];
   const int t = threadIdx.x;
   const int64_t g = blockIdx.x;
@@ -47,6 +51,15 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
     am[i] = m;
     tmax = fmaxf(tmax, m);
   }
+  if constexpr (!kDQ) {
+    if ((t & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t e = base + static_cast<int64_t>(i * 256 + t) * 4;
+        if (e < numel) absmax[e >> 6] = am[i];
+      }
+    }
+  }
   // group scale s_g = max over the 256 blocks
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -55,7 +68,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   const float sg = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
 
   // Q2: 8-bit absmax codes, q = rne(fl32(fl32(a / s) * 255)); zero group -> 0
-  if ((t & 15) == 0) {
+  if (kDQ && (t & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t e = base + static_cast<int64_t>(i * 256 + t) * 4;
@@ -70,7 +83,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       }
     }
   }
-  if (t == 0) scale[g] = sg;
+  if (kDQ && t == 0) scale[g] = sg;
 
   // Q3 + Q4: codes from x = fl32(w / a) and the 15 thresholds; a zero block
   // has x = 0 everywhere (code 7).  4 codes -> 16 bits per chunk.
@@ -97,8 +110,16 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
 hipError_t launch_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
                                float* scale, hipStream_t s) {
   const int64_t groups = ceil_div(numel, kGroupElems);
-  hipLaunchKernelGGL(k_nf4_quantize, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, w,
-                     numel, codes, absmax_q, scale);
+  hipLaunchKernelGGL(k_nf4_quantize<true>, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, w,
+                     numel, codes, absmax_q, scale, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
+                                    hipStream_t s) {
+  const int64_t groups = ceil_div(numel, kGroupElems);
+  hipLaunchKernelGGL(k_nf4_quantize<false>, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, w,
+                     numel, codes, nullptr, nullptr, absmax);
   return hipGetLastError();
 }
 
@@ -106,14 +127,17 @@ hipError_t launch_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, ui
 // Dequantize: each thread expands 32 weights (16 code bytes, half a block)
 // into 64 bytes of bf16 with the per-block v_perm table.
 // ---------------------------------------------------------------------------
+// kDQ = false: a_hat is the fp32 block absmax (absmax[blk]) itself.
+template <bool kDQ>
 __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ absmax_q,
                                                         const float* __restrict__ scale,
+                                                        const float* __restrict__ absmax,
                                                         int64_t numel, uint16_t* __restrict__ out) {
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 32-weight chunk
   if (c * 32 >= numel) return;
   const int64_t blk = c >> 1;
-  const float ahat = dq_absmax(absmax_q[blk], scale[blk >> 8]);
+  const float ahat = kDQ ? dq_absmax(absmax_q[blk], scale[blk >> 8]) : absmax[blk];
   const Nf4Table tab = make_table(ahat);
   const u32x4 cw = *reinterpret_cast<const u32x4*>(codes + c * 16);
   u32x4* dst = reinterpret_cast<u32x4*>(out + c * 32);
@@ -128,8 +152,16 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                                  int64_t numel, uint16_t* out, hipStream_t s) {
   const int64_t chunks = numel / 32;
-  hipLaunchKernelGGL(k_nf4_dequantize, dim3(static_cast<uint32_t>(ceil_div(chunks, 256))),
-                     dim3(256), 0, s, codes, absmax_q, scale, numel, out);
+  hipLaunchKernelGGL(k_nf4_dequantize<true>, dim3(static_cast<uint32_t>(ceil_div(chunks, 256))),
+                     dim3(256), 0, s, codes, absmax_q, scale, nullptr, numel, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel,
+                                      uint16_t* out, hipStream_t s) {
+  const int64_t chunks = numel / 32;
+  hipLaunchKernelGGL(k_nf4_dequantize<false>, dim3(static_cast<uint32_t>(ceil_div(chunks, 256))),
+                     dim3(256), 0, s, codes, nullptr, nullptr, absmax, numel, out);
   return hipGetLastError();
 }
 

@@ -147,6 +147,28 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
                                         static_cast<hipStream_t>(stream)));
 }
 
+int nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
+                      qlora_stream stream) {
+  if (numel < 0 || (numel % kBlock) != 0) return QLORA_ERR_SHAPE;
+  if (numel > (int64_t(1) << 45)) return QLORA_ERR_SHAPE;
+  if (numel == 0) return QLORA_OK;
+  if (!w || !codes || !absmax) return QLORA_ERR_NULL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
+  if (int st = check_device()) return st;
+  return launched(launch_nf4_quantize_nodq(w, numel, codes, absmax, static_cast<hipStream_t>(stream)));
+}
+
+int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel, qlora_bf16* w_out,
+                        qlora_stream stream) {
+  if (numel < 0 || (numel % kBlock) != 0) return QLORA_ERR_SHAPE;
+  if (numel > (int64_t(1) << 45)) return QLORA_ERR_SHAPE;
+  if (numel == 0) return QLORA_OK;
+  if (!codes || !absmax || !w_out) return QLORA_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(absmax) || !aligned16(w_out)) return QLORA_ERR_ALIGN;
+  if (int st = check_device()) return st;
+  return launched(launch_nf4_dequantize_nodq(codes, absmax, numel, w_out, static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                              int backward) {
   if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;

@@ -124,6 +124,24 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
                    int64_t numel, qlora_bf16* w_out, qlora_stream stream);
 
 /*
+ * nf4_quantize_nodq / nf4_dequantize_nodq -- the same format without double
+ * quantization: one exact fp32 absmax per 64-weight block, 4 + 32/64 = 4.5
+ * bits per weight (paperclase "QLoRA", Parte 3, "Bits por parametro": 4 bits
+ * plus the absmax; ultralytics glossary "QLoRA": the NF4 construction and
+ * its mean-squared-error comparison use exact block absmax values).
+ * Codes exactly as nf4_quantize (they use the exact absmax in both formats);
+ * w_hat = bf16_rne(fl32(L[c] * a_b)).
+ *   codes  [numel/2];  absmax [numel/64] fp32 (out of quantize, in of dequantize)
+ *   numel  >= 0, multiple of 64 (0 is a no-op)
+ * The linear calls take the double-quantized format only.
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
+ */
+int nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
+                      qlora_stream stream);
+int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel, qlora_bf16* w_out,
+                        qlora_stream stream);
+
+/*
  * Workspace bytes needed by qlora_linear_fwd (backward = 0) or
  * qlora_linear_bwd (backward = 1) for T tokens, in/out features and rank r.
  * Returns 0 for invalid shapes and at least 256 otherwise.  Host only.

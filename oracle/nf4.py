@@ -189,6 +189,31 @@ def dequantize(codes_packed, absmax_q, scale) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# The format without double quantization (4 + 32/64 = 4.5 bits per weight)
+# --------------------------------------------------------------------------
+
+def quantize_nodq(w: np.ndarray, nearest=None):
+    """Q1, Q3, Q4 with the exact fp32 block absmax stored as is (paperclase
+    "QLoRA", Parte 3: 4 bits plus the absmax per block; ultralytics "QLoRA":
+    the MSE comparison quantizes with exact block absmax values) ->
+    (codes uint8[numel/2], absmax f32[numel/64])."""
+    a = block_absmax(w)
+    return pack_nibbles(nf4_codes(w, a, nearest=nearest)), a
+
+
+def dequantize_nodq_f32(codes_packed, absmax, levels=None) -> np.ndarray:
+    """fl32(L[c] * a_b) per element."""
+    lv = nf4_levels() if levels is None else levels
+    c = unpack_nibbles(codes_packed)
+    return (lv[c] * np.repeat(np.asarray(absmax, dtype=np.float32), BLOCK)).astype(np.float32)
+
+
+def dequantize_nodq(codes_packed, absmax) -> np.ndarray:
+    """bf16_rne(fl32(L[c] * a_b)) as bf16 bit patterns."""
+    return bf16_rne_bits(dequantize_nodq_f32(codes_packed, absmax))
+
+
+# --------------------------------------------------------------------------
 # Quantizers used only for the pages' worked examples
 # --------------------------------------------------------------------------
 

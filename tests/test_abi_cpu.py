@@ -191,6 +191,21 @@ def test_linear_validation():
         assert len(lib.qlora_status_string(s)) > 0
 
 
+def test_nodq_validation():
+    lib = _lib()
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.nf4_quantize_nodq.argtypes = [vp, i64, vp, vp, vp]
+    lib.nf4_dequantize_nodq.argtypes = [vp, vp, i64, vp, vp]
+    F = _FAKE
+    assert lib.nf4_quantize_nodq(F, 65, F, F, None) == -2
+    assert lib.nf4_quantize_nodq(F, 64, F, None, None) == -1
+    assert lib.nf4_quantize_nodq(F, 64, F, _MISALIGNED, None) == -3
+    assert lib.nf4_quantize_nodq(F, 0, F, F, None) == 0
+    assert lib.nf4_dequantize_nodq(F, F, -64, F, None) == -2
+    assert lib.nf4_dequantize_nodq(F, None, 64, F, None) == -1
+    assert lib.nf4_dequantize_nodq(F, F, 0, F, None) == 0
+
+
 def test_merge_validation():
     lib = _lib()
     i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p

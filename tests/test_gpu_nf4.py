@@ -151,3 +151,37 @@ def test_flat_2pow30_sampled_groups():
         _assert_bits_equal(sc_h[g:g + 1], rsc, f"scale g={g}")
         got = host_bits(back[g * G:(g + 1) * G])
         _assert_bits_equal(got, onf4.dequantize(rc, raq, rsc), f"dequant g={g}")
+
+
+# ------------------------------------------ format without double quantization
+
+@pytest.mark.parametrize("shape", [(256, 256), (4096, 4096), (64 * (256 * 3 + 37),)])
+def test_nodq_quantize_dequantize_bit_exact(shape):
+    q = require_gpu()
+    banner(f"no-double-quant quantize/dequantize shape={shape}")
+    w_host = synth.normal_f32(13, shape, synth.W_STD)
+    w_host.reshape(-1)[0:64] = 0.0  # a zero block
+    codes, absmax = q.nf4_quantize_nodq(dev_f32(w_host))
+    torch.cuda.synchronize()
+    rc, ra = onf4.quantize_nodq(w_host, nearest=onative.nearest_level)
+    _assert_bits_equal(host(codes), rc, "codes")
+    _assert_bits_equal(host(absmax), ra, "absmax")
+    n = int(np.prod(shape))
+    back = q.nf4_dequantize_nodq(codes, absmax, n)
+    torch.cuda.synchronize()
+    _assert_bits_equal(host_bits(back), onf4.dequantize_nodq(rc, ra), "dequant")
+
+
+def test_nodq_gpu_codes_replay_the_mse_experiment():
+    # ultralytics glossary "QLoRA": seed 0, randn(4096, 64) * 0.02, exact block
+    # absmax, nearest NF4 level: the printed MSE is 3.395e-06.  The GPU's
+    # codes and absmax, reconstructed in fp32 as on the page, give it again.
+    q = require_gpu()
+    banner("MSE experiment from GPU codes")
+    torch.manual_seed(0)
+    w = (torch.randn(4096, 64) * 0.02).numpy()
+    codes, absmax = q.nf4_quantize_nodq(dev_f32(w))
+    torch.cuda.synchronize()
+    restored = onf4.dequantize_nodq_f32(host(codes), host(absmax)).reshape(w.shape)
+    mse = np.mean((restored.astype(np.float64) - w.astype(np.float64)) ** 2)
+    assert f"{mse:.3e}" == "3.395e-06", mse

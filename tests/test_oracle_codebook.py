@@ -90,3 +90,18 @@ def test_mse_experiment_reproduces_page(golden):
         assert f"{mse:.3e}" == g[f"{name}_mse"], (name, mse)
     reduction = 100 * (1 - out["nf4"] / out["uniform16"])
     assert abs(reduction - float(g["reduction_percent_approx"])) < 1.0
+
+
+def test_mse_experiment_through_the_stored_format_without_double_quant(golden):
+    # the same experiment through the 4.5-bit storage (codes + fp32 block
+    # absmax) and its fp32 reconstruction: identical to the page's print
+    import torch
+    g = golden("ultralytics_mse.txt")
+    torch.manual_seed(int(g["seed"]))
+    rows, cols = (int(v) for v in g["shape"].split())
+    w = (torch.randn(rows, cols) * float(g["std"])).numpy()
+    codes, absmax = onf4.quantize_nodq(w)
+    assert codes.size * 8 + absmax.size * 32 == 4.5 * w.size  # 4 + 32/64 bits per weight
+    restored = onf4.dequantize_nodq_f32(codes, absmax).reshape(w.shape)
+    mse = np.mean((restored.astype(np.float64) - w.astype(np.float64)) ** 2)
+    assert f"{mse:.3e}" == g["nf4_mse"]
