@@ -401,6 +401,51 @@ def train_leg(q, synth, dev, bf):
     res["mlp_fwd_bwd_ms"] = round(tot_ms, 3)
     res["mlp_fwd_bwd_TFLOPs"] = round(tf, 1)
     res["frac_of_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+
+    # gate and up share X: one multi-projection call each way (one LoRA
+    # down-projection pass, one GEMM launch over both, one dX GEMM)
+    gu = wl.projections[:2]
+    n_in = gu[0].in_features
+    Ws, As, Bs = [], [], []
+    for pi, p in enumerate(gu):
+        w = torch.from_numpy(synth.weight(3, pi, p.out_features, n_in)).to(dev)
+        Ws.append(q.nf4_quantize_weight(w))
+        del w
+        As.append(bf(synth.lora_A(3, pi, r, n_in)))
+        Bs.append(bf(synth.lora_B(3, pi, p.out_features, r)))
+    N = sum(p.out_features for p in gu)
+    X = bf(synth.activations(3, 0, T, n_in))
+    dY = bf(synth.activations(3, 0, T, N, "dY"))
+    Y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
+    dAs = [torch.empty(r, n_in, dtype=torch.float32, device=dev) for _ in gu]
+    dBs = [torch.empty(p.out_features, r, dtype=torch.float32, device=dev) for p in gu]
+    outs = [p.out_features for p in gu]
+    wsf = q.make_workspace(q.qlora_workspace_bytes_multi(T, n_in, outs, r, False), dev)
+    wsb = q.make_workspace(q.qlora_workspace_bytes_multi(T, n_in, outs, r, True), dev)
+
+    def fwd2():
+        q.qlora_linear_fwd_multi(Ws, X, As, Bs, r, alpha, Y=Y, ws=wsf)
+
+    def bwd2():
+        q.qlora_linear_bwd_multi(Ws, X, dY, As, Bs, r, alpha, dX=dX, dAs=dAs, dBs=dBs, ws=wsb)
+
+    for _ in range(8):
+        fwd2()
+        bwd2()
+    ms_f = timed(fwd2, 20)
+    ms_b = timed(bwd2, 20)
+    flop_f = 2 * T * n_in * N + 2 * T * r * (2 * n_in + N)
+    flop_b = 2 * T * n_in * N + 4 * T * r * (2 * n_in + N)
+    res["gate_up_fused"] = {"fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
+                            "fwd_TFLOPs": round(flop_f / (ms_f * 1e-3) / 1e12, 1),
+                            "bwd_TFLOPs": round(flop_b / (ms_b * 1e-3) / 1e12, 1)}
+    d = res["down"]
+    fused_ms = ms_f + ms_b + d["fwd_ms"] + d["bwd_ms"]
+    tf2 = tot_flop / (fused_ms * 1e-3) / 1e12
+    res["mlp_fused_fwd_bwd_ms"] = round(fused_ms, 3)
+    res["mlp_fused_fwd_bwd_TFLOPs"] = round(tf2, 1)
+    res["mlp_fused_frac_of_bf16_peak"] = round(tf2 / BF16_PEAK_TFLOPS, 4)
     return res
 
 

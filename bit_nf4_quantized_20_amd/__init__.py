@@ -8,7 +8,8 @@ library has not been built, importing this package raises.
 Names and semantics follow include/qlora.h:
     nf4_storage_bytes, nf4_quantize, nf4_dequantize, qlora_workspace_bytes,
     nf4_quantize_nodq, nf4_dequantize_nodq,
-    qlora_linear_fwd, qlora_linear_bwd, qlora_merge_workspace_bytes, qlora_merge,
+    qlora_linear_fwd, qlora_linear_bwd, qlora_workspace_bytes_multi, qlora_linear_fwd_multi,
+    qlora_linear_bwd_multi, qlora_merge_workspace_bytes, qlora_merge,
     nf4_codebook, nf4_code_thresholds, qlora_status_string
 """
 
@@ -61,6 +62,17 @@ _lib.qlora_linear_fwd.restype = ctypes.c_int
 _lib.qlora_linear_bwd.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, _p, _i64,
                                   ctypes.c_float, _p, _p, _p, _p, _sz, _p]
 _lib.qlora_linear_bwd.restype = ctypes.c_int
+_lib.qlora_workspace_bytes_multi.argtypes = [_i64, _i64, ctypes.POINTER(_i64), ctypes.c_int, _i64,
+                                             ctypes.c_int]
+_lib.qlora_workspace_bytes_multi.restype = _sz
+_lib.qlora_linear_fwd_multi.argtypes = [ctypes.POINTER(_NF4WeightC), ctypes.c_int, _p, _i64,
+                                        ctypes.POINTER(_p), ctypes.POINTER(_p), _i64, ctypes.c_float,
+                                        _p, _p, _sz, _p]
+_lib.qlora_linear_fwd_multi.restype = ctypes.c_int
+_lib.qlora_linear_bwd_multi.argtypes = [ctypes.POINTER(_NF4WeightC), ctypes.c_int, _p, _p, _i64,
+                                        ctypes.POINTER(_p), ctypes.POINTER(_p), _i64, ctypes.c_float,
+                                        _p, ctypes.POINTER(_p), ctypes.POINTER(_p), _p, _sz, _p]
+_lib.qlora_linear_bwd_multi.restype = ctypes.c_int
 _lib.nf4_quantize_nodq.argtypes = [_p, _i64, _p, _p, _p]
 _lib.nf4_quantize_nodq.restype = ctypes.c_int
 _lib.nf4_dequantize_nodq.argtypes = [_p, _p, _i64, _p, _p]
@@ -277,6 +289,69 @@ def qlora_merge(W: NF4Weight, A, B, r: int, alpha: float, out=None, ws=None):
     _check(_lib.qlora_merge(ctypes.byref(wc), _ptr(A), _ptr(B), r, float(alpha), _ptr(out), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(dev)), "qlora_merge")
     return out
+
+
+def qlora_workspace_bytes_multi(T: int, in_features: int, out_features, r: int, backward: bool) -> int:
+    outs = (_i64 * len(out_features))(*[int(o) for o in out_features])
+    return int(_lib.qlora_workspace_bytes_multi(T, in_features, outs, len(out_features), r,
+                                                1 if backward else 0))
+
+
+def _multi_ws(ws, T, n_in, outs, r, backward, device):
+    need = qlora_workspace_bytes_multi(T, n_in, outs, r, backward)
+    if ws is None:
+        ws = make_workspace(need, device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _ptr_array(ts):
+    return (_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def qlora_linear_fwd_multi(Ws, X, As, Bs, r: int, alpha: float, Y=None, ws=None):
+    """Projections sharing X (e.g. q|k|v, gate|up): Y [T, sum out_i] bf16 with
+    projection i's columns side by side."""
+    n = len(Ws)
+    T = X.shape[0]
+    n_in = Ws[0].cols
+    outs = [W.rows for W in Ws]
+    _need(X, torch.bfloat16, "X", T * n_in)
+    for W, A, B in zip(Ws, As, Bs):
+        _need(A, torch.bfloat16, "A", r * W.cols)
+        _need(B, torch.bfloat16, "B", W.rows * r)
+    if Y is None:
+        Y = torch.empty(T, sum(outs), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", T * sum(outs))
+    ws, ws_bytes = _multi_ws(ws, T, n_in, outs, r, False, X.device)
+    wc = (_NF4WeightC * n)(*[W._c() for W in Ws])
+    _check(_lib.qlora_linear_fwd_multi(wc, n, _ptr(X), T, _ptr_array(As), _ptr_array(Bs), r,
+                                       float(alpha), _ptr(Y), _ptr(ws), ws_bytes, _stream(X.device)),
+           "qlora_linear_fwd_multi")
+    return Y
+
+
+def qlora_linear_bwd_multi(Ws, X, dY, As, Bs, r: int, alpha: float, dX=None, dAs=None, dBs=None,
+                           ws=None):
+    """-> (dX [T, in] bf16 summed over the projections, [dA_i fp32], [dB_i fp32])."""
+    n = len(Ws)
+    T = X.shape[0]
+    n_in = Ws[0].cols
+    outs = [W.rows for W in Ws]
+    dev = X.device
+    _need(X, torch.bfloat16, "X", T * n_in)
+    _need(dY, torch.bfloat16, "dY", T * sum(outs))
+    if dX is None:
+        dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
+    if dAs is None:
+        dAs = [torch.empty(r, n_in, dtype=torch.float32, device=dev) for _ in range(n)]
+    if dBs is None:
+        dBs = [torch.empty(o, r, dtype=torch.float32, device=dev) for o in outs]
+    ws, ws_bytes = _multi_ws(ws, T, n_in, outs, r, True, dev)
+    wc = (_NF4WeightC * n)(*[W._c() for W in Ws])
+    _check(_lib.qlora_linear_bwd_multi(wc, n, _ptr(X), _ptr(dY), T, _ptr_array(As), _ptr_array(Bs),
+                                       r, float(alpha), _ptr(dX), _ptr_array(dAs), _ptr_array(dBs),
+                                       _ptr(ws), ws_bytes, _stream(dev)), "qlora_linear_bwd_multi")
+    return dX, dAs, dBs
 
 
 def nf4_codebook():

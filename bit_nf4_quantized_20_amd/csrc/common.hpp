@@ -50,30 +50,41 @@ hipError_t launch_nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* code
 hipError_t launch_nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel,
                                       uint16_t* out, hipStream_t s);
 // out[c][r] = W_hat[r][c] for W_hat [rows][cols]; rows % 64 == 0, cols % 64 == 0
+// (out rows have stride ldo elements, ldo >= rows)
 hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t* absmax_q,
                                             const float* scale, int64_t rows, int64_t cols,
-                                            uint16_t* out, hipStream_t s);
+                                            uint16_t* out, int64_t ldo, hipStream_t s);
 
-// sU[t][j] = scale * sum_k in[t][k] P[j][k] for j < r (P rows K-contiguous),
-// 0 for r <= j < rp, as bf16 pairs hi + lo.  Written to (either may be null)
-//   pad    [T][2*rp]   hi in columns [0, rp), lo in [rp, 2*rp)
-//   hilo_t [2*rp][ldt] transposed: hi rows [0, rp), lo rows [rp, 2*rp)
-// `part` is fp32 scratch of lora_down_part_bytes(T, K, rp) bytes.  K % 64 == 0.
-size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t rp);
-hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* P, int64_t r,
-                            float scale, uint16_t* pad, uint16_t* hilo_t, int64_t ldt, int64_t rp,
-                            float* part, hipStream_t s);
+// Projections that share one input (q|k|v, gate|up) go through one call.
+constexpr int kMaxProj = 8;
+struct DownFactors { const uint16_t* p[kMaxProj]; };
+
+// sU[t][p rp + j] = scale * sum_k in[t][k] P_p[j][k] for the nP rank factors
+// P_p [r][K] (K-contiguous; in [T][K] with row stride ldin), j < r; 0 for
+// r <= j < rp; as bf16 pairs hi + lo.  Written to (either may be null)
+//   pad    [T][ldpad]        projection p: hi in columns [2p rp, 2p rp + rp),
+//                            lo in [2p rp + rp, 2(p+1) rp)
+//   hilo_t [nP][2 rp][ldt]   transposed: hi rows [0, rp), lo rows [rp, 2 rp)
+// `part` is fp32 scratch of lora_down_part_bytes(T, K, nP * rp) bytes.
+// K % 64 == 0, rp % 64 == 0.
+size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t nprp);
+hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t K,
+                            const uint16_t* const* P, int nP, int64_t r, float scale, uint16_t* pad,
+                            int64_t ldpad, uint16_t* hilo_t, int64_t ldt, int64_t rp, float* part,
+                            hipStream_t s);
 // out(j, c) += sum_t (Pt[j][t] + Pt[rp + j][t]) Q[t][c] for j < r, c < C (C % 64
 // == 0), atomically into out[j * C + c] (out_jc) or out[c * r + j].
+// (Q rows have stride ldq elements, ldq >= C)
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
-                            int64_t C, int64_t r, float* out, bool out_jc, hipStream_t s);
+                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s);
 // dst[c][r] = src[r][c] for src [R][C]
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
                                  hipStream_t s);
 // dst[i][j] = dst[i][Cp + j] (R x 2Cp, bf16) = src(i, j) for j < C, else 0, where
 // src(i, j) = src[i * C + j] (!transpose) or src[j * R + i] (transpose).
+// (dst rows have stride ldd elements, ldd >= 2 Cp)
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
-                           int64_t Cp, hipStream_t s);
+                           int64_t Cp, int64_t ldd, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
 
 // C[M][N] (bf16, ldc) = sum over the two K segments of act_i[m][k] * wt_i[n][k]
@@ -84,11 +95,18 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
                           int64_t ldc, hipStream_t s);
 
-// Same, with the main segment's weight given as NF4 storage of W_hat [N][K0]
-// (dequantized while staged into LDS).
-hipError_t launch_gemm_nf4(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
-                           const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
-                           int64_t K0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
+// Same, with the main segment's weight given as NF4 projections stacked
+// along N (nproj <= kMaxProj; projection i owns output columns
+// [sum_{j<i} rows_j, ... + rows_i) and is dequantized while staged into
+// LDS); the LoRA segment's activation is each projection's act1 (row stride
+// lda1), its weight wt1 [N][ldw1] shared.
+struct Nf4Proj {
+  const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
+  int64_t rows;
+  const uint16_t* act1;
+};
+hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,
+                           int64_t lda0, int64_t K0, int64_t lda1, const uint16_t* wt1,
                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);
 
 // W_merged[m][n] = bf16(W_hat[m][n] + s * sum_j Bp[m][j] Atp[n][j]) for the
@@ -106,6 +124,6 @@ bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                              int64_t in, int64_t out, const uint16_t* X, int64_t T,
                              const uint16_t* A, const uint16_t* B, int64_t r, float s,
-                             uint16_t* Y, hipStream_t st);
+                             uint16_t* Y, int64_t ldy, hipStream_t st);
 
 }  // namespace qlora

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
-    uint16_t* __restrict__ Y, int64_t out) {
+    uint16_t* __restrict__ Y, int64_t out, int64_t ldy) {
   // staging tiles during the main loop; reused for the epilogue afterwards
   __shared__ u32x4 s_tiles[kWaves][2][kTileSlots];
   __shared__ u32x4 s_codes[kWaves][kCodeSlots];
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
       for (int j = 0; j < r; ++j) lora += s_u[t * kUP + j] * s_b[m][j];
       y[e] = base + s * lora;
     }
-    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * out + r0 + rr) = pack_bf16x2(y[0], y[1]);
+    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * ldy + r0 + rr) = pack_bf16x2(y[0], y[1]);
   }
 }
 
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
-    uint16_t* __restrict__ Y, int64_t out) {
+    uint16_t* __restrict__ Y, int64_t out, int64_t ldy) {
   constexpr int kPairs = kWaves / 2;
   __shared__ u32x4 s_x[kPairs][2][kTileSlots];   // X tiles by chunk parity
   __shared__ u32x4 s_a[kPairs][kTileSlots];      // A tile of each U wave
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
       for (int j = 0; j < r; ++j) lora += s_u[t][j] * s_b[m][j];
       y[e] = base + s * lora;
     }
-    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * out + r0 + rr) = pack_bf16x2(y[0], y[1]);
+    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * ldy + r0 + rr) = pack_bf16x2(y[0], y[1]);
   }
 }
 
@@ -527,7 +527,7 @@ bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r) {
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                              int64_t in, int64_t out, const uint16_t* X, int64_t T,
                              const uint16_t* A, const uint16_t* B, int64_t r, float s,
-                             uint16_t* Y, hipStream_t st) {
+                             uint16_t* Y, int64_t ldy, hipStream_t st) {
   if (!decode_fits(T, in, out, r)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(out / kRows));
   const dim3 block(kThreads);
@@ -535,10 +535,10 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, cons
   const int iT = static_cast<int>(T), ir = static_cast<int>(r);
 #define QLORA_DEC(RTV)                                                                            \
   hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, codes, absmax_q, scale, in, X, iT, \
-                     A, B, ir, s, Y, out)
+                     A, B, ir, s, Y, out, ldy)
   if (rt <= 1)
     hipLaunchKernelGGL(k_decode_fwd_split, grid, block, 0, st, codes, absmax_q, scale, in, X, iT, A, B,
-                       ir, s, Y, out);
+                       ir, s, Y, out, ldy);
   else if (rt <= 2) QLORA_DEC(2);
   else QLORA_DEC(4);
 #undef QLORA_DEC

@@ -224,19 +224,39 @@ __device__ __forceinline__ void xcd_tile(int64_t gm, int64_t gn, int64_t& mt, in
   nt = in_g / gm_g;
 }
 
+// One projection of an NF4 main segment: its rows [n0, n0 + rows) of C, its
+// storage and its LoRA activation block (act1 of the extension segment).
+struct Nf4Seg {
+  const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
+  int64_t n0, rows;
+  const uint16_t* act1;
+};
+
 struct GemmArgs {
   int64_t M, N;
-  // main segment activation and weight (bf16 weight, or NF4 when codes != nullptr)
+  // main segment activation and weight: a bf16 weight (wt0), or NF4
+  // projections stacked along N (nseg >= 1; no tile straddles two)
   const uint16_t* act0; int64_t lda0;
   const uint16_t* wt0; int64_t ldw0;
-  const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
+  int nseg;
+  Nf4Seg seg[kMaxProj];
   int64_t K0;
-  // LoRA extension segment
+  // LoRA extension segment (with NF4 projections, act1 comes from seg[])
   const uint16_t* act1; int64_t lda1;
   const uint16_t* wt1; int64_t ldw1;
   int64_t K1;
   uint16_t* C; int64_t ldc;
 };
+
+// The projection holding output column n0 (uniform; constant indices only,
+// so the table stays in scalar registers).
+__device__ __forceinline__ Nf4Seg seg_of(const GemmArgs& p, int64_t n0) {
+  Nf4Seg sg = p.seg[0];
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i)
+    if (i < p.nseg && n0 >= p.seg[i].n0) sg = p.seg[i];
+  return sg;
+}
 
 }  // namespace
 
@@ -332,7 +352,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
     TA ta;
     TQ tq;
     ta.init(p.act0, p.lda0, m0, p.M, tid);
-    tq.init(p.codes, p.absmax_q, p.scale, p.K0, n0, p.N, tid);
+    const Nf4Seg sg = seg_of(p, n0);
+    tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
     struct R { typename TA::Regs a; typename TQ::Regs w; };
     R r0, r1;
     segment(r0, r1, 0, s0,
@@ -364,7 +385,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   if (s1 > 0) {  // LoRA extension segment
     TA ta;
     TW tw;
-    ta.init(p.act1, p.lda1, m0, p.M, tid);
+    ta.init(kNf4 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, tid);
     tw.init(p.wt1, p.ldw1, n0, p.N, tid);
     struct R { typename TA::Regs a; typename TW::Regs w; };
     R r0, r1;
@@ -552,7 +573,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
   if constexpr (kNf4) {
     Nf4Tile<BN, NT> tq;
-    tq.init(p.codes, p.absmax_q, p.scale, p.K0, n0, p.N, tid);
+    const Nf4Seg sg = seg_of(p, n0);
+    tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
     main_loop(ta, tq, s0);
   } else {
     DtlTile<BN, NW> tw;
@@ -564,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   if (s1 > 0) {
     DtlTile<BM, NW> ta1;
     DtlTile<BN, NW> tw1;
-    ta1.init(p.act1, p.lda1, m0, p.M, wv, lane);
+    ta1.init(kNf4 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, wv, lane);
     tw1.init(p.wt1, p.ldw1, n0, p.N, wv, lane);
     for (int64_t e = 0; e < s1; ++e) {
       __syncthreads();  // every wave is done reading stage 0
@@ -627,18 +649,49 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
                           int64_t ldc, hipStream_t s) {
-  GemmArgs a{M, N, act0, lda0, wt0, ldw0, nullptr, nullptr, nullptr, K0,
-             act1, lda1, wt1, ldw1, K1, C, ldc};
+  GemmArgs a{};
+  a.M = M; a.N = N; a.act0 = act0; a.lda0 = lda0; a.wt0 = wt0; a.ldw0 = ldw0; a.nseg = 0; a.K0 = K0;
+  a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1; a.C = C; a.ldc = ldc;
   return launch_tiles<false>(a, s);
 }
 
-hipError_t launch_gemm_nf4(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
-                           const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
-                           int64_t K0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
+hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,
+                           int64_t lda0, int64_t K0, int64_t lda1, const uint16_t* wt1,
                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s) {
-  GemmArgs a{M, N, act0, lda0, nullptr, 0, codes, absmax_q, scale, K0,
-             act1, lda1, wt1, ldw1, K1, C, ldc};
-  return launch_tiles<true>(a, s);
+  if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.M = M; a.act0 = act0; a.lda0 = lda0; a.K0 = K0; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1;
+  a.K1 = K1; a.ldc = ldc;
+  int64_t n = 0;
+  for (int i = 0; i < nproj; ++i) n += proj[i].rows;
+  a.N = n;
+  // one launch when no tile straddles two projections, else one per projection
+  const int64_t tile = ceil_div(M, 256) * ceil_div(n, 256) >= 256 ? 256 : 128;
+  bool aligned = true;
+  for (int i = 0; i + 1 < nproj; ++i) aligned = aligned && (proj[i].rows % tile == 0);
+  if (aligned) {
+    a.nseg = nproj;
+    int64_t n0 = 0;
+    for (int i = 0; i < nproj; ++i) {
+      a.seg[i] = Nf4Seg{proj[i].codes, proj[i].absmax_q, proj[i].scale, n0, proj[i].rows, proj[i].act1};
+      n0 += proj[i].rows;
+    }
+    a.C = C;
+    return launch_tiles<true>(a, s);
+  }
+  int64_t n0 = 0;
+  for (int i = 0; i < nproj; ++i) {
+    GemmArgs b = a;
+    b.N = proj[i].rows;
+    b.nseg = 1;
+    b.seg[0] = Nf4Seg{proj[i].codes, proj[i].absmax_q, proj[i].scale, 0, proj[i].rows, proj[i].act1};
+    b.wt1 = wt1 + n0 * ldw1;
+    b.C = C + n0;
+    const hipError_t e = launch_tiles<true>(b, s);
+    if (e != hipSuccess) return e;
+    n0 += proj[i].rows;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qlora

@@ -49,9 +49,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t down_rsrc(const uint16_t* base
 }
 }  // namespace
 
-// part[kc][t][j] (fp32, [KC][T][rp]) = sum over chunk kc of in[t][k] P[j][k]
-__global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restrict__ in, int64_t T,
-                                                        int64_t K, const uint16_t* __restrict__ P,
+// part[kc][t][p rp + j] (fp32, [KC][T][nP rp]) = sum over chunk kc of
+// in[t][k] P_p[j][k], for the nP rank factors P_p (one per projection).
+__global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restrict__ in, int64_t ldin,
+                                                        int64_t T, int64_t K, DownFactors P,
                                                         int r, int rp, int64_t kch,
                                                         float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kDownTok * 64];
@@ -61,19 +62,22 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kDownTok;
   const int64_t kc = blockIdx.y;
-  const int j0 = static_cast<int>(blockIdx.z) * kDownRanks;
+  const int tiles_per_p = rp / kDownRanks;
+  const int pj = static_cast<int>(blockIdx.z) / tiles_per_p;           // projection
+  const int j0 = (static_cast<int>(blockIdx.z) % tiles_per_p) * kDownRanks;
+  const int npr = static_cast<int>(gridDim.z) * kDownRanks;            // nP * rp
   const int64_t kbeg = kc * kch;
   const int64_t kend = kbeg + kch < K ? kbeg + kch : K;
   const int nsteps = static_cast<int>((kend - kbeg) / 64);
 
   // rows past T (tokens) or r (ranks) read as zero
-  const __amdgpu_buffer_rsrc_t rs_x = down_rsrc(in, K, t0, T);
-  const __amdgpu_buffer_rsrc_t rs_p = down_rsrc(P, K, j0, r);
+  const __amdgpu_buffer_rsrc_t rs_x = down_rsrc(in, ldin, t0, T);
+  const __amdgpu_buffer_rsrc_t rs_p = down_rsrc(P.p[pj], K, j0, r);
   uint32_t xoff[4], poff[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int id = tid + 256 * i, row = id >> 3, q = id & 7;
-    xoff[i] = static_cast<uint32_t>((row * K + q * 8) * 2);
+    xoff[i] = static_cast<uint32_t>((row * ldin + q * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -138,12 +142,11 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
   for (int c = 0; c < 2; ++c) {
     const int64_t t = t0 + wm * 64 + c * 32 + r32;
     if (t >= T) continue;
-    float* dst = part + (kc * T + t) * rp + j0 + wn * 32 + 4 * h;
+    float* dst = part + (kc * T + t) * npr + pj * rp + j0 + wn * 32 + 4 * h;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      if (j0 + wn * 32 + 8 * g + 4 * h < rp)
-        *reinterpret_cast<f32x4v*>(dst + 8 * g) =
-            f32x4v{acc[c][4 * g], acc[c][4 * g + 1], acc[c][4 * g + 2], acc[c][4 * g + 3]};
+      *reinterpret_cast<f32x4v*>(dst + 8 * g) =
+          f32x4v{acc[c][4 * g], acc[c][4 * g + 1], acc[c][4 * g + 2], acc[c][4 * g + 3]};
   }
 }
 
@@ -156,23 +159,27 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
 // both stores are coalesced.
 constexpr int kDownMaxKC = 16;
 __global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__ part, int64_t T, int KC,
-                                                       int rp, float scale, uint16_t* __restrict__ pad,
-                                                       uint16_t* __restrict__ hilo_t, int64_t ldt) {
+                                                       int nP, int rp, float scale, uint16_t* __restrict__ pad,
+                                                       int64_t ldpad, uint16_t* __restrict__ hilo_t,
+                                                       int64_t ldt) {
   __shared__ uint32_t s_t[64][17];  // [rank][token] hi | lo << 16
   const int tid = threadIdx.x;
   const int64_t tb = static_cast<int64_t>(blockIdx.x) * 16;
   const int jb = static_cast<int>(blockIdx.y) * 64;
   // phase 1: thread -> rank jb + tid % 64, tokens tb + tid / 64 + 4 i
   const int jl = tid & 63;
+  const int npr = nP * rp;
+  // rank columns of this workgroup: projection pj, ranks jj .. jj + 63 (rp % 64 == 0)
+  const int pj = jb / rp, jj = jb % rp;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tl = (tid >> 6) + 4 * i;
     const int64_t t = tb + tl;
-    const bool ok = t < T && jb + jl < rp;
+    const bool ok = t < T;
     float pv[kDownMaxKC];
 #pragma unroll
     for (int q = 0; q < kDownMaxKC; ++q)
-      pv[q] = (ok && q < KC) ? part[(static_cast<int64_t>(q) * T + t) * rp + jb + jl] : 0.f;
+      pv[q] = (ok && q < KC) ? part[(static_cast<int64_t>(q) * T + t) * npr + jb + jl] : 0.f;
     float v = 0.f;
 #pragma unroll
     for (int q = 0; q < kDownMaxKC; ++q) v += pv[q];
@@ -181,8 +188,9 @@ __global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__
     const float hi = __builtin_bit_cast(float, hb << 16);
     const uint32_t lb = pack_bf16x2(v - hi, 0.f) & 0xffffu;
     if (ok && pad != nullptr) {
-      pad[t * 2 * rp + jb + jl] = static_cast<uint16_t>(hb);
-      pad[t * 2 * rp + rp + jb + jl] = static_cast<uint16_t>(lb);
+      uint16_t* row = pad + t * ldpad + pj * 2 * rp + jj + jl;
+      row[0] = static_cast<uint16_t>(hb);
+      row[rp] = static_cast<uint16_t>(lb);
     }
     s_t[jl][tl] = hb | (lb << 16);  // tokens >= T hold zero
   }
@@ -195,10 +203,10 @@ __global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = (tid >> 4) + 16 * i;
-    if (jb + j >= rp) break;
     const uint32_t v = s_t[j][tl];
-    hilo_t[static_cast<int64_t>(jb + j) * ldt + t] = static_cast<uint16_t>(v & 0xffffu);
-    hilo_t[static_cast<int64_t>(rp + jb + j) * ldt + t] = static_cast<uint16_t>(v >> 16);
+    uint16_t* blk = hilo_t + static_cast<int64_t>(pj) * 2 * rp * ldt;  // projection pj's [2 rp][ldt]
+    blk[static_cast<int64_t>(jj + j) * ldt + t] = static_cast<uint16_t>(v & 0xffffu);
+    blk[static_cast<int64_t>(rp + jj + j) * ldt + t] = static_cast<uint16_t>(v >> 16);
   }
 }
 
@@ -217,29 +225,34 @@ int64_t down_chunk(int64_t T, int64_t K, int64_t rp) {
 }
 }  // namespace
 
-size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t rp) {
-  const int64_t kch = down_chunk(T, K, rp);
-  return static_cast<size_t>(ceil_div(K, kch) * T * rp * 4);
+size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t nprp) {
+  const int64_t kch = down_chunk(T, K, nprp);
+  return static_cast<size_t>(ceil_div(K, kch) * T * nprp * 4);
 }
 
-hipError_t launch_lora_down(const uint16_t* in, int64_t T, int64_t K, const uint16_t* P, int64_t r,
-                            float scale, uint16_t* pad, uint16_t* hilo_t, int64_t ldt, int64_t rp,
-                            float* part, hipStream_t s) {
+hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t K,
+                            const uint16_t* const* P, int nP, int64_t r, float scale, uint16_t* pad,
+                            int64_t ldpad, uint16_t* hilo_t, int64_t ldt, int64_t rp, float* part,
+                            hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (nP < 1 || nP > kMaxProj) return hipErrorInvalidValue;
   // 32-bit buffer offsets: one tile's rows of `in` and P stay under 2^31 bytes
-  if (kDownTok * K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const int64_t kch = down_chunk(T, K, rp);
+  if (kDownTok * ldin * 2 >= (int64_t(1) << 31) || kDownRanks * K * 2 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  DownFactors f{};
+  for (int i = 0; i < nP; ++i) f.p[i] = P[i];
+  const int64_t kch = down_chunk(T, K, nP * rp);
   const int64_t KC = ceil_div(K, kch);
   const dim3 grid(static_cast<uint32_t>(ceil_div(T, kDownTok)), static_cast<uint32_t>(KC),
-                  static_cast<uint32_t>(ceil_div(rp, kDownRanks)));
-  hipLaunchKernelGGL(k_lora_down_part, grid, dim3(256), 0, s, in, T, K, P, static_cast<int>(r),
+                  static_cast<uint32_t>(nP * rp / kDownRanks));
+  hipLaunchKernelGGL(k_lora_down_part, grid, dim3(256), 0, s, in, ldin, T, K, f, static_cast<int>(r),
                      static_cast<int>(rp), kch, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tt = hilo_t != nullptr ? (ldt > T ? ldt : T) : T;
-  const dim3 fgrid(static_cast<uint32_t>(ceil_div(tt, 16)), static_cast<uint32_t>(ceil_div(rp, 64)));
-  hipLaunchKernelGGL(k_lora_down_fin, fgrid, dim3(256), 0, s, part, T, static_cast<int>(KC),
-                     static_cast<int>(rp), scale, pad, hilo_t, ldt);
+  const dim3 fgrid(static_cast<uint32_t>(ceil_div(tt, 16)), static_cast<uint32_t>(nP * rp / 64));
+  hipLaunchKernelGGL(k_lora_down_fin, fgrid, dim3(256), 0, s, part, T, static_cast<int>(KC), nP,
+                     static_cast<int>(rp), scale, pad, ldpad, hilo_t, ldt);
   return hipGetLastError();
 }
 
@@ -275,8 +288,8 @@ __device__ __forceinline__ int grad_qslot(int c, int w) { return kGradPitch * c 
 template <int JT, bool kJC>
 __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ Pt, int64_t T,
                                                    int64_t ldt, int rp, const uint16_t* __restrict__ Q,
-                                                   int64_t C, int r, int j0, float* __restrict__ out,
-                                                   int64_t TS) {
+                                                   int64_t C, int64_t ldq, int r, int j0,
+                                                   float* __restrict__ out, int64_t TS) {
   constexpr int kPRows = 64 * JT;  // hi rows [0, 32JT), lo rows [32JT, 64JT)
   __shared__ uint32_t s_q[2][kGradCT * kGradPitch];
   __shared__ uint32_t s_p[2][kPRows * kGradPitch];
@@ -290,9 +303,9 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 
   // Q resource starts at this slice and ends at row T (or 2^31 - 1 bytes;
   // the host keeps a slice under 2^30 bytes)
-  const uint64_t q_bytes = static_cast<uint64_t>(T - ts) * C * 2;
+  const uint64_t q_bytes = static_cast<uint64_t>(T - ts) * ldq * 2;
   const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Q + ts * C), 0, static_cast<int>(q_bytes < 0x7fffffffu ? q_bytes : 0x7fffffffu),
+      const_cast<uint16_t*>(Q + ts * ldq), 0, static_cast<int>(q_bytes < 0x7fffffffu ? q_bytes : 0x7fffffffu),
       kBufferWord3);
   const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Pt), 0, static_cast<int>(static_cast<uint64_t>(2 * rp) * ldt * 2), kBufferWord3);
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t t = t0 - ts + 2 * (tp0 + 16 * (i >> 1)) + (i & 1);  // rows past T read as zero
-      const uint32_t off = col_ok ? static_cast<uint32_t>((t * C + c0 + 8 * cg) * 2) : kPastEnd;
+      const uint32_t off = col_ok ? static_cast<uint32_t>((t * ldq + c0 + 8 * cg) * 2) : kPastEnd;
       qv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_q, off, 0, 0));
     }
 #pragma unroll
@@ -401,7 +414,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 }
 
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
-                            int64_t C, int64_t r, float* out, bool out_jc, hipStream_t s) {
+                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   // token slices (multiples of 64) for about 512 workgroups
   const int64_t ctiles = ceil_div(C, kGradCT);
@@ -410,7 +423,7 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
   if (slices > max_slices) slices = max_slices;
   if (slices < 1) slices = 1;
   // 32-bit buffer offsets: a slice of Q stays under 2^30 bytes, Pt under 2^31
-  const int64_t min_slices = ceil_div(T * C * 2, int64_t(1) << 30);
+  const int64_t min_slices = ceil_div(T * ldq * 2, int64_t(1) << 30);
   if (slices < min_slices) slices = min_slices;
   if (2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int64_t TS = round_up(ceil_div(T, slices), 64);
@@ -422,7 +435,7 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
     const int jt = static_cast<int>(ceil_div(left < 32 * kGradMaxJT ? left : 32 * kGradMaxJT, 32));
     const int ij0 = static_cast<int>(j0);
 #define QLORA_GRAD(JTV, JC)                                                                          \
-  hipLaunchKernelGGL((k_lora_grad<JTV, JC>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ir, ij0, out, TS)
+  hipLaunchKernelGGL((k_lora_grad<JTV, JC>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ldq, ir, ij0, out, TS)
     if (out_jc) {
       if (jt <= 1) QLORA_GRAD(1, true);
       else if (jt <= 2) QLORA_GRAD(2, true);
@@ -444,21 +457,21 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pad_bf16(const uint16_t* __restrict__ src, int64_t R,
                                                   int64_t C, int transpose,
-                                                  uint16_t* __restrict__ dst, int64_t Cp) {
+                                                  uint16_t* __restrict__ dst, int64_t Cp, int64_t ldd) {
   // dst row i = [src row i zero-padded to Cp | the same again]
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= R * Cp) return;
   const int64_t i = idx / Cp, j = idx % Cp;
   uint16_t v = 0;
   if (j < C) v = transpose ? src[j * R + i] : src[i * C + j];
-  dst[i * 2 * Cp + j] = v;
-  dst[i * 2 * Cp + Cp + j] = v;
+  dst[i * ldd + j] = v;
+  dst[i * ldd + Cp + j] = v;
 }
 
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
-                           int64_t Cp, hipStream_t s) {
+                           int64_t Cp, int64_t ldd, hipStream_t s) {
   hipLaunchKernelGGL(k_pad_bf16, dim3(static_cast<uint32_t>(ceil_div(R * Cp, 256))), dim3(256), 0,
-                     s, src, R, C, transpose ? 1 : 0, dst, Cp);
+                     s, src, R, C, transpose ? 1 : 0, dst, Cp, ldd);
   return hipGetLastError();
 }
 

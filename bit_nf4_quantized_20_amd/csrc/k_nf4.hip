@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
                                                           const uint8_t* __restrict__ absmax_q,
                                                           const float* __restrict__ scale,
                                                           int64_t rows, int64_t cols,
-                                                          uint16_t* __restrict__ out) {
+                                                          uint16_t* __restrict__ out, int64_t ldo) {
   constexpr int kPitch = 64 + 2;  // bf16 elements per LDS row (odd dword pitch)
   __shared__ uint16_t tile[4][64 * kPitch];
   const int wv = threadIdx.x >> 6;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // lane now owns output row (c0 + lane), elements r0 .. r0+63
-  u32x4* dst = reinterpret_cast<u32x4*>(out + (c0 + lane) * rows + r0);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + (c0 + lane) * ldo + r0);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     uint32_t d[4];
@@ -229,10 +229,10 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
 
 hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t* absmax_q,
                                             const float* scale, int64_t rows, int64_t cols,
-                                            uint16_t* out, hipStream_t s) {
+                                            uint16_t* out, int64_t ldo, hipStream_t s) {
   const int64_t tiles = (rows / 64) * (cols / 64);
   hipLaunchKernelGGL(k_nf4_dequantize_t, dim3(static_cast<uint32_t>(ceil_div(tiles, 4))), dim3(256),
-                     0, s, codes, absmax_q, scale, rows, cols, out);
+                     0, s, codes, absmax_q, scale, rows, cols, out, ldo);
   return hipGetLastError();
 }
 

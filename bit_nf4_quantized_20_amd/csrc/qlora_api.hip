@@ -61,34 +61,52 @@ struct BwdLayout {
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
 
-bool fwd_uses_decode(int64_t T, int64_t in, int64_t out, int64_t r) { return decode_fits(T, in, out, r); }
+// n projections sharing `in`: outs[i] rows each, N = sum outs[i]
+int64_t total_out(const int64_t* outs, int n) {
+  int64_t N = 0;
+  for (int i = 0; i < n; ++i) N += outs[i];
+  return N;
+}
 
-FwdLayout fwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
+// the small-token forward takes each projection on its own and needs no workspace
+bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
+  for (int i = 0; i < n; ++i)
+    if (!decode_fits(T, in, outs[i], r)) return false;
+  return true;
+}
+
+FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
   FwdLayout l{0, 0, 0, 0};
   Carve c;
-  if (fwd_uses_decode(T, in, out, r)) return l;  // the fused small-token kernel needs none
-  const int64_t rp = padded_rank(r);
-  l.u_pad = c.take(static_cast<size_t>(T * rp * 4));
-  l.b_pad = c.take(static_cast<size_t>(out * rp * 4));
-  l.part = c.take(lora_down_part_bytes(T, in, rp));
+  if (fwd_uses_decode(T, in, outs, n, r)) return l;
+  const int64_t rp = padded_rank(r), N = total_out(outs, n);
+  l.u_pad = c.take(static_cast<size_t>(T * n * rp * 4));  // [T][n 2rp] bf16
+  l.b_pad = c.take(static_cast<size_t>(N * rp * 4));      // [N][2rp] bf16
+  l.part = c.take(lora_down_part_bytes(T, in, n * rp));
   l.total = c.off;
   return l;
 }
 
 int64_t token_pitch(int64_t T) { return round_up(T, 8); }
 
-BwdLayout bwd_layout(int64_t T, int64_t in, int64_t out, int64_t r) {
-  const int64_t rp = padded_rank(r);
+BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
+  const int64_t rp = padded_rank(r), N = total_out(outs, n);
+  int64_t out_max = 0;
+  size_t part = lora_down_part_bytes(T, in, n * rp);
+  for (int i = 0; i < n; ++i) {
+    out_max = outs[i] > out_max ? outs[i] : out_max;
+    const size_t pv = lora_down_part_bytes(T, outs[i], rp);
+    part = pv > part ? pv : part;
+  }
   Carve c;
   BwdLayout l;
-  l.ut = c.take(static_cast<size_t>(2 * rp * token_pitch(T) * 2));
-  l.vt = c.take(static_cast<size_t>(2 * rp * token_pitch(T) * 2));
-  l.v_pad = c.take(static_cast<size_t>(T * rp * 4));
-  l.b_t = c.take(static_cast<size_t>(r * out * 2));
-  l.a_t_pad = c.take(static_cast<size_t>(in * rp * 4));
-  l.w_dq_t = c.take(static_cast<size_t>(in * out * 2));
-  const size_t pu = lora_down_part_bytes(T, in, rp), pv = lora_down_part_bytes(T, out, rp);
-  l.part = c.take(pu > pv ? pu : pv);
+  l.ut = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));  // [n][2rp][T'] bf16
+  l.vt = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));
+  l.v_pad = c.take(static_cast<size_t>(T * n * rp * 4));                // [T][n 2rp] bf16
+  l.b_t = c.take(static_cast<size_t>(r * out_max * 2));                 // one B^T at a time
+  l.a_t_pad = c.take(static_cast<size_t>(in * n * rp * 4));             // [in][n 2rp] bf16
+  l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));                   // [in][N] bf16
+  l.part = c.take(part);
   l.total = c.off;
   return l;
 }
@@ -171,72 +189,126 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
 
 size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                              int backward) {
-  if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;
-  const size_t need = backward ? bwd_layout(T, in_features, out_features, r).total
-                               : fwd_layout(T, in_features, out_features, r).total;
+  return qlora_workspace_bytes_multi(T, in_features, &out_features, 1, r, backward);
+}
+
+size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t* out_features,
+                                   int n, int64_t r, int backward) {
+  if (n < 1 || n > kMaxProj || out_features == nullptr) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
+  const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r).total
+                               : fwd_layout(T, in_features, out_features, n, r).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
 
-int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
-                     const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
-                     qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream) {
-  if (int st = check_weight(W)) return st;
-  const int64_t out = W->rows, in = W->cols;
-  if (!linear_shapes_ok(T, in, out, r)) return QLORA_ERR_SHAPE;
-  if (!A || !B) return QLORA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Checks the n projections (shared in_features, rank r) and collects their
+// row counts; QLORA_OK or the first error.
+int check_projections(const qlora_nf4_weight* W, int n, int64_t T, int64_t r, int64_t* outs,
+                      int64_t* in) {
+  if (W == nullptr) return QLORA_ERR_NULL;
+  if (n < 1 || n > kMaxProj) return QLORA_ERR_SHAPE;
+  for (int i = 0; i < n; ++i) {
+    if (int st = check_weight(&W[i])) return st;
+    if (W[i].cols != W[0].cols) return QLORA_ERR_SHAPE;
+    if (!linear_shapes_ok(T, W[i].cols, W[i].rows, r)) return QLORA_ERR_SHAPE;
+    outs[i] = W[i].rows;
+  }
+  *in = W[0].cols;
+  return QLORA_OK;
+}
+
+int check_factors(const qlora_bf16* const* A, const qlora_bf16* const* B, int n) {
+  if (A == nullptr || B == nullptr) return QLORA_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    if (!A[i] || !B[i]) return QLORA_ERR_NULL;
+    if (!aligned16(A[i]) || !aligned16(B[i])) return QLORA_ERR_ALIGN;
+  }
+  return QLORA_OK;
+}
+
+int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64_t T,
+                    const qlora_bf16* const* A, const qlora_bf16* const* B, int64_t r, float alpha,
+                    qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream) {
+  int64_t outs[kMaxProj], in = 0;
+  if (int st = check_projections(W, n, T, r, outs, &in)) return st;
+  if (int st = check_factors(A, B, n)) return st;
   if (T > 0 && (!X || !Y)) return QLORA_ERR_NULL;
-  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y)) return QLORA_ERR_ALIGN;
+  if (!aligned16(X) || !aligned16(Y)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
   if (T == 0) return QLORA_OK;
-  const FwdLayout lay = fwd_layout(T, in, out, r);
+  const FwdLayout lay = fwd_layout(T, in, outs, n, r);
   if (lay.total > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = alpha / static_cast<float>(r);
-  if (fwd_uses_decode(T, in, out, r))
-    return launched(launch_decode_fwd(W->codes, W->absmax_q, W->absmax_scale, in, out, X, T, A, B,
-                                      r, scale, Y, s));
+  const int64_t N = total_out(outs, n);
+  if (fwd_uses_decode(T, in, outs, n, r)) {
+    int64_t off = 0;
+    for (int i = 0; i < n; ++i) {
+      const hipError_t e = launch_decode_fwd(W[i].codes, W[i].absmax_q, W[i].absmax_scale, in, outs[i],
+                                             X, T, A[i], B[i], r, scale, Y + off, N, s);
+      if (e != hipSuccess) return launched(e);
+      off += outs[i];
+    }
+    return QLORA_OK;
+  }
 
   const int64_t rp = padded_rank(r);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* u_pad = reinterpret_cast<uint16_t*>(base + lay.u_pad);
   uint16_t* b_pad = reinterpret_cast<uint16_t*>(base + lay.b_pad);
   float* part = reinterpret_cast<float*>(base + lay.part);
-  hipError_t e = launch_lora_down(X, T, in, A, r, scale, u_pad, nullptr, 0, rp, part, s);  // s X A^T
-  if (e == hipSuccess) e = launch_pad_bf16(B, out, r, false, b_pad, rp, s);
+  // s X A_i^T for every projection in one pass over X: [T][n 2rp]
+  hipError_t e = launch_lora_down(X, in, T, in, A, n, r, scale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s);
+  Nf4Proj proj[kMaxProj];
+  int64_t off = 0;
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * 2 * rp, rp, 2 * rp, s);
+    proj[i] = Nf4Proj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], u_pad + i * 2 * rp};
+    off += outs[i];
+  }
   if (e == hipSuccess)
-    e = launch_gemm_nf4(T, out, X, in, W->codes, W->absmax_q, W->absmax_scale, in, u_pad, 2 * rp,
-                        b_pad, 2 * rp, 2 * rp, Y, out, s);
+    e = launch_gemm_nf4(T, n, proj, X, in, in, n * 2 * rp, b_pad, 2 * rp, 2 * rp, Y, N, s);
   return launched(e);
 }
 
-int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora_bf16* dY,
-                     int64_t T, const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
-                     qlora_bf16* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
-                     qlora_stream stream) {
-  if (int st = check_weight(W)) return st;
-  const int64_t out = W->rows, in = W->cols;
-  if (!linear_shapes_ok(T, in, out, r)) return QLORA_ERR_SHAPE;
-  if (!A || !B || !dA || !dB) return QLORA_ERR_NULL;
+int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const qlora_bf16* dY,
+                    int64_t T, const qlora_bf16* const* A, const qlora_bf16* const* B, int64_t r,
+                    float alpha, qlora_bf16* dX, float* const* dA, float* const* dB, void* ws,
+                    size_t ws_bytes, qlora_stream stream) {
+  int64_t outs[kMaxProj], in = 0;
+  if (int st = check_projections(W, n, T, r, outs, &in)) return st;
+  if (int st = check_factors(A, B, n)) return st;
+  if (dA == nullptr || dB == nullptr) return QLORA_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    if (!dA[i] || !dB[i]) return QLORA_ERR_NULL;
+    if (!aligned16(dA[i]) || !aligned16(dB[i])) return QLORA_ERR_ALIGN;
+  }
   if (T > 0 && (!X || !dY || !dX)) return QLORA_ERR_NULL;
-  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
-      !aligned16(dA) || !aligned16(dB))
-    return QLORA_ERR_ALIGN;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
-  const BwdLayout lay = bwd_layout(T, in, out, r);
+  const BwdLayout lay = bwd_layout(T, in, outs, n, r);
   if (T > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_fill_f32(dA, r * in, 0.f, s);
-  if (e == hipSuccess) e = launch_fill_f32(dB, out * r, 0.f, s);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    e = launch_fill_f32(dA[i], r * in, 0.f, s);
+    if (e == hipSuccess) e = launch_fill_f32(dB[i], outs[i] * r, 0.f, s);
+  }
   if (T == 0 || e != hipSuccess) return launched(e);
 
   const float scale = alpha / static_cast<float>(r);
-  const int64_t rp = padded_rank(r), tp = token_pitch(T);
+  const int64_t rp = padded_rank(r), tp = token_pitch(T), N = total_out(outs, n);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* ut = reinterpret_cast<uint16_t*>(base + lay.ut);
   uint16_t* vt = reinterpret_cast<uint16_t*>(base + lay.vt);
@@ -244,19 +316,68 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora
   uint16_t* b_t = reinterpret_cast<uint16_t*>(base + lay.b_t);
   uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(base + lay.a_t_pad);
   uint16_t* w_dq_t = reinterpret_cast<uint16_t*>(base + lay.w_dq_t);
-
   float* part = reinterpret_cast<float*>(base + lay.part);
-  e = launch_lora_down(X, T, in, A, r, scale, nullptr, ut, tp, rp, part, s);           // (sU)^T
-  if (e == hipSuccess) e = launch_transpose_bf16(B, out, r, b_t, s);                  // B^T [r][out]
-  if (e == hipSuccess) e = launch_lora_down(dY, T, out, b_t, r, scale, v_pad, vt, tp, rp, part, s);  // sV
-  if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, s);           // A^T padded
+
+  // (sU_i)^T for every projection in one pass over X
+  e = launch_lora_down(X, in, T, in, A, n, r, scale, nullptr, 0, ut, tp, rp, part, s);
+  int64_t off = 0;
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    // s V_i = s dY_i B_i with dY_i the projection's columns of dY
+    e = launch_transpose_bf16(B[i], outs[i], r, b_t, s);
+    const uint16_t* bt = b_t;
+    if (e == hipSuccess)
+      e = launch_lora_down(dY + off, N, T, outs[i], &bt, 1, r, scale, v_pad + i * 2 * rp, n * 2 * rp,
+                           vt + i * 2 * rp * tp, tp, rp, part, s);
+    if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
+    if (e == hipSuccess)
+      e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
+                                           w_dq_t + off, N, s);
+    off += outs[i];
+  }
+  // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
   if (e == hipSuccess)
-    e = launch_nf4_dequantize_transposed(W->codes, W->absmax_q, W->absmax_scale, out, in, w_dq_t, s);
-  if (e == hipSuccess)
-    e = launch_gemm_nt(T, in, dY, out, w_dq_t, out, out, v_pad, 2 * rp, a_t_pad, 2 * rp, 2 * rp, dX, in, s);
-  if (e == hipSuccess) e = launch_lora_grad(vt, T, tp, rp, X, in, r, dA, true, s);    // dA = (sV)^T X
-  if (e == hipSuccess) e = launch_lora_grad(ut, T, tp, rp, dY, out, r, dB, false, s); // dB = dY^T (sU)
+    e = launch_gemm_nt(T, in, dY, N, w_dq_t, N, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp,
+                       dX, in, s);
+  off = 0;
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, dA[i], true, s);  // dA_i
+    if (e == hipSuccess)
+      e = launch_lora_grad(ut + i * 2 * rp * tp, T, tp, rp, dY + off, outs[i], N, r, dB[i], false, s);
+    off += outs[i];
+  }
   return launched(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
+                     const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
+                     qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream) {
+  return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64_t T,
+                           const qlora_bf16* const* A, const qlora_bf16* const* B, int64_t r,
+                           float alpha, qlora_bf16* Y, void* ws, size_t ws_bytes,
+                           qlora_stream stream) {
+  return linear_fwd_impl(W, n, X, T, A, B, r, alpha, Y, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora_bf16* dY,
+                     int64_t T, const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
+                     qlora_bf16* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                     qlora_stream stream) {
+  return linear_bwd_impl(W, 1, X, dY, T, &A, &B, r, alpha, dX, &dA, &dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X,
+                           const qlora_bf16* dY, int64_t T, const qlora_bf16* const* A,
+                           const qlora_bf16* const* B, int64_t r, float alpha, qlora_bf16* dX,
+                           float* const* dA, float* const* dB, void* ws, size_t ws_bytes,
+                           qlora_stream stream) {
+  return linear_bwd_impl(W, n, X, dY, T, A, B, r, alpha, dX, dA, dB, ws, ws_bytes, stream);
 }
 
 size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, int64_t r) {
@@ -285,8 +406,8 @@ int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16
   const int64_t rp = padded_rank(r);
   uint16_t* b_pad = static_cast<uint16_t*>(ws);
   uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + round_up(out * rp * 4, 256));
-  hipError_t e = launch_pad_bf16(B, out, r, false, b_pad, rp, s);
-  if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, s);
+  hipError_t e = launch_pad_bf16(B, out, r, false, b_pad, rp, 2 * rp, s);
+  if (e == hipSuccess) e = launch_pad_bf16(A, in, r, true, a_t_pad, rp, 2 * rp, s);
   if (e == hipSuccess)
     e = launch_merge(W->codes, W->absmax_q, W->absmax_scale, out, in, b_pad, a_t_pad, 2 * rp, rp,
                      alpha / static_cast<float>(r), W_out, s);

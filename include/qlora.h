@@ -172,6 +172,36 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
                      qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream);
 
 /*
+ * Multi-projection forms: n (1..8) projections that share the input X and
+ * the rank r / alpha, e.g. q|k|v or gate|up (coddykit "LoRA y QLoRA": the
+ * adapters go on several target modules of the same layer; ultralytics
+ * glossary "QLoRA": adapters on every linear).  One pass computes
+ * X A_i^T for all i, one GEMM launch covers all projections (their outputs
+ * side by side), and the backward's dX is one GEMM over the concatenated
+ * outputs, rounded once:
+ *   Y  [T, N] bf16,  N = sum_i out_i; projection i owns columns
+ *                    [sum_{j<i} out_j, sum_{j<=i} out_j) of Y (and of dY)
+ *   dX [T, in] = sum_i (dY_i W_hat_i + s (dY_i B_i) A_i), one rounding
+ *   dA[i] [r, in], dB[i] [out_i, r] fp32, overwritten
+ *   W[i]  NF4 weights, all with the same cols = in;  A[i], B[i] as above
+ * Arguments and errors otherwise as for the single-projection calls; the
+ * workspace is sized by qlora_workspace_bytes_multi (0 for invalid shapes,
+ * n outside 1..8 or a NULL out_features).  n = 1 is exactly the
+ * single-projection call.
+ */
+size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t* out_features,
+                                   int n, int64_t r, int backward);
+int qlora_linear_fwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64_t T,
+                           const qlora_bf16* const* A, const qlora_bf16* const* B, int64_t r,
+                           float alpha, qlora_bf16* Y, void* ws, size_t ws_bytes,
+                           qlora_stream stream);
+int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X,
+                           const qlora_bf16* dY, int64_t T, const qlora_bf16* const* A,
+                           const qlora_bf16* const* B, int64_t r, float alpha, qlora_bf16* dX,
+                           float* const* dA, float* const* dB, void* ws, size_t ws_bytes,
+                           qlora_stream stream);
+
+/*
  * qlora_linear_bwd -- B1..B3 for the forward above, with s = alpha/r:
  *   dX = dY W_hat + s (dY B) A        [T, in]  bf16 (one rounding)
  *   dA = s (dY B)^T X                 [r, in]  fp32

@@ -191,6 +191,37 @@ def test_linear_validation():
         assert len(lib.qlora_status_string(s)) > 0
 
 
+def test_multi_projection_validation():
+    lib = _lib()
+    i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.qlora_workspace_bytes_multi.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes_multi.restype = sz
+    lib.qlora_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes.restype = sz
+    lib.qlora_linear_fwd_multi.argtypes = [ctypes.POINTER(_W), ctypes.c_int, vp, i64, ctypes.POINTER(vp),
+                                           ctypes.POINTER(vp), i64, ctypes.c_float, vp, vp, sz, vp]
+    lib.qlora_linear_fwd_multi.restype = ctypes.c_int
+    outs = (i64 * 3)(4096, 1024, 1024)
+    one = (i64 * 1)(4096)
+    # n = 1 is the single-projection size; more projections need more
+    assert lib.qlora_workspace_bytes_multi(64, 4096, one, 1, 16, 1) == lib.qlora_workspace_bytes(64, 4096, 4096, 16, 1)
+    assert lib.qlora_workspace_bytes_multi(64, 4096, outs, 3, 16, 1) > lib.qlora_workspace_bytes(64, 4096, 4096, 16, 1)
+    assert lib.qlora_workspace_bytes_multi(64, 4096, outs, 0, 16, 0) == 0
+    assert lib.qlora_workspace_bytes_multi(64, 4096, outs, 9, 16, 0) == 0
+    assert lib.qlora_workspace_bytes_multi(64, 4096, None, 1, 16, 0) == 0
+    F = _FAKE
+    Ws = (_W * 2)(_W(F, F, F, 128, 256), _W(F, F, F, 64, 256))
+    ptrs = (vp * 2)(F, F)
+    nulls = (vp * 2)(F, None)
+    ws = lib.qlora_workspace_bytes_multi(32, 256, (i64 * 2)(128, 64), 2, 8, 0)
+    call = lambda **k: lib.qlora_linear_fwd_multi(k.get("W", Ws), k.get("n", 2), F, 32, k.get("A", ptrs),
+                                                  ptrs, 8, 16.0, F, F, k.get("wsb", ws), None)
+    assert call(n=0) == -2 and call(n=9) == -2
+    assert call(W=(_W * 2)(_W(F, F, F, 128, 256), _W(F, F, F, 64, 320))) == -2  # in differs
+    assert call(A=nulls) == -1
+    assert call(wsb=ws - 1) == -4
+
+
 def test_nodq_validation():
     lib = _lib()
     i64, vp = ctypes.c_int64, ctypes.c_void_p
