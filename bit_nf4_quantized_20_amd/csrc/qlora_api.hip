@@ -53,8 +53,14 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t u_pad, b_pad, part, total;
+  size_t u_pad, b_pad, part, w_dq, total;
 };
+
+// From this many tokens on, the forward dequantizes each weight once into the
+// workspace and runs the bf16 GEMM: the fused kernel repeats the
+// dequantization for every 256-token tile (16 times at T = 4096), which
+// costs more than one extra pass of 2.5 bytes per weight.
+constexpr int64_t kMaterializeTokens = 2048;
 struct BwdLayout {
   size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, total;
 };
@@ -76,13 +82,14 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 }
 
 FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
-  FwdLayout l{0, 0, 0, 0};
+  FwdLayout l{0, 0, 0, 0, 0};
   Carve c;
   if (fwd_uses_decode(T, in, outs, n, r)) return l;
   const int64_t rp = padded_rank(r), N = total_out(outs, n);
   l.u_pad = c.take(static_cast<size_t>(T * n * rp * 4));  // [T][n 2rp] bf16
-  l.b_pad = c.take(static_cast<size_t>(N * rp * 4));      // [N][2rp] bf16
+  l.b_pad = c.take(static_cast<size_t>(N * n * rp * 4));  // [N][2rp] or [N][n 2rp] bf16
   l.part = c.take(lora_down_part_bytes(T, in, n * rp));
+  if (T >= kMaterializeTokens) l.w_dq = c.take(static_cast<size_t>(N * in * 2));  // [N][in] bf16
   l.total = c.off;
   return l;
 }
@@ -267,6 +274,25 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   float* part = reinterpret_cast<float*>(base + lay.part);
   // s X A_i^T for every projection in one pass over X: [T][n 2rp]
   hipError_t e = launch_lora_down(X, in, T, in, A, n, r, scale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s);
+  if (T >= kMaterializeTokens) {
+    // W_hat of every projection into [N][in] bf16, then the bf16 GEMM; the
+    // LoRA term as extra K-steps over [sU_0 | sU_1 | ...] against B_i placed
+    // block-diagonally in [N][n 2rp]
+    uint16_t* w_dq = reinterpret_cast<uint16_t*>(base + lay.w_dq);
+    const int64_t ldb = n * 2 * rp;
+    if (e == hipSuccess && n > 1) e = launch_fill_f32(reinterpret_cast<float*>(b_pad), N * ldb / 2, 0.f, s);
+    int64_t off = 0;
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+      e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * ldb + i * 2 * rp, rp, ldb, s);
+      if (e == hipSuccess)
+        e = launch_nf4_dequantize(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i] * in,
+                                  w_dq + off * in, s);
+      off += outs[i];
+    }
+    if (e == hipSuccess)
+      e = launch_gemm_nt(T, N, X, in, w_dq, in, in, u_pad, ldb, b_pad, ldb, ldb, Y, N, s);
+    return launched(e);
+  }
   Nf4Proj proj[kMaxProj];
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {

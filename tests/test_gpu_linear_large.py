@@ -105,3 +105,10 @@ def test_ragged_tokens_on_large_tiles():
     # q-shaped 4096 x 4096 with T = 4136: 17 x 16 tiles of 256, the last row of
     # tiles 40 tokens tall (rows past T read as zero and are not stored)
     _check(4, 0, T=4136)
+
+
+def test_fused_dequant_gemm_below_materialize_threshold():
+    # 8B MLP gate at T = 1536 (6 x 56 tiles of 256): the forward takes the fused
+    # NF4 GEMM (codes dequantized while staged into LDS); from T = 2048 on it
+    # dequantizes the weight once into the workspace instead
+    _check(3, 0, T=1536)
