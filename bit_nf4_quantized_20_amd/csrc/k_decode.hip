@@ -33,6 +33,8 @@
 //
 // Epilogue: the eight waves' fp32 accumulators of the base product and of U
 // meet in LDS; Y = base + s U B^T is rounded to bf16 once.
+#include <type_traits>
+
 #include "common.hpp"
 #include "nf4_format.hpp"
 
@@ -322,7 +324,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
 // member's address-unit stalls with the other's vector arithmetic.  The X
 // tile of a chunk is written by the U wave and read by both, double-buffered
 // by chunk parity with one workgroup barrier per chunk.
+//
+// Two chunks' loads are in flight per wave.  That only holds if the wait
+// counts the compiler derives at each consumer allow the younger chunk to
+// stay outstanding, which needs one fixed issue order:
+//   - every load of a chunk step is issued unconditionally (offsets of rows,
+//     pieces or chunks that do not exist are pushed past the buffer end and
+//     read zeros without touching memory), so no branch decides whether a
+//     load exists;
+//   - the steps run from chunk -2: the first two only issue loads, so each
+//     register set is filled by the same instructions every time;
+//   - with NS > 0 the step sequence is fully unrolled (NS steps, compile-time
+//     register sets, no loop-carried copies that would force a full wait);
+//     NS = 0 keeps a loop whose start is hidden from the optimizer so the
+//     loading steps are not peeled off into a differently ordered prologue.
+// XP = token-row pairs of the X tile (T <= 2 XP).
 // ---------------------------------------------------------------------------
+template <int XP, int NS>
 __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
@@ -348,11 +366,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
 
   const int bw0 = static_cast<int>(nb * qtr / kPairs), bw1 = static_cast<int>(nb * (qtr + 1) / kPairs);
   const int nch = (bw1 - bw0 + 3) / 4;
-  const int nch_all = static_cast<int>((ceil_div(nb, kPairs) + 3) / 4);  // same for every wave
+  // steps every wave runs (the same count for all: one barrier each), even
+  const int nsteps = NS > 0 ? NS : static_cast<int>(round_up((ceil_div(nb, kPairs) + 3) / 4, 2));
   const uint32_t row = static_cast<uint32_t>(r0) + n;
   const uint32_t inu = static_cast<uint32_t>(in), nbu = static_cast<uint32_t>(nb);
-  const int xpairs = (T + 1) / 2;
-  const int apairs = (r + 1) / 2;
 
   const uint32_t wbytes = static_cast<uint32_t>(static_cast<uint64_t>(out) * in / 2);
   const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
@@ -368,48 +385,69 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(out) * r * 2), kBufferWord3);
 
-  // B rows of this workgroup (16 x r <= 256 values), converted in the epilogue
+  // B rows of this workgroup (16 x r <= 256 values), converted in the
+  // epilogue; every thread loads (past the end for tid >= 256), so no branch
+  // makes the compiler wait for this load before the main loop
   uint32_t braw;
   {
     const int rr = tid >> 4, j = tid & 15;
     const uint32_t off = (rr < kRows && j < r) ? ((static_cast<uint32_t>(r0) + rr) * r + j) * 2 : kPastEnd;
-    braw = tid < kRows * 16 ? __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0) : 0u;
+    braw = __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // runs step(c, d) for c = -2 .. nsteps - 1, d = c & 1 a compile-time index
+  auto run_steps = [&](auto&& step) {
+    if constexpr (NS > 0) {
+#pragma unroll
+      for (int c = -2; c < NS; c += 2) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      int cstart = -2;
+      __asm__ volatile("" : "+s"(cstart));  // opaque start: the loading steps stay in the loop
+      for (int c = cstart; c < nsteps; c += 2) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
+      }
+    }
+  };
 
   if (dq_wave) {
     // ------------------------------------------------ dequantize waves
     u32x4* tc = s_codes[qtr];
-    auto load_codes = [&](CodeStage& cs, int c) {
+    CodeStage cs[2];
+    auto load_codes = [&](CodeStage& st, int c) {
+      const uint32_t pe = c < nch ? 0u : kPastEnd;  // uniform, OR-ed into the offsets
       const uint32_t base = static_cast<uint32_t>(bw0 + 4 * c) * 32 + 16 * (lane & 7);
       const uint32_t rl = static_cast<uint32_t>(r0) + (lane >> 3);
-      cs.c0 = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, rl * (inu / 2) + base, 0, kStream));
-      cs.c1 = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, (rl + 8) * (inu / 2) + base, 0, kStream));
+      st.c0 = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, (rl * (inu / 2) + base) | pe, 0, kStream));
+      st.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs_codes, ((rl + 8) * (inu / 2) + base) | pe, 0, kStream));
       const uint32_t bi = row * nbu + static_cast<uint32_t>(bw0 + 4 * c + g);
-      cs.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi, 0, 0);
-      cs.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (bi >> 8) * 4, 0, 0));
+      st.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi | pe, 0, 0);
+      st.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, ((bi >> 8) * 4) | pe, 0, 0));
     };
-    auto step = [&](int c, CodeStage& cs, const u32x4* tx) {
-      const bool live = c < nch;
+    auto step = [&](int c, auto d) {
+      CodeStage& st = cs[decltype(d)::value];
       u32x4 cc0 = zero4, cc1 = zero4;
-      uint32_t qv = 0u;
-      float sv = 0.f;
-      if (live) {
+      float ah = 0.f;
+      if (c >= 0) {
+        // codes to their owners: row n, block g = pieces 2g, 2g + 1
         const int m = lane >> 3, pc = lane & 7;
-        tc[8 * m + (pc ^ ((m >> 1) & 7))] = cs.c0;
-        tc[8 * (m + 8) + (pc ^ (((m + 8) >> 1) & 7))] = cs.c1;
+        tc[8 * m + (pc ^ ((m >> 1) & 7))] = st.c0;
+        tc[8 * (m + 8) + (pc ^ (((m + 8) >> 1) & 7))] = st.c1;
         cc0 = tc[8 * n + ((2 * g) ^ ((n >> 1) & 7))];
         cc1 = tc[8 * n + ((2 * g + 1) ^ ((n >> 1) & 7))];
-        qv = cs.q;
-        sv = cs.sc;
-        if (c + 2 < nch) load_codes(cs, c + 2);
+        ah = dq_absmax(st.q, st.sc);
       }
-      __syncthreads();  // X(c) is in tx
-      if (live) {
-        const Nf4Table tab = make_table(dq_absmax(qv, sv));
+      load_codes(st, c + 2);
+      if (c >= 0) {
+        __syncthreads();  // X(c) is in its tile
+        const u32x4* tx = s_x[qtr][decltype(d)::value];
+        const Nf4Table tab = make_table(ah);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
@@ -421,51 +459,41 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
         }
       }
     };
-    CodeStage cs0, cs1;
-    if (nch > 0) load_codes(cs0, 0);
-    if (nch > 1) load_codes(cs1, 1);
-    for (int c = 0; c < nch_all; c += 2) {
-      step(c, cs0, s_x[qtr][0]);
-      if (c + 1 < nch_all) step(c + 1, cs1, s_x[qtr][1]);
-    }
+    run_steps(step);
   } else {
     // ------------------------------------------------ U waves
     u32x4* ta = s_a[qtr];
-    auto load_rows = [&](u32x4 (&reg)[8], const __amdgpu_buffer_rsrc_t& rs, int npairs, int c) {
+    u32x4 xs[2][XP], as[2][8];
+    auto load_rows = [&](auto& reg, const __amdgpu_buffer_rsrc_t& rs, auto npairs, int c) {
       const uint32_t k0 = static_cast<uint32_t>(bw0 + 4 * c) * 64;
-      const int kvalid = (bw1 - bw0 - 4 * c) * 64;
+      // valid k of this chunk: 256, fewer in a partial last chunk, none past the range
+      const int lim = c < nch ? min((bw1 - bw0 - 4 * c) * 64, 256) : 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i >= npairs) break;
+      for (int i = 0; i < decltype(npairs)::value; ++i) {
         const int t = 2 * i + half, p = piece ^ t;
-        const uint32_t off = (kvalid >= 256 || 8 * p < kvalid) ? ((t * inu) + k0 + 8 * p) * 2 : kPastEnd;
+        const uint32_t off = 8 * p < lim ? ((t * inu) + k0 + 8 * p) * 2 : kPastEnd;
         reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
       }
     };
-    // token / rank rows that no chunk writes stay zero in both X tiles and the A tile
+    // token rows that no chunk writes stay zero in both X tiles
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i >= xpairs) {
-        s_x[qtr][0][64 * i + lane] = zero4;
-        s_x[qtr][1][64 * i + lane] = zero4;
-      }
-      if (i >= apairs) ta[64 * i + lane] = zero4;
+    for (int i = XP; i < 8; ++i) {
+      s_x[qtr][0][64 * i + lane] = zero4;
+      s_x[qtr][1][64 * i + lane] = zero4;
     }
-    auto step = [&](int c, u32x4 (&xr)[8], u32x4 (&ar)[8], u32x4* tx) {
-      const bool live = c < nch;
-      if (live) {
+    auto step = [&](int c, auto d) {
+      constexpr int kD = decltype(d)::value;
+      u32x4* tx = s_x[qtr][kD];
+      if (c >= 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i < xpairs) tx[64 * i + lane] = xr[i];
-          if (i < apairs) ta[64 * i + lane] = ar[i];
-        }
-        if (c + 2 < nch) {
-          load_rows(xr, rs_x, xpairs, c + 2);
-          load_rows(ar, rs_a, apairs, c + 2);
-        }
+        for (int i = 0; i < XP; ++i) tx[64 * i + lane] = xs[kD][i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ta[64 * i + lane] = as[kD][i];
       }
-      __syncthreads();  // X(c) is in tx for the partner
-      if (live) {
+      load_rows(xs[kD], rs_x, std::integral_constant<int, XP>{}, c + 2);
+      load_rows(as[kD], rs_a, std::integral_constant<int, 8>{}, c + 2);  // ranks >= r read zeros
+      if (c >= 0) {
+        __syncthreads();  // X(c) is in tx for the partner
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
@@ -474,19 +502,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
         }
       }
     };
-    u32x4 x0[8], x1[8], a0[8], a1[8];
-    if (nch > 0) {
-      load_rows(x0, rs_x, xpairs, 0);
-      load_rows(a0, rs_a, apairs, 0);
-    }
-    if (nch > 1) {
-      load_rows(x1, rs_x, xpairs, 1);
-      load_rows(a1, rs_a, apairs, 1);
-    }
-    for (int c = 0; c < nch_all; c += 2) {
-      step(c, x0, a0, s_x[qtr][0]);
-      if (c + 1 < nch_all) step(c + 1, x1, a1, s_x[qtr][1]);
-    }
+    run_steps(step);
   }
 
   // ---------------- epilogue: waves 0-3 hold D[row][token], 4-7 D[rank][token]
@@ -501,20 +517,21 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
     s_u[t][j] = u;
   }
   __syncthreads();
-  if (tid < T * (kRows / 2)) {
-    const int t = tid / (kRows / 2), rr = 2 * (tid % (kRows / 2));
-    float y[2];
+  // Y = base + s U B^T: four adjacent lanes per output, each summing a quarter
+  // of the 16 ranks (ranks >= r are zero in U and B)
+  for (int o = tid; o < T * 64; o += kThreads) {
+    const int t = o >> 6, m = (o >> 2) & 15, jq = o & 3;
+    float lora = 0.f;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int m = rr + e;
+    for (int i = 0; i < 4; ++i) lora += s_u[t][4 * jq + i] * s_b[m][4 * jq + i];
+    lora += __shfl_xor(lora, 1);
+    lora += __shfl_xor(lora, 2);
+    if (jq == 0) {
       float base = 0.f;
 #pragma unroll
       for (int w = 0; w < kPairs; ++w) base += s_acc[w][16 * (m >> 2) + t][m & 3];
-      float lora = 0.f;
-      for (int j = 0; j < r; ++j) lora += s_u[t][j] * s_b[m][j];
-      y[e] = base + s * lora;
+      Y[static_cast<int64_t>(t) * ldy + r0 + m] = static_cast<uint16_t>(pack_bf16x2(base + s * lora, 0.f));
     }
-    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * ldy + r0 + rr) = pack_bf16x2(y[0], y[1]);
   }
 }
 
@@ -536,10 +553,28 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, cons
 #define QLORA_DEC(RTV)                                                                            \
   hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, codes, absmax_q, scale, in, X, iT, \
                      A, B, ir, s, Y, out, ldy)
-  if (rt <= 1)
-    hipLaunchKernelGGL(k_decode_fwd_split, grid, block, 0, st, codes, absmax_q, scale, in, X, iT, A, B,
-                       ir, s, Y, out, ldy);
-  else if (rt <= 2) QLORA_DEC(2);
+  if (rt <= 1) {
+    // chunk steps per wave: fully unrolled when they number 4 (in <= 4096)
+    // or 8 (in <= 8192), a loop otherwise
+    const int64_t steps = round_up((ceil_div(in / 64, 4) + 3) / 4, 2);
+    const int ns = steps == 4 ? 4 : steps == 8 ? 8 : 0;
+    const int xp = T <= 2 ? 1 : T <= 4 ? 2 : T <= 8 ? 4 : 8;
+#define QLORA_SPLIT(XPV, NSV)                                                                     \
+  hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV>), grid, block, 0, st, codes, absmax_q, scale, in, X, \
+                     iT, A, B, ir, s, Y, out, ldy)
+#define QLORA_SPLIT_NS(XPV)        \
+  do {                             \
+    if (ns == 4) QLORA_SPLIT(XPV, 4); \
+    else if (ns == 8) QLORA_SPLIT(XPV, 8); \
+    else QLORA_SPLIT(XPV, 0);      \
+  } while (0)
+    if (xp == 1) QLORA_SPLIT_NS(1);
+    else if (xp == 2) QLORA_SPLIT_NS(2);
+    else if (xp == 4) QLORA_SPLIT_NS(4);
+    else QLORA_SPLIT_NS(8);
+#undef QLORA_SPLIT_NS
+#undef QLORA_SPLIT
+  } else if (rt <= 2) QLORA_DEC(2);
   else QLORA_DEC(4);
 #undef QLORA_DEC
   return hipGetLastError();
