@@ -399,8 +399,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
   // runs step(c, d) for c = -2 .. nsteps - 1, d = c & 1 a compile-time index
   auto run_steps = [&](auto&& step) {
     if constexpr (NS > 0) {
+      // With 8 or more token rows the U waves' loads (X and A, L2 resident)
+      // go out first: the dequantize waves issue their codes (HBM) once the
+      // U waves have issued their first two chunks.
+      if constexpr (XP >= 4) {
+        if (dq_wave) __syncthreads();
+      }
+      step(-2, std::integral_constant<int, 0>{});
+      step(-1, std::integral_constant<int, 1>{});
+      if constexpr (XP >= 4) {
+        if (!dq_wave) __syncthreads();
+      }
 #pragma unroll
-      for (int c = -2; c < NS; c += 2) {
+      for (int c = 0; c < NS; c += 2) {
         step(c, std::integral_constant<int, 0>{});
         step(c + 1, std::integral_constant<int, 1>{});
       }
