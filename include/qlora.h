@@ -147,7 +147,8 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  * Returns 0 for invalid shapes and at least 256 otherwise.  Host only.
  *
  * The workspace is scratch for intermediate products (padded LoRA factors,
- * the transposed dequantized weight of the backward).  It needs no
+ * the transposed dequantized weight of the backward and, from T = 2048 on,
+ * the forward's dequantized weight: 2 * out * in bytes).  It needs no
  * initialisation and keeps nothing between calls.  The small-token forward
  * (T <= 16 and r <= 64) does not use it; ws may then be NULL.  Calls that
  * overlap in time (different streams) must not share a workspace.
