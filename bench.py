@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "QLoRA linear fwd+bwd TFLOP/s and NF4 weight-stream GB/s (% of roofline)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+DROPOUT_P = 0.05  # the lora_dropout value the pages configure
 NF4_BYTES_PER_WEIGHT = 0.515869140625
 
 
@@ -349,7 +350,7 @@ def train_leg(q, synth, dev, bf):
     wl = synth.WORKLOADS[3]
     T, r, alpha = wl.tokens[0], wl.r, wl.alpha
     res = {"T": T, "r": r, "alpha": alpha}
-    tot_flop, tot_ms = 0.0, 0.0
+    tot_flop, tot_ms, tot_dms = 0.0, 0.0, 0.0
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -396,11 +397,33 @@ def train_leg(q, synth, dev, bf):
                        "fwd_bwd_TFLOPs": round((flop_f + flop_b) / ((ms_f + ms_b) * 1e-3) / 1e12, 1)}
         tot_flop += flop_f + flop_b
         tot_ms += ms_f + ms_b
-        del W, X, dY, Y, dX, wsf, wsb
+
+        # the same step with LoRA dropout (p = 0.05, a fresh seeded keep mask)
+        keep = torch.from_numpy(synth.keep_mask(synth.seed_for(3, pi, "keep"), T, n_in, DROPOUT_P)).to(dev)
+        wdf = q.make_workspace(q.qlora_workspace_bytes_dropout(T, n_in, n_out, r, False), dev)
+
+        def dfwd():
+            q.qlora_linear_fwd_dropout(W, X, keep, DROPOUT_P, A, B, r, alpha, Y=Y, ws=wdf)
+
+        def dbwd():
+            q.qlora_linear_bwd_dropout(W, X, dY, keep, DROPOUT_P, A, B, r, alpha, dX=dX, dA=dA, dB=dB,
+                                       ws=wsb)
+
+        for _ in range(8):
+            dfwd()
+            dbwd()
+        dms_f = timed(dfwd, 20)
+        dms_b = timed(dbwd, 20)
+        res[p.name]["dropout_fwd_ms"] = round(dms_f, 3)
+        res[p.name]["dropout_bwd_ms"] = round(dms_b, 3)
+        tot_dms += dms_f + dms_b
+        del W, X, dY, Y, dX, wsf, wsb, wdf, keep
     tf = tot_flop / (tot_ms * 1e-3) / 1e12
     res["mlp_fwd_bwd_ms"] = round(tot_ms, 3)
     res["mlp_fwd_bwd_TFLOPs"] = round(tf, 1)
     res["frac_of_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+    res["mlp_dropout"] = {"p": DROPOUT_P, "fwd_bwd_ms": round(tot_dms, 3),
+                          "fwd_bwd_TFLOPs": round(tot_flop / (tot_dms * 1e-3) / 1e12, 1)}
 
     # gate and up share X: one multi-projection call each way (one LoRA
     # down-projection pass, one GEMM launch over both, one dX GEMM)

@@ -81,6 +81,14 @@ _lib.qlora_merge_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.qlora_merge_workspace_bytes.restype = _sz
 _lib.qlora_merge.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, ctypes.c_float, _p, _p, _sz, _p]
 _lib.qlora_merge.restype = ctypes.c_int
+_lib.qlora_workspace_bytes_dropout.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+_lib.qlora_workspace_bytes_dropout.restype = _sz
+_lib.qlora_linear_fwd_dropout.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _i64, _p, ctypes.c_float, _p,
+                                          _p, _i64, ctypes.c_float, _p, _p, _sz, _p]
+_lib.qlora_linear_fwd_dropout.restype = ctypes.c_int
+_lib.qlora_linear_bwd_dropout.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, ctypes.c_float,
+                                          _p, _p, _i64, ctypes.c_float, _p, _p, _p, _p, _sz, _p]
+_lib.qlora_linear_bwd_dropout.restype = ctypes.c_int
 _lib.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
 _lib.nf4_codebook.restype = None
 _lib.nf4_code_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -267,6 +275,70 @@ def qlora_linear_bwd(W: NF4Weight, X, dY, A, B, r: int, alpha: float, dX=None, d
     _check(_lib.qlora_linear_bwd(ctypes.byref(wc), _ptr(X), _ptr(dY), T, _ptr(A), _ptr(B), r,
                                  float(alpha), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
                                  _stream(dev)), "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+def qlora_workspace_bytes_dropout(T: int, in_features: int, out_features: int, r: int,
+                                  backward: bool) -> int:
+    return int(_lib.qlora_workspace_bytes_dropout(T, in_features, out_features, r, 1 if backward else 0))
+
+
+def _dropout_ws(ws, T, n_in, n_out, r, backward, device):
+    need = qlora_workspace_bytes_dropout(T, n_in, n_out, r, backward)
+    if ws is None:
+        key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+        ws = _WS_CACHE.get(key)
+        if ws is None or ws.numel() < need:
+            ws = make_workspace(need, device)
+            _WS_CACHE[key] = ws
+    return ws, ws.numel() * ws.element_size()
+
+
+def qlora_linear_fwd_dropout(W: NF4Weight, X, keep, p: float, A, B, r: int, alpha: float, Y=None,
+                             ws=None):
+    """Y = X W_hat^T + (alpha/r) ((keep o X / (1 - p)) A^T) B^T; keep is the
+    packed mask [T, in/8] uint8 (bit k % 8 of byte k / 8 = element k kept)."""
+    T = X.shape[0]
+    _need(X, torch.bfloat16, "X", T * W.cols)
+    _need(keep, torch.uint8, "keep", T * (W.cols // 8))
+    _need(A, torch.bfloat16, "A", r * W.cols)
+    _need(B, torch.bfloat16, "B", W.rows * r)
+    if Y is None:
+        Y = torch.empty(T, W.rows, dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", T * W.rows)
+    ws, ws_bytes = _dropout_ws(ws, T, W.cols, W.rows, r, False, X.device)
+    wc = W._c()
+    _check(_lib.qlora_linear_fwd_dropout(ctypes.byref(wc), _ptr(X), T, _ptr(keep), float(p), _ptr(A),
+                                         _ptr(B), r, float(alpha), _ptr(Y), _ptr(ws), ws_bytes,
+                                         _stream(X.device)), "qlora_linear_fwd_dropout")
+    return Y
+
+
+def qlora_linear_bwd_dropout(W: NF4Weight, X, dY, keep, p: float, A, B, r: int, alpha: float, dX=None,
+                             dA=None, dB=None, ws=None):
+    """Backward of qlora_linear_fwd_dropout with the same mask ->
+    (dX [T, in] bf16, dA [r, in] fp32, dB [out, r] fp32)."""
+    T = X.shape[0]
+    _need(X, torch.bfloat16, "X", T * W.cols)
+    _need(dY, torch.bfloat16, "dY", T * W.rows)
+    _need(keep, torch.uint8, "keep", T * (W.cols // 8))
+    _need(A, torch.bfloat16, "A", r * W.cols)
+    _need(B, torch.bfloat16, "B", W.rows * r)
+    dev = X.device
+    if dX is None:
+        dX = torch.empty(T, W.cols, dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty(r, W.cols, dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty(W.rows, r, dtype=torch.float32, device=dev)
+    _need(dX, torch.bfloat16, "dX", T * W.cols)
+    _need(dA, torch.float32, "dA", r * W.cols)
+    _need(dB, torch.float32, "dB", W.rows * r)
+    ws, ws_bytes = _dropout_ws(ws, T, W.cols, W.rows, r, True, dev)
+    wc = W._c()
+    _check(_lib.qlora_linear_bwd_dropout(ctypes.byref(wc), _ptr(X), _ptr(dY), T, _ptr(keep), float(p),
+                                         _ptr(A), _ptr(B), r, float(alpha), _ptr(dX), _ptr(dA), _ptr(dB),
+                                         _ptr(ws), ws_bytes, _stream(dev)), "qlora_linear_bwd_dropout")
     return dX, dA, dB
 
 

@@ -68,15 +68,20 @@ struct DownFactors { const uint16_t* p[kMaxProj]; };
 // `part` is fp32 scratch of lora_down_part_bytes(T, K, nP * rp) bytes.
 // K % 64 == 0, rp % 64 == 0.
 size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t nprp);
+// keep (optional, LoRA dropout): in[t][k] counts only where bit k % 8 of
+// keep[t * ldk + k / 8] is set.
 hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t K,
                             const uint16_t* const* P, int nP, int64_t r, float scale, uint16_t* pad,
                             int64_t ldpad, uint16_t* hilo_t, int64_t ldt, int64_t rp, float* part,
-                            hipStream_t s);
+                            hipStream_t s, const uint8_t* keep = nullptr, int64_t ldk = 0);
 // out(j, c) += sum_t (Pt[j][t] + Pt[rp + j][t]) Q[t][c] for j < r, c < C (C % 64
 // == 0), atomically into out[j * C + c] (out_jc) or out[c * r + j].
-// (Q rows have stride ldq elements, ldq >= C)
+// (Q rows have stride ldq elements, ldq >= C).  keep (optional, LoRA dropout,
+// out_jc only): Q[t][c] counts only where bit c % 8 of keep[t * ldk + c / 8]
+// is set; every sum is multiplied by oscale.
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
-                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s);
+                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s,
+                            const uint8_t* keep = nullptr, int64_t ldk = 0, float oscale = 1.f);
 // dst[c][r] = src[r][c] for src [R][C]
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
                                  hipStream_t s);
@@ -90,10 +95,15 @@ hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
 // C[M][N] (bf16, ldc) = sum over the two K segments of act_i[m][k] * wt_i[n][k]
 // (bf16, K-contiguous, leading dims lda_i / ldw_i).  K0, K1 multiples of 64
 // (K1 may be 0).  N % 64 == 0.
+// keep (optional): LoRA dropout mask of C's elements, bit n % 8 of byte
+// keep[m * ldk + n / 8]; the extension segment's product is multiplied by
+// keep_scale where the bit is set and by 0 elsewhere before the main segment
+// is added, so C is still rounded once.
 hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
-                          int64_t ldc, hipStream_t s);
+                          int64_t ldc, hipStream_t s, const uint8_t* keep = nullptr, int64_t ldk = 0,
+                          float keep_scale = 1.f);
 
 // Same, with the main segment's weight given as NF4 projections stacked
 // along N (nproj <= kMaxProj; projection i owns output columns

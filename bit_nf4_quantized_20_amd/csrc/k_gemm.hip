@@ -246,7 +246,40 @@ struct GemmArgs {
   const uint16_t* wt1; int64_t ldw1;
   int64_t K1;
   uint16_t* C; int64_t ldc;
+  // LoRA dropout (null: none): the extension segment runs first and its
+  // product is multiplied element-wise by keep_scale * keep[m][n] before the
+  // main segment adds to the same accumulator (bit n % 8 of byte
+  // keep[m * ldk + n / 8])
+  const uint8_t* keep; int64_t ldk; float keep_scale;
 };
+
+// acc[a][c][e] holds C[m][n] with m = m_base + 32 c + r32 and
+// n = n_base + 32 a + 8 (e / 4) + 4 half + e % 4 (the layout of
+// v_mfma_f32_32x32x16_bf16 as these kernels use it).  Multiplies each
+// element by keep_scale where its keep bit is set, by 0 elsewhere.
+template <int FN, int FM>
+__device__ __forceinline__ void apply_keep(f32x16 (&acc)[FN][FM], const GemmArgs& p, int64_t m_base,
+                                           int64_t n_base, int r32, int half) {
+  const uint64_t kbytes = static_cast<uint64_t>(p.M) * p.ldk;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.keep), 0, static_cast<int>(kbytes < 0x7fffffffu ? kbytes : 0x7fffffffu),
+      0x00020000);
+#pragma unroll
+  for (int c = 0; c < FM; ++c) {
+    const int64_t m = m_base + 32 * c + r32;
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n_base + 32 * a + 8 * g;  // a multiple of 8: one byte
+        // rows past M and columns past N are never stored: read nothing for them
+        const uint32_t off = (m < p.M && n < p.N) ? static_cast<uint32_t>(m * p.ldk + n / 8) : 0x80000000u;
+        const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0) >> (4 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][c][4 * g + i] *= ((bits >> i) & 1u) ? p.keep_scale : 0.f;
+      }
+  }
+}
 
 // The projection holding output column n0 (uniform; constant indices only,
 // so the table stays in scalar registers).
@@ -347,49 +380,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   const int64_t s0 = p.K0 / kBK, s1 = p.K1 / kBK;
   using TA = Bf16Tile<BM, NT>;
   using TW = Bf16Tile<BN, NT>;
-  if constexpr (kNf4) {
-    using TQ = Nf4Tile<BN, NT>;
-    TA ta;
-    TQ tq;
-    ta.init(p.act0, p.lda0, m0, p.M, tid);
-    const Nf4Seg sg = seg_of(p, n0);
-    tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
-    struct R { typename TA::Regs a; typename TQ::Regs w; };
-    R r0, r1;
-    segment(r0, r1, 0, s0,
-            [&](R& r, int64_t e) {
-              ta.load(r.a, e * kBK);
-              tq.load(r.w, e * kBK);
-            },
-            [&](const R& r, int b) {
-              TA::store(r.a, s_act[b], tid);
-              TQ::store(r.w, s_wt[b], tid);
-            });
-  } else {
-    TA ta;
-    TW tw;
-    ta.init(p.act0, p.lda0, m0, p.M, tid);
-    tw.init(p.wt0, p.ldw0, n0, p.N, tid);
-    struct R { typename TA::Regs a; typename TW::Regs w; };
-    R r0, r1;
-    segment(r0, r1, 0, s0,
-            [&](R& r, int64_t e) {
-              ta.load(r.a, e * kBK);
-              tw.load(r.w, e * kBK);
-            },
-            [&](const R& r, int b) {
-              TA::store(r.a, s_act[b], tid);
-              TW::store(r.w, s_wt[b], tid);
-            });
-  }
-  if (s1 > 0) {  // LoRA extension segment
+  // main segment over global steps [first, first + s0)
+  auto main_seg = [&](int64_t first) {
+    if constexpr (kNf4) {
+      using TQ = Nf4Tile<BN, NT>;
+      TA ta;
+      TQ tq;
+      ta.init(p.act0, p.lda0, m0, p.M, tid);
+      const Nf4Seg sg = seg_of(p, n0);
+      tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
+      struct R { typename TA::Regs a; typename TQ::Regs w; };
+      R r0, r1;
+      segment(r0, r1, first, first + s0,
+              [&](R& r, int64_t e) {
+                ta.load(r.a, e * kBK);
+                tq.load(r.w, e * kBK);
+              },
+              [&](const R& r, int b) {
+                TA::store(r.a, s_act[b], tid);
+                TQ::store(r.w, s_wt[b], tid);
+              });
+    } else {
+      TA ta;
+      TW tw;
+      ta.init(p.act0, p.lda0, m0, p.M, tid);
+      tw.init(p.wt0, p.ldw0, n0, p.N, tid);
+      struct R { typename TA::Regs a; typename TW::Regs w; };
+      R r0, r1;
+      segment(r0, r1, first, first + s0,
+              [&](R& r, int64_t e) {
+                ta.load(r.a, e * kBK);
+                tw.load(r.w, e * kBK);
+              },
+              [&](const R& r, int b) {
+                TA::store(r.a, s_act[b], tid);
+                TW::store(r.w, s_wt[b], tid);
+              });
+    }
+  };
+  // LoRA extension segment over global steps [first, first + s1)
+  auto lora_seg = [&](int64_t first) {
+    if (s1 <= 0) return;
     TA ta;
     TW tw;
     ta.init(kNf4 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, tid);
     tw.init(p.wt1, p.ldw1, n0, p.N, tid);
     struct R { typename TA::Regs a; typename TW::Regs w; };
     R r0, r1;
-    segment(r0, r1, s0, s0 + s1,
+    segment(r0, r1, first, first + s1,
             [&](R& r, int64_t e) {
               ta.load(r.a, e * kBK);
               tw.load(r.w, e * kBK);
@@ -398,6 +436,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
               TA::store(r.a, s_act[b], tid);
               TW::store(r.w, s_wt[b], tid);
             });
+  };
+  if (p.keep != nullptr) {
+    // dropout: the adapter product alone, masked, then the base on top
+    lora_seg(0);
+    apply_keep<FN, FM>(acc, p, m0 + wm * WM, n0 + wn * WN, r32, half);
+    main_seg(s1);
+  } else {
+    main_seg(0);
+    lora_seg(s0);
   }
 
   // epilogue: D[n][m] -> C[m][n]; lane holds m = r32, n = 8*(e/4) + 4*half + e%4
@@ -569,21 +616,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   };
 
   const int64_t s0 = p.K0 / kBK, s1 = p.K1 / kBK;
-  DtlTile<BM, NW> ta;
-  ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
-  if constexpr (kNf4) {
-    Nf4Tile<BN, NT> tq;
-    const Nf4Seg sg = seg_of(p, n0);
-    tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
-    main_loop(ta, tq, s0);
-  } else {
-    DtlTile<BN, NW> tw;
-    tw.init(p.wt0, p.ldw0, n0, p.N, wv, lane);
-    main_loop(ta, tw, s0);
-  }
-
   // LoRA extension segment (a few steps): copy, barrier, compute
-  if (s1 > 0) {
+  auto lora_seg = [&]() {
+    if (s1 <= 0) return;
     DtlTile<BM, NW> ta1;
     DtlTile<BN, NW> tw1;
     ta1.init(kNf4 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, wv, lane);
@@ -601,7 +636,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
         mfmas(f);
       }
     }
+  };
+  if (p.keep != nullptr) {
+    // dropout: the adapter product alone, masked, then the base on top
+    lora_seg();
+    apply_keep<FN, FM>(acc, p, m0 + wm * WM, n0 + wn * WN, r32, half);
+    __syncthreads();  // every wave is done reading stage 0 before the main copies
   }
+  DtlTile<BM, NW> ta;
+  ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
+  if constexpr (kNf4) {
+    Nf4Tile<BN, NT> tq;
+    const Nf4Seg sg = seg_of(p, n0);
+    tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
+    main_loop(ta, tq, s0);
+  } else {
+    DtlTile<BN, NW> tw;
+    tw.init(p.wt0, p.ldw0, n0, p.N, wv, lane);
+    main_loop(ta, tw, s0);
+  }
+  if (p.keep == nullptr) lora_seg();
 
   // epilogue: D[n][m] -> C[m][n]; lane holds m = r32, n = 8*(e/4) + 4*half + e%4
 #pragma unroll
@@ -648,10 +702,12 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t lda0,
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
-                          int64_t ldc, hipStream_t s) {
+                          int64_t ldc, hipStream_t s, const uint8_t* keep, int64_t ldk,
+                          float keep_scale) {
   GemmArgs a{};
   a.M = M; a.N = N; a.act0 = act0; a.lda0 = lda0; a.wt0 = wt0; a.ldw0 = ldw0; a.nseg = 0; a.K0 = K0;
   a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1; a.C = C; a.ldc = ldc;
+  a.keep = keep; a.ldk = ldk; a.keep_scale = keep_scale;
   return launch_tiles<false>(a, s);
 }
 

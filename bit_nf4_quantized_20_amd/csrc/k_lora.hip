@@ -15,6 +15,19 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 namespace {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// LoRA dropout: eight bf16 (one 16-byte piece) with the eight keep bits of
+// byte b (bit e for element e); dropped elements become +0.
+__device__ __forceinline__ u32x4 keep_bf16x8(u32x4 v, uint32_t b) {
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t lo = ((b >> (2 * d)) & 1u) ? 0x0000ffffu : 0u;
+    const uint32_t hi = ((b >> (2 * d + 1)) & 1u) ? 0xffff0000u : 0u;
+    o[d] = v[d] & (lo | hi);
+  }
+  return o;
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -51,10 +64,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t down_rsrc(const uint16_t* base
 
 // part[kc][t][p rp + j] (fp32, [KC][T][nP rp]) = sum over chunk kc of
 // in[t][k] P_p[j][k], for the nP rank factors P_p (one per projection).
+// kMask: in[t][k] counts only where bit k % 8 of keep[t * ldk + k / 8] is set.
+template <bool kMask>
 __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restrict__ in, int64_t ldin,
                                                         int64_t T, int64_t K, DownFactors P,
                                                         int r, int rp, int64_t kch,
-                                                        float* __restrict__ part) {
+                                                        float* __restrict__ part,
+                                                        const uint8_t* __restrict__ keep, int64_t ldk) {
   __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kDownTok * 64];
   __shared__ __attribute__((aligned(16))) uint16_t s_p[2][kDownRanks * 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -85,11 +101,28 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
     poff[i] = static_cast<uint32_t>((row * K + q * 8) * 2);
   }
   u32x4 xv[4], pv[2];
+  uint32_t kb[4];
+  // keep bytes of this workgroup's token rows (rows past T read zero)
+  const uint64_t kbytes = kMask ? static_cast<uint64_t>(T > t0 ? T - t0 : 0) * ldk : 0;
+  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kMask ? keep + t0 * ldk : keep), 0,
+      static_cast<int>(kbytes < 0x7fffffffu ? kbytes : 0x7fffffffu), kDownBufWord3);
+  uint32_t koff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i, row = id >> 3, q = id & 7;
+    koff[i] = static_cast<uint32_t>(row * ldk + q);
+  }
   auto load = [&](int st) {
     const int so = static_cast<int>((kbeg + 64 * static_cast<int64_t>(st)) * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xoff[i], so, 0));
+    if constexpr (kMask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kb[i] = __builtin_amdgcn_raw_buffer_load_b8(rs_k, koff[i], static_cast<int>(so / 16), 0);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, poff[i], so, 0));
@@ -98,7 +131,9 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int id = tid + 256 * i, row = id >> 3, q = id & 7;
-      *reinterpret_cast<u32x4*>(&s_x[b][row * 64 + down_swz(row, q) * 8]) = xv[i];
+      u32x4 v = xv[i];
+      if constexpr (kMask) v = keep_bf16x8(v, kb[i]);
+      *reinterpret_cast<u32x4*>(&s_x[b][row * 64 + down_swz(row, q) * 8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -233,7 +268,7 @@ size_t lora_down_part_bytes(int64_t T, int64_t K, int64_t nprp) {
 hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t K,
                             const uint16_t* const* P, int nP, int64_t r, float scale, uint16_t* pad,
                             int64_t ldpad, uint16_t* hilo_t, int64_t ldt, int64_t rp, float* part,
-                            hipStream_t s) {
+                            hipStream_t s, const uint8_t* keep, int64_t ldk) {
   if (T <= 0) return hipSuccess;
   if (nP < 1 || nP > kMaxProj) return hipErrorInvalidValue;
   // 32-bit buffer offsets: one tile's rows of `in` and P stay under 2^31 bytes
@@ -245,8 +280,14 @@ hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t
   const int64_t KC = ceil_div(K, kch);
   const dim3 grid(static_cast<uint32_t>(ceil_div(T, kDownTok)), static_cast<uint32_t>(KC),
                   static_cast<uint32_t>(nP * rp / kDownRanks));
-  hipLaunchKernelGGL(k_lora_down_part, grid, dim3(256), 0, s, in, ldin, T, K, f, static_cast<int>(r),
-                     static_cast<int>(rp), kch, part);
+  if (keep != nullptr) {
+    if (kDownTok * ldk >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_lora_down_part<true>, grid, dim3(256), 0, s, in, ldin, T, K, f,
+                       static_cast<int>(r), static_cast<int>(rp), kch, part, keep, ldk);
+  } else {
+    hipLaunchKernelGGL(k_lora_down_part<false>, grid, dim3(256), 0, s, in, ldin, T, K, f,
+                       static_cast<int>(r), static_cast<int>(rp), kch, part, keep, ldk);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tt = hilo_t != nullptr ? (ldt > T ? ldt : T) : T;
@@ -285,11 +326,15 @@ __device__ __forceinline__ int grad_qslot(int c, int w) { return kGradPitch * c 
 
 // kJC: output out[j*C + c] (else out[c*r + j]).  The MFMA orientation
 // follows it, so a wave's 32 lanes always add to 32 consecutive floats.
-template <int JT, bool kJC>
+// kMask: Q[t][c] counts only where bit c % 8 of keep[t * ldk + c / 8] is set;
+// every output sum is multiplied by oscale.
+template <int JT, bool kJC, bool kMask>
 __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ Pt, int64_t T,
                                                    int64_t ldt, int rp, const uint16_t* __restrict__ Q,
                                                    int64_t C, int64_t ldq, int r, int j0,
-                                                   float* __restrict__ out, int64_t TS) {
+                                                   float* __restrict__ out, int64_t TS,
+                                                   const uint8_t* __restrict__ keep, int64_t ldk,
+                                                   float oscale) {
   constexpr int kPRows = 64 * JT;  // hi rows [0, 32JT), lo rows [32JT, 64JT)
   __shared__ uint32_t s_q[2][kGradCT * kGradPitch];
   __shared__ uint32_t s_p[2][kPRows * kGradPitch];
@@ -314,7 +359,12 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
   const int cg = tid & 15, tp0 = tid >> 4;
   const bool col_ok = c0 + 8 * cg < C;
   u32x4 qv[4];
+  uint32_t kb[4];
   u32x4 pv[2 * JT];
+  const uint64_t kbytes = kMask ? static_cast<uint64_t>(T - ts) * ldk : 0;
+  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kMask ? keep + ts * ldk : keep), 0,
+      static_cast<int>(kbytes < 0x7fffffffu ? kbytes : 0x7fffffffu), kBufferWord3);
   auto load = [&](int step) {
     const int64_t t0 = ts + 64 * static_cast<int64_t>(step);
 #pragma unroll
@@ -322,6 +372,10 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
       const int64_t t = t0 - ts + 2 * (tp0 + 16 * (i >> 1)) + (i & 1);  // rows past T read as zero
       const uint32_t off = col_ok ? static_cast<uint32_t>((t * ldq + c0 + 8 * cg) * 2) : kPastEnd;
       qv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_q, off, 0, 0));
+      if constexpr (kMask) {
+        const uint32_t koff = col_ok ? static_cast<uint32_t>(t * ldk + (c0 + 8 * cg) / 8) : kPastEnd;
+        kb[i] = __builtin_amdgcn_raw_buffer_load_b8(rs_k, koff, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2 * JT; ++i) {
@@ -333,6 +387,10 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
     }
   };
   auto store = [&](int buf) {
+    if constexpr (kMask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = keep_bf16x8(qv[i], kb[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const u32x4 a = qv[2 * i], b = qv[2 * i + 1];
@@ -396,7 +454,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = j0 + 32 * jt + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (j < r) atomicAdd(out + static_cast<int64_t>(j) * C + cc, acc[jt][e]);
+        if (j < r) atomicAdd(out + static_cast<int64_t>(j) * C + cc, acc[jt][e] * oscale);
       }
   } else {
     // D[c][j]: lane holds rank j, rows c = 8*(e/4) + 4*h + e%4 of the wave's tile
@@ -407,14 +465,15 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t cc = c0 + 32 * wv + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (cc < C) atomicAdd(out + cc * r + j, acc[jt][e]);
+        if (cc < C) atomicAdd(out + cc * r + j, acc[jt][e] * oscale);
       }
     }
   }
 }
 
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
-                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s) {
+                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s,
+                            const uint8_t* keep, int64_t ldk, float oscale) {
   if (T <= 0) return hipSuccess;
   // token slices (multiples of 64) for about 512 workgroups
   const int64_t ctiles = ceil_div(C, kGradCT);
@@ -426,6 +485,7 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
   const int64_t min_slices = ceil_div(T * ldq * 2, int64_t(1) << 30);
   if (slices < min_slices) slices = min_slices;
   if (2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (keep != nullptr && T * ldk >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int64_t TS = round_up(ceil_div(T, slices), 64);
   slices = ceil_div(T, TS);
   const dim3 grid(static_cast<uint32_t>(ctiles), static_cast<uint32_t>(slices));
@@ -434,16 +494,21 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
     const int64_t left = r - j0;
     const int jt = static_cast<int>(ceil_div(left < 32 * kGradMaxJT ? left : 32 * kGradMaxJT, 32));
     const int ij0 = static_cast<int>(j0);
-#define QLORA_GRAD(JTV, JC)                                                                          \
-  hipLaunchKernelGGL((k_lora_grad<JTV, JC>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ldq, ir, ij0, out, TS)
-    if (out_jc) {
-      if (jt <= 1) QLORA_GRAD(1, true);
-      else if (jt <= 2) QLORA_GRAD(2, true);
-      else QLORA_GRAD(4, true);
+#define QLORA_GRAD(JTV, JC, MK)                                                                      \
+  hipLaunchKernelGGL((k_lora_grad<JTV, JC, MK>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ldq, ir, ij0, \
+                     out, TS, keep, ldk, oscale)
+    if (keep != nullptr) {  // the masked operand is X: dA, out_jc
+      if (jt <= 1) QLORA_GRAD(1, true, true);
+      else if (jt <= 2) QLORA_GRAD(2, true, true);
+      else QLORA_GRAD(4, true, true);
+    } else if (out_jc) {
+      if (jt <= 1) QLORA_GRAD(1, true, false);
+      else if (jt <= 2) QLORA_GRAD(2, true, false);
+      else QLORA_GRAD(4, true, false);
     } else {
-      if (jt <= 1) QLORA_GRAD(1, false);
-      else if (jt <= 2) QLORA_GRAD(2, false);
-      else QLORA_GRAD(4, false);
+      if (jt <= 1) QLORA_GRAD(1, false, false);
+      else if (jt <= 2) QLORA_GRAD(2, false, false);
+      else QLORA_GRAD(4, false, false);
     }
 #undef QLORA_GRAD
     const hipError_t e = hipGetLastError();

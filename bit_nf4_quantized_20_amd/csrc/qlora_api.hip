@@ -81,10 +81,12 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
   return true;
 }
 
-FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
+// dropout: the small-token kernel has no mask, so that call always takes the
+// general path
+FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout) {
   FwdLayout l{0, 0, 0, 0, 0};
   Carve c;
-  if (fwd_uses_decode(T, in, outs, n, r)) return l;
+  if (!dropout && fwd_uses_decode(T, in, outs, n, r)) return l;
   const int64_t rp = padded_rank(r), N = total_out(outs, n);
   l.u_pad = c.take(static_cast<size_t>(T * n * rp * 4));  // [T][n 2rp] bf16
   l.b_pad = c.take(static_cast<size_t>(N * n * rp * 4));  // [N][2rp] or [N][n 2rp] bf16
@@ -205,7 +207,15 @@ size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t
   for (int i = 0; i < n; ++i)
     if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
   const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r).total
-                               : fwd_layout(T, in_features, out_features, n, r).total;
+                               : fwd_layout(T, in_features, out_features, n, r, false).total;
+  return need > kMinWorkspace ? need : kMinWorkspace;
+}
+
+size_t qlora_workspace_bytes_dropout(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
+                                     int backward) {
+  if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;
+  const size_t need = backward ? bwd_layout(T, in_features, &out_features, 1, r).total
+                               : fwd_layout(T, in_features, &out_features, 1, r, true).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
 
@@ -229,6 +239,13 @@ int check_projections(const qlora_nf4_weight* W, int n, int64_t T, int64_t r, in
   return QLORA_OK;
 }
 
+// LoRA dropout arguments: no mask means no dropout; with a mask, 0 <= p < 1
+int check_dropout(const uint8_t* keep, float p) {
+  if (keep == nullptr) return QLORA_OK;
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return QLORA_ERR_VALUE;
+  return QLORA_OK;
+}
+
 int check_factors(const qlora_bf16* const* A, const qlora_bf16* const* B, int n) {
   if (A == nullptr || B == nullptr) return QLORA_ERR_NULL;
   for (int i = 0; i < n; ++i) {
@@ -238,17 +255,22 @@ int check_factors(const qlora_bf16* const* A, const qlora_bf16* const* B, int n)
   return QLORA_OK;
 }
 
+// keep / p: LoRA dropout (keep == nullptr: none; n == 1 only), see
+// qlora_linear_fwd_dropout
 int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64_t T,
                     const qlora_bf16* const* A, const qlora_bf16* const* B, int64_t r, float alpha,
-                    qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream) {
+                    qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream,
+                    const uint8_t* keep = nullptr, float p = 0.f) {
   int64_t outs[kMaxProj], in = 0;
   if (int st = check_projections(W, n, T, r, outs, &in)) return st;
   if (int st = check_factors(A, B, n)) return st;
   if (T > 0 && (!X || !Y)) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(Y)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
+  const bool dropout = keep != nullptr;
+  if (int st = check_dropout(keep, p)) return st;
   if (T == 0) return QLORA_OK;
-  const FwdLayout lay = fwd_layout(T, in, outs, n, r);
+  const FwdLayout lay = fwd_layout(T, in, outs, n, r, dropout);
   if (lay.total > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
@@ -256,7 +278,7 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = alpha / static_cast<float>(r);
   const int64_t N = total_out(outs, n);
-  if (fwd_uses_decode(T, in, outs, n, r)) {
+  if (!dropout && fwd_uses_decode(T, in, outs, n, r)) {
     int64_t off = 0;
     for (int i = 0; i < n; ++i) {
       const hipError_t e = launch_decode_fwd(W[i].codes, W[i].absmax_q, W[i].absmax_scale, in, outs[i],
@@ -272,8 +294,11 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   uint16_t* u_pad = reinterpret_cast<uint16_t*>(base + lay.u_pad);
   uint16_t* b_pad = reinterpret_cast<uint16_t*>(base + lay.b_pad);
   float* part = reinterpret_cast<float*>(base + lay.part);
-  // s X A_i^T for every projection in one pass over X: [T][n 2rp]
-  hipError_t e = launch_lora_down(X, in, T, in, A, n, r, scale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s);
+  // s X A_i^T for every projection in one pass over X: [T][n 2rp]; with
+  // dropout s / (1 - p) (keep o X) A^T
+  const float uscale = dropout ? scale / (1.f - p) : scale;
+  hipError_t e = launch_lora_down(X, in, T, in, A, n, r, uscale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s,
+                                  keep, in / 8);
   if (T >= kMaterializeTokens) {
     // W_hat of every projection into [N][in] bf16, then the bf16 GEMM; the
     // LoRA term as extra K-steps over [sU_0 | sU_1 | ...] against B_i placed
@@ -308,7 +333,8 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
 int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const qlora_bf16* dY,
                     int64_t T, const qlora_bf16* const* A, const qlora_bf16* const* B, int64_t r,
                     float alpha, qlora_bf16* dX, float* const* dA, float* const* dB, void* ws,
-                    size_t ws_bytes, qlora_stream stream) {
+                    size_t ws_bytes, qlora_stream stream, const uint8_t* keep = nullptr,
+                    float p = 0.f) {
   int64_t outs[kMaxProj], in = 0;
   if (int st = check_projections(W, n, T, r, outs, &in)) return st;
   if (int st = check_factors(A, B, n)) return st;
@@ -320,6 +346,7 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   if (T > 0 && (!X || !dY || !dX)) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
+  if (int st = check_dropout(keep, p)) return st;
   const BwdLayout lay = bwd_layout(T, in, outs, n, r);
   if (T > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
@@ -344,8 +371,11 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   uint16_t* w_dq_t = reinterpret_cast<uint16_t*>(base + lay.w_dq_t);
   float* part = reinterpret_cast<float*>(base + lay.part);
 
-  // (sU_i)^T for every projection in one pass over X
-  e = launch_lora_down(X, in, T, in, A, n, r, scale, nullptr, 0, ut, tp, rp, part, s);
+  // (sU_i)^T for every projection in one pass over X (with dropout the
+  // masked input: s / (1 - p) (keep o X) A^T, which dB then uses as is)
+  const float inv_keep = keep != nullptr ? 1.f / (1.f - p) : 1.f;
+  e = launch_lora_down(X, in, T, in, A, n, r, scale * inv_keep, nullptr, 0, ut, tp, rp, part, s, keep,
+                       in / 8);
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     // s V_i = s dY_i B_i with dY_i the projection's columns of dY
@@ -361,12 +391,15 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     off += outs[i];
   }
   // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
+  // (with dropout the adapter term is masked and scaled by 1 / (1 - p)
+  // before the base is added)
   if (e == hipSuccess)
     e = launch_gemm_nt(T, in, dY, N, w_dq_t, N, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp,
-                       dX, in, s);
+                       dX, in, s, keep, in / 8, inv_keep);
   off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
-    e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, dA[i], true, s);  // dA_i
+    e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, dA[i], true, s, keep, in / 8,
+                         inv_keep);  // dA_i
     if (e == hipSuccess)
       e = launch_lora_grad(ut + i * 2 * rp * tp, T, tp, rp, dY + off, outs[i], N, r, dB[i], false, s);
     off += outs[i];
@@ -404,6 +437,26 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
                            float* const* dA, float* const* dB, void* ws, size_t ws_bytes,
                            qlora_stream stream) {
   return linear_bwd_impl(W, n, X, dY, T, A, B, r, alpha, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
+                             const uint8_t* keep, float p, const qlora_bf16* A, const qlora_bf16* B,
+                             int64_t r, float alpha, qlora_bf16* Y, void* ws, size_t ws_bytes,
+                             qlora_stream stream) {
+  if (T > 0 && keep == nullptr) return QLORA_ERR_NULL;
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return QLORA_ERR_VALUE;
+  if (T == 0) keep = nullptr;
+  return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, ws, ws_bytes, stream, keep, p);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora_bf16* dY,
+                             int64_t T, const uint8_t* keep, float p, const qlora_bf16* A,
+                             const qlora_bf16* B, int64_t r, float alpha, qlora_bf16* dX, float* dA,
+                             float* dB, void* ws, size_t ws_bytes, qlora_stream stream) {
+  if (T > 0 && keep == nullptr) return QLORA_ERR_NULL;
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return QLORA_ERR_VALUE;
+  if (T == 0) keep = nullptr;
+  return linear_bwd_impl(W, 1, X, dY, T, &A, &B, r, alpha, dX, &dA, &dB, ws, ws_bytes, stream, keep, p);
 }
 
 size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, int64_t r) {

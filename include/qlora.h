@@ -221,6 +221,38 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora
                      qlora_stream stream);
 
 /*
+ * LoRA dropout (training).  coddykit "LoRA y QLoRA" configures the adapter
+ * with lora_dropout = 0.05; reading taken here (as in the PEFT layer the page
+ * configures): dropout acts on the adapter's input only,
+ *   X~ = keep o X / (1 - p),   Y = X W_hat^T + s (X~ A^T) B^T,
+ * and the backward of that forward:
+ *   dX = dY W_hat + (keep / (1 - p)) o (s (dY B) A)   (one bf16 rounding)
+ *   dA = s (dY B)^T X~,   dB = s dY^T (X~ A^T).
+ * The mask is drawn by the caller and passed in (the library has no random
+ * number generator): keep [T, in / 8] bytes, row-major, bit k % 8 of byte
+ * keep[t * in/8 + k / 8] set = element (t, k) kept; any alignment.  The
+ * forward and backward of one step must get the same mask.  0 <= p < 1
+ * (p = 0 with every bit set equals the plain linear up to summation order).
+ * Single projection only.  These calls always take the general (workspace)
+ * path, also for T <= 16:
+ *   ws of ws_bytes >= qlora_workspace_bytes_dropout(T, in, out, r, backward)
+ * (0 for invalid shapes, at least 256 otherwise; host only).
+ * T == 0: the forward does nothing, the backward writes zeros to dA and dB.
+ * Errors: NULL (keep NULL with T > 0, or as the plain calls), VALUE (p not in
+ * [0, 1) or alpha not finite), SHAPE, ALIGN, WORKSPACE, DEVICE, LAUNCH.
+ */
+size_t qlora_workspace_bytes_dropout(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
+                                     int backward);
+int qlora_linear_fwd_dropout(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
+                             const uint8_t* keep, float p, const qlora_bf16* A, const qlora_bf16* B,
+                             int64_t r, float alpha, qlora_bf16* Y, void* ws, size_t ws_bytes,
+                             qlora_stream stream);
+int qlora_linear_bwd_dropout(const qlora_nf4_weight* W, const qlora_bf16* X, const qlora_bf16* dY,
+                             int64_t T, const uint8_t* keep, float p, const qlora_bf16* A,
+                             const qlora_bf16* B, int64_t r, float alpha, qlora_bf16* dX, float* dA,
+                             float* dB, void* ws, size_t ws_bytes, qlora_stream stream);
+
+/*
  * Workspace bytes needed by qlora_merge: 0 for invalid shapes, at least 256
  * otherwise.  Host only.  Scratch only; needs no initialisation.
  */

@@ -71,6 +71,46 @@ def merge(W_hat, A, B, alpha: float, r: int) -> np.ndarray:
     return widen(W_hat) + s * (widen(B) @ widen(A))
 
 
+def unpack_keep(keep_bytes, T: int, n_in: int) -> np.ndarray:
+    """The dropout keep mask as a bool [T, in] array from its packed form:
+    bytes [T, in/8], bit k % 8 of byte k / 8 of row t set = element (t, k)
+    kept (the layout the library's dropout calls take)."""
+    b = np.asarray(keep_bytes, dtype=np.uint8).reshape(T, n_in // 8)
+    bits = (b[:, :, None] >> np.arange(8, dtype=np.uint8)[None, None, :]) & 1
+    return bits.reshape(T, n_in).astype(bool)
+
+
+def dropped_input(X, keep, p: float) -> np.ndarray:
+    """X~ = keep o X / (1 - p): the adapter's input under LoRA dropout
+    (coddykit "LoRA y QLoRA" configures lora_dropout = 0.05; reading: inverted
+    dropout on the adapter input only, the base sees X)."""
+    return np.where(keep, widen(X), 0.0) / (1.0 - float(p))
+
+
+def linear_fwd_dropout(W_hat, X, A, B, alpha: float, r: int, keep, p: float) -> np.ndarray:
+    """Y = X W_hat^T + (alpha/r) (X~ A^T) B^T, fp64, X~ as in dropped_input."""
+    s = float(alpha) / float(r)
+    Xd, Wd, Ad, Bd = widen(X), widen(W_hat), widen(A), widen(B)
+    Xt = dropped_input(X, keep, p)
+    return Xd @ Wd.T + s * ((Xt @ Ad.T) @ Bd.T)
+
+
+def linear_bwd_dropout(W_hat, X, dY, A, B, alpha: float, r: int, keep, p: float):
+    """(dX, dA, dB) in fp64 for linear_fwd_dropout with the mask held fixed
+    (the chain rule through X~ = keep o X / (1 - p)):
+        V  = dY B
+        dX = dY W_hat + (keep / (1 - p)) o (s V A)
+        dA = s V^T X~,   dB = s dY^T (X~ A^T)"""
+    s = float(alpha) / float(r)
+    Xd, Wd, Ad, Bd, Gd = widen(X), widen(W_hat), widen(A), widen(B), widen(dY)
+    Xt = dropped_input(X, keep, p)
+    V = Gd @ Bd
+    dX = Gd @ Wd + np.where(keep, s * (V @ Ad), 0.0) / (1.0 - float(p))
+    dA = s * (V.T @ Xt)
+    dB = s * (Gd.T @ (Xt @ Ad.T))
+    return dX, dA, dB
+
+
 def rel_frobenius(got, ref) -> float:
     """||got - ref||_F / ||ref||_F in fp64 (the acceptance measure)."""
     g = np.asarray(got, dtype=np.float64)

@@ -13,6 +13,9 @@ draws standard_normal in fp32, scaled by the standard deviation:
     W ~ N(0, 0.02)       (the pages' law for pretrained weights)
     X, dY ~ N(0, 1)
     A ~ N(0, 1/in)       B ~ N(0, 0.01)
+LoRA dropout keep masks (tensor id 5): element (t, k) kept when a uniform
+draw in [0, 1) is >= p, packed 8 elements per byte, element k in bit k % 8
+of byte k / 8 of its row.
 """
 
 from dataclasses import dataclass
@@ -22,7 +25,7 @@ import torch
 
 W_STD = 0.02
 B_STD = 0.01
-TENSOR_ID = {"W": 0, "X": 1, "A": 2, "B": 3, "dY": 4}
+TENSOR_ID = {"W": 0, "X": 1, "A": 2, "B": 3, "dY": 4, "keep": 5}
 
 
 def seed_for(workload: int, projection: int, tensor: str) -> int:
@@ -95,3 +98,11 @@ def lora_A(workload: int, projection: int, r: int, in_f: int) -> np.ndarray:
 
 def lora_B(workload: int, projection: int, out_f: int, r: int) -> np.ndarray:
     return bf16_bits(normal_f32(seed_for(workload, projection, "B"), (out_f, r), B_STD))
+
+
+def keep_mask(seed: int, T: int, in_f: int, p: float) -> np.ndarray:
+    """Dropout keep mask [T, in/8] uint8 (bit k % 8 of byte k / 8 = element k
+    kept), each element kept with probability 1 - p."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kept = rng.random((T, in_f)) >= p
+    return np.packbits(kept, axis=1, bitorder="little")

@@ -262,6 +262,44 @@ def test_merge_validation():
     assert call(ws=None) == -4 and call(wsb=ws - 1) == -4
 
 
+def test_dropout_validation():
+    lib = _lib()
+    i64, sz, vp, f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    lib.qlora_workspace_bytes_dropout.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes_dropout.restype = sz
+    lib.qlora_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes.restype = sz
+    lib.qlora_linear_fwd_dropout.argtypes = [ctypes.POINTER(_W), vp, i64, vp, f32, vp, vp, i64, f32, vp,
+                                             vp, sz, vp]
+    lib.qlora_linear_fwd_dropout.restype = ctypes.c_int
+    lib.qlora_linear_bwd_dropout.argtypes = [ctypes.POINTER(_W), vp, vp, i64, vp, f32, vp, vp, i64, f32,
+                                             vp, vp, vp, vp, sz, vp]
+    lib.qlora_linear_bwd_dropout.restype = ctypes.c_int
+    # the dropout forward always takes the general path: at T <= 16 it needs
+    # the workspace the plain small-token forward does without
+    assert lib.qlora_workspace_bytes(16, 4096, 4096, 16, 0) == 256
+    assert lib.qlora_workspace_bytes_dropout(16, 4096, 4096, 16, 0) > 256
+    assert lib.qlora_workspace_bytes_dropout(64, 4096, 4096, 16, 1) == lib.qlora_workspace_bytes(64, 4096, 4096, 16, 1)
+    assert lib.qlora_workspace_bytes_dropout(16, 100, 4096, 16, 0) == 0
+    F = _FAKE
+    W = _W(F, F, F, 128, 256)
+    ws = lib.qlora_workspace_bytes_dropout(32, 256, 128, 8, 0)
+    fwd = lambda **k: lib.qlora_linear_fwd_dropout(ctypes.byref(W), F, k.get("T", 32), k.get("keep", F),
+                                                   k.get("p", 0.05), F, F, 8, 16.0, F, F,
+                                                   k.get("wsb", ws), None)
+    assert fwd(keep=None) == -1
+    assert fwd(p=1.0) == -7 and fwd(p=-0.1) == -7 and fwd(p=float("nan")) == -7
+    assert fwd(wsb=ws - 1) == -4
+    assert fwd(T=0, keep=None) == 0
+    wsb = lib.qlora_workspace_bytes_dropout(32, 256, 128, 8, 1)
+    bwd = lambda **k: lib.qlora_linear_bwd_dropout(ctypes.byref(W), F, F, 32, k.get("keep", F),
+                                                   k.get("p", 0.05), F, F, 8, 16.0, F, F, F, F,
+                                                   k.get("wsb", wsb), None)
+    assert bwd(keep=None) == -1
+    assert bwd(p=1.5) == -7
+    assert bwd(wsb=wsb - 1) == -4
+
+
 def test_valid_call_without_gpu_reports_device_error():
     # with no HIP device the first HIP call fails and the call returns
     # ERR_DEVICE without launching anything (pointers are never touched)
