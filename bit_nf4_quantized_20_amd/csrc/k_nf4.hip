@@ -125,7 +125,10 @@ hipError_t launch_nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* code
 
 // ---------------------------------------------------------------------------
 // Dequantize: each thread expands 32 weights (16 code bytes, half a block)
-// into 64 bytes of bf16 with the per-block v_perm table.
+// into 64 bytes of bf16 with the per-block v_perm table.  The results go
+// through a per-wave LDS buffer so that each store instruction writes 1 KB
+// of consecutive output (a lane's own 64 bytes written directly would put
+// 64 separate 16-byte pieces into every store instruction).
 // ---------------------------------------------------------------------------
 // kDQ = false: a_hat is the fp32 block absmax (absmax[blk]) itself.
 template <bool kDQ>
@@ -134,18 +137,36 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
                                                         const float* __restrict__ scale,
                                                         const float* __restrict__ absmax,
                                                         int64_t numel, uint16_t* __restrict__ out) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 32-weight chunk
-  if (c * 32 >= numel) return;
-  const int64_t blk = c >> 1;
-  const float ahat = kDQ ? dq_absmax(absmax_q[blk], scale[blk >> 8]) : absmax[blk];
-  const Nf4Table tab = make_table(ahat);
-  const u32x4 cw = *reinterpret_cast<const u32x4*>(codes + c * 16);
-  u32x4* dst = reinterpret_cast<u32x4*>(out + c * 32);
+  __shared__ u32x4 s_o[4][64 * 5];  // lane l's four pieces at 5 l .. 5 l + 3 (conflict-free)
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nch = numel / 32;  // 32-weight chunks
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  u32x4* so = s_o[wv];
+  if (c < nch) {
+    const int64_t blk = c >> 1;
+    const float ahat = kDQ ? dq_absmax(absmax_q[blk], scale[blk >> 8]) : absmax[blk];
+    const Nf4Table tab = make_table(ahat);
+    const u32x4 cw = *reinterpret_cast<const u32x4*>(codes + c * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t o[4];
+      lookup8(tab, cw[k], o);
+      so[lane * 5 + k] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+  // the buffer is private to this wave: a wave-level barrier orders the
+  // writes of all lanes before the reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // the wave's 64 chunks are 4 KB of consecutive output: piece P (16 B) is
+  // piece P % 4 of chunk P / 4
+  const int64_t cw0 = static_cast<int64_t>(blockIdx.x) * 256 + wv * 64;
+  u32x4* dst = reinterpret_cast<u32x4*>(out + cw0 * 32);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint32_t o[4];
-    lookup8(tab, cw[k], o);
-    dst[k] = u32x4{o[0], o[1], o[2], o[3]};
+    const int P = 64 * k + lane, sl = P >> 2;
+    if (cw0 + sl < nch) dst[P] = so[sl * 5 + (P & 3)];
   }
 }
 
@@ -166,32 +187,33 @@ hipError_t launch_nf4_dequantize_nodq(const uint8_t* codes, const float* absmax,
 }
 
 // ---------------------------------------------------------------------------
-// Transposed dequantize: out[c][r] = W_hat[r][c].  One wave per 64x64 tile:
-// lane = tile row, which is exactly one block; the tile goes through LDS and
-// each lane then writes one output row segment of 64 bf16 (128 B).
+// Transposed dequantize (the backward's W_hat^T): one wave per 64 x 64 tile.
+// Lane l dequantizes the tile's part of weight row r0 + l (one block) into an
+// LDS tile, piece p (8 columns, 16 B) of row r at slot 8 r + (p ^ key(r)),
+// key(r) = (r ^ (r >> 3)) & 7, which keeps both the row writes and the
+// transposed 16-bit reads free of bank conflicts.  Then eight lanes write one
+// output row: lane l takes output row (l >> 3) + 8 i and its elements
+// 8 (l & 7) .. + 7, so each store instruction writes eight full 128-byte
+// row segments.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ absmax_q,
                                                           const float* __restrict__ scale,
                                                           int64_t rows, int64_t cols,
                                                           uint16_t* __restrict__ out, int64_t ldo) {
-  constexpr int kPitch = 64 + 2;  // bf16 elements per LDS row (odd dword pitch)
-  __shared__ uint16_t tile[4][64 * kPitch];
-  const int wv = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  __shared__ u32x4 tile[4][64 * 8];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t col_blocks = cols / 64;
   const int64_t tile_id = static_cast<int64_t>(blockIdx.x) * 4 + wv;
   const int64_t n_tiles = (rows / 64) * col_blocks;
   if (tile_id >= n_tiles) return;  // whole wave leaves; no workgroup barrier below
-  const int64_t r0 = (tile_id / col_blocks) * 64;
-  const int64_t c0 = (tile_id % col_blocks) * 64;
-  uint16_t* tl = tile[wv];
-
+  const int64_t r0 = (tile_id / col_blocks) * 64, c0 = (tile_id % col_blocks) * 64;
+  u32x4* tl = tile[wv];
   const int64_t row = r0 + lane;
   const int64_t blk = (row * cols + c0) >> 6;
-  const float ahat = dq_absmax(absmax_q[blk], scale[blk >> 8]);
-  const Nf4Table tab = make_table(ahat);
+  const Nf4Table tab = make_table(dq_absmax(absmax_q[blk], scale[blk >> 8]));
   const u32x4* src = reinterpret_cast<const u32x4*>(codes + ((row * cols + c0) >> 1));
+  const int key = (lane ^ (lane >> 3)) & 7;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const u32x4 cw = src[h];
@@ -199,12 +221,7 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
     for (int k = 0; k < 4; ++k) {
       uint32_t o[4];
       lookup8(tab, cw[k], o);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int col = h * 32 + k * 8 + p * 2;
-        tl[lane * kPitch + col] = static_cast<uint16_t>(o[p] & 0xffffu);
-        tl[lane * kPitch + col + 1] = static_cast<uint16_t>(o[p] >> 16);
-      }
+      tl[lane * 8 + ((4 * h + k) ^ key)] = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
   // the tile is private to this wave: a wave-level barrier orders the LDS
@@ -212,18 +229,21 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // lane now owns output row (c0 + lane), elements r0 .. r0+63
-  u32x4* dst = reinterpret_cast<u32x4*>(out + (c0 + lane) * ldo + r0);
+  const uint16_t* t16 = reinterpret_cast<const uint16_t*>(tl);
+  const int pr = lane & 7, cl = lane >> 3;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int i = 0; i < 8; ++i) {
+    const int cc = cl + 8 * i;  // output row c0 + cc = weight column; its piece i of the tile row
     uint32_t d[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = q * 8 + p * 2;
-      d[p] = static_cast<uint32_t>(tl[r * kPitch + lane]) |
-             (static_cast<uint32_t>(tl[(r + 1) * kPitch + lane]) << 16);
+    for (int e = 0; e < 4; ++e) {
+      const int ra = 8 * pr + 2 * e, rb = ra + 1;
+      const int ka = (ra ^ (ra >> 3)) & 7, kb = (rb ^ (rb >> 3)) & 7;
+      const uint32_t va = t16[(ra * 8 + (i ^ ka)) * 8 + cl];
+      const uint32_t vb = t16[(rb * 8 + (i ^ kb)) * 8 + cl];
+      d[e] = va | (vb << 16);
     }
-    dst[q] = u32x4{d[0], d[1], d[2], d[3]};
+    *reinterpret_cast<u32x4*>(out + (c0 + cc) * ldo + r0 + 8 * pr) = u32x4{d[0], d[1], d[2], d[3]};
   }
 }
 
