@@ -12,7 +12,8 @@
 // L2-resident) and park it, scaled, in LDS; then each thread owns one
 // 64-weight block of the tile: it loads the block's 32 code bytes and
 // absmax, expands them with the block's v_perm table (bit-identical to
-// nf4_dequantize), adds the rank-r term and writes 128 contiguous bytes.
+// nf4_dequantize) and adds the rank-r term; the tile then leaves through LDS
+// in whole row segments.
 // Bound by the HBM stream (0.5 B read + 2 B written per weight).
 #include "common.hpp"
 #include "nf4_format.hpp"
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
                                                const uint16_t* __restrict__ Bp,
                                                const uint16_t* __restrict__ Atp, int64_t ldp, int rp,
                                                float s, uint16_t* __restrict__ out) {
-  __shared__ float s_c[kMRows * kMPitch];
+  __shared__ __attribute__((aligned(16))) float s_c[kMRows * kMPitch];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r32 = lane & 31, half = lane >> 5;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kMCols;
@@ -82,28 +83,47 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
   // thread -> row m0 + tid / 4, block (n0 + 64 (tid % 4)) of 64 weights
   const int ml = tid >> 2, nl = 64 * (tid & 3);
   const int64_t col = n0 + nl;
-  if (col >= in) return;
-  const int64_t e0 = (m0 + ml) * in + col;  // first element of the block
-  const int64_t blk = e0 >> 6;
-  const Nf4Table tab = make_table(dq_absmax(absmax_q[blk], scale[blk >> 8]));
-  const u32x4* src = reinterpret_cast<const u32x4*>(codes + (e0 >> 1));
-  u32x4* dst = reinterpret_cast<u32x4*>(out + e0);
-  const float* lr = s_c + ml * kMPitch + nl;
+  const bool live = col < in;
+  u32x4 ov[8];
+  if (live) {
+    const int64_t e0 = (m0 + ml) * in + col;  // first element of the block
+    const int64_t blk = e0 >> 6;
+    const Nf4Table tab = make_table(dq_absmax(absmax_q[blk], scale[blk >> 8]));
+    const u32x4* src = reinterpret_cast<const u32x4*>(codes + (e0 >> 1));
+    const float* lr = s_c + ml * kMPitch + nl;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const u32x4 cw = src[h];
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 cw = src[h];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t w[4];
-      lookup8(tab, cw[k], w);
-      uint32_t o[4];
+      for (int k = 0; k < 4; ++k) {
+        uint32_t w[4];
+        lookup8(tab, cw[k], w);
+        uint32_t o[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int j = 32 * h + 8 * k + 2 * p;
-        o[p] = pack_bf16x2(bf16_lo(w[p]) + lr[j], bf16_hi(w[p]) + lr[j + 1]);
+        for (int p = 0; p < 4; ++p) {
+          const int j = 32 * h + 8 * k + 2 * p;
+          o[p] = pack_bf16x2(bf16_lo(w[p]) + lr[j], bf16_hi(w[p]) + lr[j + 1]);
+        }
+        ov[4 * h + k] = u32x4{o[0], o[1], o[2], o[3]};
       }
-      dst[4 * h + k] = u32x4{o[0], o[1], o[2], o[3]};
     }
+  }
+  // The results go out through LDS (reusing s_c, 33 pieces of 16 B per row)
+  // so that each store instruction writes whole 512-byte row segments; a
+  // thread's own 128 bytes written directly would put 64 separate 16-byte
+  // pieces into every store instruction.
+  __syncthreads();  // every thread is done reading s_c
+  u32x4* s_o = reinterpret_cast<u32x4*>(s_c);
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_o[ml * 33 + (nl >> 3) + j] = ov[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int P = 256 * i + tid, rl = P >> 5, pc = P & 31;
+    const int64_t cp = n0 + 8 * pc;
+    if (cp < in) *reinterpret_cast<u32x4*>(out + (m0 + rl) * in + cp) = s_o[rl * 33 + pc];
   }
 }
 
