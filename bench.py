@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--counters-probe", action="store_true",
                     help="only run the T=16 small-token forward over the weight pool and a "
                          "256 MiB copy (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
+    ap.add_argument("--mlp-probe", action="store_true",
+                    help="only run the 8B-MLP fwd + bwd leg and print its figures (for rocprofv3 "
+                         "--pmc passes over the large-token GEMMs)")
     return ap.parse_args()
 
 
@@ -133,6 +136,10 @@ def main():
 
     if args.counters_probe:
         counters_probe(q, pool, X16, Y16, A, B, r, alpha, ws, dev)
+        return
+    if args.mlp_probe:
+        del pool
+        print(json.dumps(train_leg(q, synth, dev, bf)), flush=True)
         return
 
     b1 = decode_call_bytes(n_out, n_in, 1, r)
