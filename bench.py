@@ -476,6 +476,24 @@ def train_leg(q, synth, dev, bf):
     res["mlp_fused_fwd_bwd_ms"] = round(fused_ms, 3)
     res["mlp_fused_fwd_bwd_TFLOPs"] = round(tf2, 1)
     res["mlp_fused_frac_of_bf16_peak"] = round(tf2 / BF16_PEAK_TFLOPS, 4)
+
+    # below 2048 tokens the forward keeps the dequantization inside the GEMM's
+    # LDS staging (W_hat never written): gate and up at T = 1792 (7 x 112 tiles)
+    Tf = 1792
+    Xf = X[:Tf].contiguous()
+    Yf = torch.empty(Tf, N, dtype=torch.bfloat16, device=dev)
+    wsff = q.make_workspace(q.qlora_workspace_bytes_multi(Tf, n_in, outs, r, False), dev)
+
+    def fwdf():
+        q.qlora_linear_fwd_multi(Ws, Xf, As, Bs, r, alpha, Y=Yf, ws=wsff)
+
+    for _ in range(8):
+        fwdf()
+    ms_ff = timed(fwdf, 20)
+    flop_ff = 2 * Tf * n_in * N + 2 * Tf * r * (2 * n_in + N)
+    tff = flop_ff / (ms_ff * 1e-3) / 1e12
+    res["gate_up_fused_nf4_fwd_T1792"] = {"fwd_ms": round(ms_ff, 3), "fwd_TFLOPs": round(tff, 1),
+                                          "frac_of_bf16_peak": round(tff / BF16_PEAK_TFLOPS, 4)}
     return res
 
 
