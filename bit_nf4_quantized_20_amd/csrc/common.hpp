@@ -115,6 +115,15 @@ struct Nf4Proj {
   int64_t rows;
   const uint16_t* act1;
 };
+// bf16 weight of nproj stacked projections (rows[i] rows each, N = sum) whose
+// LoRA extension reads projection i's own activation block act1[i] for the
+// output columns of projection i (K1 = 2 rp, wt1 the stacked [N][2 rp] factor).
+// Needs every tile inside one projection: gemm_proj_aligned(M, nproj, rows).
+bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows);
+hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const uint16_t* const* act1,
+                               const uint16_t* act0, int64_t lda0, const uint16_t* wt0, int64_t ldw0,
+                               int64_t K0, int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1,
+                               uint16_t* C, int64_t ldc, hipStream_t s);
 hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,
                            int64_t lda0, int64_t K0, int64_t lda1, const uint16_t* wt1,
                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);

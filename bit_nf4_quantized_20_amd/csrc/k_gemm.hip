@@ -241,7 +241,7 @@ struct GemmArgs {
   int nseg;
   Nf4Seg seg[kMaxProj];
   int64_t K0;
-  // LoRA extension segment (with NF4 projections, act1 comes from seg[])
+  // LoRA extension segment (with nseg > 0, act1 comes from the tile's seg[])
   const uint16_t* act1; int64_t lda1;
   const uint16_t* wt1; int64_t ldw1;
   int64_t K1;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
     if (s1 <= 0) return;
     TA ta;
     TW tw;
-    ta.init(kNf4 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, tid);
+    ta.init(p.nseg > 0 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, tid);
     tw.init(p.wt1, p.ldw1, n0, p.N, tid);
     struct R { typename TA::Regs a; typename TW::Regs w; };
     R r0, r1;
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
     if (s1 <= 0) return;
     DtlTile<BM, NW> ta1;
     DtlTile<BN, NW> tw1;
-    ta1.init(kNf4 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, wv, lane);
+    ta1.init(p.nseg > 0 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, wv, lane);
     tw1.init(p.wt1, p.ldw1, n0, p.N, wv, lane);
     for (int64_t e = 0; e < s1; ++e) {
       __syncthreads();  // every wave is done reading stage 0
@@ -709,6 +709,38 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
   a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1; a.C = C; a.ldc = ldc;
   a.keep = keep; a.ldk = ldk; a.keep_scale = keep_scale;
   return launch_tiles<false>(a, s);
+}
+
+hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const uint16_t* const* act1,
+                               const uint16_t* act0, int64_t lda0, const uint16_t* wt0, int64_t ldw0,
+                               int64_t K0, int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1,
+                               uint16_t* C, int64_t ldc, hipStream_t s) {
+  if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.M = M; a.act0 = act0; a.lda0 = lda0; a.wt0 = wt0; a.ldw0 = ldw0; a.K0 = K0;
+  a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1; a.C = C; a.ldc = ldc;
+  int64_t n = 0;
+  for (int i = 0; i < nproj; ++i) n += rows[i];
+  a.N = n;
+  const int64_t tile = ceil_div(M, 256) * ceil_div(n, 256) >= 256 ? 256 : 128;
+  for (int i = 0; i + 1 < nproj; ++i)
+    if (rows[i] % tile != 0) return hipErrorInvalidValue;  // a tile would straddle two projections
+  a.nseg = nproj;
+  int64_t n0 = 0;
+  for (int i = 0; i < nproj; ++i) {
+    a.seg[i] = Nf4Seg{nullptr, nullptr, nullptr, n0, rows[i], act1[i]};
+    n0 += rows[i];
+  }
+  return launch_tiles<false>(a, s);
+}
+
+bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows) {
+  int64_t n = 0;
+  for (int i = 0; i < nproj; ++i) n += rows[i];
+  const int64_t tile = ceil_div(M, 256) * ceil_div(n, 256) >= 256 ? 256 : 128;
+  for (int i = 0; i + 1 < nproj; ++i)
+    if (rows[i] % tile != 0) return false;
+  return true;
 }
 
 hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,

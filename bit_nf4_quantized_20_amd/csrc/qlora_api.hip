@@ -300,22 +300,35 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   hipError_t e = launch_lora_down(X, in, T, in, A, n, r, uscale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s,
                                   keep, in / 8);
   if (T >= kMaterializeTokens) {
-    // W_hat of every projection into [N][in] bf16, then the bf16 GEMM; the
-    // LoRA term as extra K-steps over [sU_0 | sU_1 | ...] against B_i placed
-    // block-diagonally in [N][n 2rp]
+    // W_hat of every projection into [N][in] bf16, then the bf16 GEMM.  The
+    // LoRA term runs as extra K-steps: when no tile straddles two projections
+    // each tile reads its own projection's sU_i against B_i (stacked [N][2rp]);
+    // otherwise over [sU_0 | sU_1 | ...] against B_i placed block-diagonally
+    // in [N][n 2rp]
     uint16_t* w_dq = reinterpret_cast<uint16_t*>(base + lay.w_dq);
-    const int64_t ldb = n * 2 * rp;
-    if (e == hipSuccess && n > 1) e = launch_fill_f32(reinterpret_cast<float*>(b_pad), N * ldb / 2, 0.f, s);
+    const bool per_proj = n > 1 && gemm_proj_aligned(T, n, outs);
+    const int64_t ldb = per_proj ? 2 * rp : n * 2 * rp;
+    if (e == hipSuccess && n > 1 && !per_proj)
+      e = launch_fill_f32(reinterpret_cast<float*>(b_pad), N * ldb / 2, 0.f, s);
     int64_t off = 0;
     for (int i = 0; i < n && e == hipSuccess; ++i) {
-      e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * ldb + i * 2 * rp, rp, ldb, s);
+      e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * ldb + (per_proj ? 0 : i * 2 * rp), rp, ldb,
+                          s);
       if (e == hipSuccess)
         e = launch_nf4_dequantize(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i] * in,
                                   w_dq + off * in, s);
       off += outs[i];
     }
-    if (e == hipSuccess)
-      e = launch_gemm_nt(T, N, X, in, w_dq, in, in, u_pad, ldb, b_pad, ldb, ldb, Y, N, s);
+    if (e == hipSuccess) {
+      if (per_proj) {
+        const uint16_t* act1[kMaxProj];
+        for (int i = 0; i < n; ++i) act1[i] = u_pad + i * 2 * rp;
+        e = launch_gemm_nt_proj(T, n, outs, act1, X, in, w_dq, in, in, n * 2 * rp, b_pad, ldb, 2 * rp, Y, N,
+                                s);
+      } else {
+        e = launch_gemm_nt(T, N, X, in, w_dq, in, in, u_pad, ldb, b_pad, ldb, ldb, Y, N, s);
+      }
+    }
     return launched(e);
   }
   Nf4Proj proj[kMaxProj];
