@@ -91,6 +91,9 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
                            int64_t Cp, int64_t ldd, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
+// count (<= kMaxFill) buffers dst[i] of n[i] floats set to v in one launch
+constexpr int kMaxFill = 2 * kMaxProj;
+hipError_t launch_fill_many_f32(float* const* dst, const int64_t* n, int count, float v, hipStream_t s);
 
 // C[M][N] (bf16, ldc) = sum over the two K segments of act_i[m][k] * wt_i[n][k]
 // (bf16, K-contiguous, leading dims lda_i / ldw_i).  K0, K1 multiples of 64

@@ -570,4 +570,40 @@ hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Several buffers set to v in one launch (a small kernel costs its launch
+// more than its work): buffer b covers workgroups [first[b], first[b + 1]).
+struct FillList {
+  float* dst[kMaxFill];
+  int64_t n[kMaxFill];
+  int64_t first[kMaxFill + 1];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void k_fill_many_f32(FillList L, float v) {
+  const int64_t wg = blockIdx.x;
+  int b = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxFill; ++i)
+    if (i < L.count && wg >= L.first[i]) b = i;
+  const int64_t idx = (wg - L.first[b]) * 256 + threadIdx.x;
+  if (idx < L.n[b]) L.dst[b][idx] = v;
+}
+
+hipError_t launch_fill_many_f32(float* const* dst, const int64_t* n, int count, float v, hipStream_t s) {
+  if (count < 1 || count > kMaxFill) return hipErrorInvalidValue;
+  FillList L{};
+  L.count = count;
+  int64_t wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    L.dst[i] = dst[i];
+    L.n[i] = n[i];
+    L.first[i] = wgs;
+    wgs += ceil_div(n[i], 256);
+  }
+  L.first[count] = wgs;
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_many_f32, dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, s, L, v);
+  return hipGetLastError();
+}
+
 }  // namespace qlora

@@ -366,11 +366,17 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   if (int st = check_device()) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  for (int i = 0; i < n && e == hipSuccess; ++i) {
-    e = launch_fill_f32(dA[i], r * in, 0.f, s);
-    if (e == hipSuccess) e = launch_fill_f32(dB[i], outs[i] * r, 0.f, s);
+  // dA_i, dB_i are overwritten: zeroed here (one launch), the gradient
+  // kernels then add their token slices
+  float* zero_dst[kMaxFill];
+  int64_t zero_n[kMaxFill];
+  for (int i = 0; i < n; ++i) {
+    zero_dst[2 * i] = dA[i];
+    zero_n[2 * i] = r * in;
+    zero_dst[2 * i + 1] = dB[i];
+    zero_n[2 * i + 1] = outs[i] * r;
   }
+  hipError_t e = launch_fill_many_f32(zero_dst, zero_n, 2 * n, 0.f, s);
   if (T == 0 || e != hipSuccess) return launched(e);
 
   const float scale = alpha / static_cast<float>(r);
