@@ -43,6 +43,11 @@ int launched(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNC
 // ---------------------------------------------------------------------------
 constexpr size_t kMinWorkspace = 256;
 
+// Largest tensor of the quantize / dequantize calls: 2^36 weights (256 GiB
+// as fp32, more than one GPU holds); the dequantize grid runs one thread per
+// 32 weights and stays below 2^32 threads.
+constexpr int64_t kMaxNumel = int64_t(1) << 36;
+
 struct Carve {
   size_t off = 0;
   size_t take(size_t bytes) {
@@ -127,6 +132,19 @@ bool linear_shapes_ok(int64_t T, int64_t in, int64_t out, int64_t r) {
   return true;
 }
 
+// Every bf16 operand of a linear call -- X, Y / dY, dX, and the dequantized
+// weight the large-token paths build in the workspace -- stays below 2^31
+// bytes: the kernels address the rows of a tile with 32-bit offsets.
+constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
+
+bool bf16_matrix_fits(int64_t rows, int64_t cols) {
+  return rows <= 0 || cols <= 0 || cols <= kMaxOperandBytes / 2 / rows;
+}
+
+bool operands_fit(int64_t T, int64_t in, int64_t N) {
+  return bf16_matrix_fits(T, in) && bf16_matrix_fits(T, N) && bf16_matrix_fits(N, in);
+}
+
 int check_weight(const qlora_nf4_weight* W) {
   if (W == nullptr || W->codes == nullptr || W->absmax_q == nullptr || W->absmax_scale == nullptr)
     return QLORA_ERR_NULL;
@@ -151,7 +169,7 @@ int nf4_storage_bytes(int64_t numel, size_t* codes_bytes, size_t* absmax_q_bytes
 int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
                  float* absmax_scale, qlora_stream stream) {
   if (numel < 0 || (numel % kBlock) != 0) return QLORA_ERR_SHAPE;
-  if (numel > (int64_t(1) << 45)) return QLORA_ERR_SHAPE;
+  if (numel > kMaxNumel) return QLORA_ERR_SHAPE;
   if (numel == 0) return QLORA_OK;
   if (!w || !codes || !absmax_q || !absmax_scale) return QLORA_ERR_NULL;
   if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale))
@@ -164,7 +182,7 @@ int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_
 int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_scale,
                    int64_t numel, qlora_bf16* w_out, qlora_stream stream) {
   if (numel < 0 || (numel % kBlock) != 0) return QLORA_ERR_SHAPE;
-  if (numel > (int64_t(1) << 45)) return QLORA_ERR_SHAPE;
+  if (numel > kMaxNumel) return QLORA_ERR_SHAPE;
   if (numel == 0) return QLORA_OK;
   if (!codes || !absmax_q || !absmax_scale || !w_out) return QLORA_ERR_NULL;
   if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(w_out))
@@ -177,7 +195,7 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
 int nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
                       qlora_stream stream) {
   if (numel < 0 || (numel % kBlock) != 0) return QLORA_ERR_SHAPE;
-  if (numel > (int64_t(1) << 45)) return QLORA_ERR_SHAPE;
+  if (numel > kMaxNumel) return QLORA_ERR_SHAPE;
   if (numel == 0) return QLORA_OK;
   if (!w || !codes || !absmax) return QLORA_ERR_NULL;
   if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
@@ -188,7 +206,7 @@ int nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absm
 int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel, qlora_bf16* w_out,
                         qlora_stream stream) {
   if (numel < 0 || (numel % kBlock) != 0) return QLORA_ERR_SHAPE;
-  if (numel > (int64_t(1) << 45)) return QLORA_ERR_SHAPE;
+  if (numel > kMaxNumel) return QLORA_ERR_SHAPE;
   if (numel == 0) return QLORA_OK;
   if (!codes || !absmax || !w_out) return QLORA_ERR_NULL;
   if (!aligned16(codes) || !aligned16(absmax) || !aligned16(w_out)) return QLORA_ERR_ALIGN;
@@ -206,6 +224,7 @@ size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t
   if (n < 1 || n > kMaxProj || out_features == nullptr) return 0;
   for (int i = 0; i < n; ++i)
     if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
+  if (!operands_fit(T, in_features, total_out(out_features, n))) return 0;
   const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r).total
                                : fwd_layout(T, in_features, out_features, n, r, false).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
@@ -214,6 +233,7 @@ size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t
 size_t qlora_workspace_bytes_dropout(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                                      int backward) {
   if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;
+  if (!operands_fit(T, in_features, out_features)) return 0;
   const size_t need = backward ? bwd_layout(T, in_features, &out_features, 1, r).total
                                : fwd_layout(T, in_features, &out_features, 1, r, true).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
@@ -236,6 +256,7 @@ int check_projections(const qlora_nf4_weight* W, int n, int64_t T, int64_t r, in
     outs[i] = W[i].rows;
   }
   *in = W[0].cols;
+  if (!operands_fit(T, *in, total_out(outs, n))) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
 
@@ -480,6 +501,7 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* W, const qlora_bf16* X, con
 
 size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, int64_t r) {
   if (!linear_shapes_ok(0, in_features, out_features, r)) return 0;
+  if (!operands_fit(0, in_features, out_features)) return 0;
   const int64_t rp = padded_rank(r);
   Carve c;
   c.take(static_cast<size_t>(out_features * rp * 4));  // B padded [out][2 rp]
@@ -491,7 +513,7 @@ int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16
                 float alpha, qlora_bf16* W_out, void* ws, size_t ws_bytes, qlora_stream stream) {
   if (int st = check_weight(W)) return st;
   const int64_t out = W->rows, in = W->cols;
-  if (!linear_shapes_ok(0, in, out, r)) return QLORA_ERR_SHAPE;
+  if (!linear_shapes_ok(0, in, out, r) || !operands_fit(0, in, out)) return QLORA_ERR_SHAPE;
   if (!A || !B || !W_out) return QLORA_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(W_out)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;

@@ -47,7 +47,8 @@ typedef void* qlora_stream;    /* hipStream_t */
 enum qlora_status {
   QLORA_OK = 0,
   QLORA_ERR_NULL = -1,      /* a required pointer is NULL */
-  QLORA_ERR_SHAPE = -2,     /* a size is negative, not a multiple of 64, or out of range */
+  QLORA_ERR_SHAPE = -2,     /* a size is negative, not a multiple of 64, or out of range
+                               (linear calls: a bf16 operand of 2^31 bytes or more) */
   QLORA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
   QLORA_ERR_WORKSPACE = -4, /* workspace missing or smaller than qlora_workspace_bytes() */
   QLORA_ERR_LAUNCH = -5,    /* a kernel launch failed (hipGetLastError) */
@@ -103,7 +104,7 @@ int nf4_storage_bytes(int64_t numel, size_t* codes_bytes, size_t* absmax_q_bytes
  * block gets codes 7 and q 0; a zero group gets s 0.  The last group may be
  * partial.  The codes use the exact fp32 a_b.
  *   w            [numel] fp32, finite (non-finite input: outputs unspecified)
- *   numel        >= 0, multiple of 64; 0 is a no-op
+ *   numel        >= 0, multiple of 64, at most 2^36; 0 is a no-op
  *   codes        [numel/2] out;  absmax_q [numel/64] out;
  *   absmax_scale [ceil(numel/16384)] out
  * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
@@ -117,6 +118,7 @@ int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_
  * (paperclase "QLoRA", Parte 2: w_hat = NF4[c] * absmax; ultralytics "QLoRA":
  * weights are dequantized to bfloat16 right before the matmul).
  *   codes, absmax_q, absmax_scale as produced by nf4_quantize for numel
+ *   (numel limits as for nf4_quantize)
  *   w_out [numel] bf16 out (row-major, same order as the quantized input)
  * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
  */
@@ -132,7 +134,7 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
  * Codes exactly as nf4_quantize (they use the exact absmax in both formats);
  * w_hat = bf16_rne(fl32(L[c] * a_b)).
  *   codes  [numel/2];  absmax [numel/64] fp32 (out of quantize, in of dequantize)
- *   numel  >= 0, multiple of 64 (0 is a no-op)
+ *   numel  >= 0, multiple of 64, at most 2^36 (0 is a no-op)
  * The linear calls take the double-quantized format only.
  * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
  */
@@ -166,6 +168,10 @@ size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_feature
  *   A   [r, in] bf16;  B [out, r] bf16;  1 <= r <= 256;  alpha finite
  *   Y   [T, out] bf16 out
  *   ws  workspace of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 0)
+ * Size limit (all linear calls, also multi / dropout / merge): X, Y, dY, dX
+ * and the dequantized weight [out, in] in bf16 must each be smaller than
+ * 2^31 bytes (QLORA_ERR_SHAPE otherwise); larger token batches are split
+ * into several calls.
  * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE, LAUNCH.
  */
 int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,

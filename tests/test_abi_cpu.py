@@ -191,6 +191,46 @@ def test_linear_validation():
         assert len(lib.qlora_status_string(s)) > 0
 
 
+def test_operand_size_limit():
+    # every bf16 operand (X, Y / dY, dX, the dequantized weight) must stay
+    # below 2^31 bytes: 2^31 - 2 bytes pass, 2^31 are refused, on every side
+    lib = _api(_lib())
+    i64, sz = ctypes.c_int64, ctypes.c_size_t
+    lib.qlora_workspace_bytes_dropout.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes_dropout.restype = sz
+    lib.qlora_merge_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.qlora_merge_workspace_bytes.restype = sz
+    limit = 1 << 30                                   # bf16 elements in 2^31 bytes
+    assert lib.qlora_workspace_bytes(limit // 4096 - 1, 4096, 64, 16, 0) > 0
+    assert lib.qlora_workspace_bytes(limit // 4096, 4096, 64, 16, 0) == 0     # X
+    assert lib.qlora_workspace_bytes(limit // 8192, 64, 8192, 16, 1) == 0     # Y / dY
+    assert lib.qlora_workspace_bytes(1, 1 << 15, 1 << 15, 16, 0) == 0         # weight
+    assert lib.qlora_workspace_bytes(1, 1 << 15, (1 << 15) - 64, 16, 0) > 0
+    assert lib.qlora_workspace_bytes_dropout(limit // 4096, 4096, 64, 16, 0) == 0
+    assert lib.qlora_merge_workspace_bytes(1 << 15, 1 << 15, 16) == 0
+    assert lib.qlora_merge_workspace_bytes(1 << 15, (1 << 15) - 64, 16) > 0
+    F = _FAKE
+    W = _W(F, F, F, 64, 4096)
+    call = lambda T: lib.qlora_linear_fwd(ctypes.byref(W), F, T, F, F, 16, 32.0, F, F, 1 << 40, None)
+    assert call(limit // 4096) == -2
+    assert call(limit // 4096 - 1) == -6             # valid: fails only at the device check
+
+
+def test_tensor_size_limit():
+    # quantize / dequantize take at most 2^36 weights (one dequantize thread
+    # per 32 weights stays below 2^32 threads)
+    lib = _api(_lib())
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.nf4_quantize_nodq.argtypes = [vp, i64, vp, vp, vp]
+    lib.nf4_dequantize_nodq.argtypes = [vp, vp, i64, vp, vp]
+    F, big = _FAKE, (1 << 36) + 64
+    assert lib.nf4_quantize(F, big, F, F, F, None) == -2
+    assert lib.nf4_dequantize(F, F, F, big, F, None) == -2
+    assert lib.nf4_quantize_nodq(F, big, F, F, None) == -2
+    assert lib.nf4_dequantize_nodq(F, F, big, F, None) == -2
+    assert lib.nf4_quantize(F, 1 << 36, F, F, F, None) == -6   # valid: only the device check fails
+
+
 def test_multi_projection_validation():
     lib = _lib()
     i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
