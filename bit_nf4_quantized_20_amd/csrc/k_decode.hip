@@ -46,6 +46,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 16;
 constexpr int kTileSlots = 16 * 32;  // 16 rows x 32 pieces of 16 B (8 KB)
 constexpr int kCodeSlots = 16 * 8;   // 16 rows x 8 pieces: one chunk of codes (2 KB)
+// Split kernel tiles: rows of 32 pieces padded to 33, so piece p of row t
+// sits at slot 33 t + p.  A fragment read (16 rows at one piece) then falls
+// on 16 distinct 4-bank groups, and every lane's slots differ by constants,
+// which the LDS instructions take as immediate offsets.
+constexpr int kPitch = 33;
+constexpr int kPadSlots = 16 * kPitch;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kStream = 2;               // cache policy nt: streamed once
 constexpr uint32_t kPastEnd = 0x80000000u;  // past every buffer (all < 2^31 bytes)
@@ -338,17 +344,21 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
 //     register sets, no loop-carried copies that would force a full wait);
 //     NS = 0 keeps a loop whose start is hidden from the optimizer so the
 //     loading steps are not peeled off into a differently ordered prologue.
-// XP = token-row pairs of the X tile (T <= 2 XP).
+// XP = token-row pairs of the X tile (T <= 2 XP).  kFull: every wave's
+// block range is whole chunks (in % 1024 == 0), so no load needs a per-lane
+// range test; a step past the range reads through an empty buffer resource.
+// Each load's per-lane offset (row and piece) is fixed for the whole kernel
+// and the chunk's position goes into the scalar offset.
 // ---------------------------------------------------------------------------
-template <int XP, int NS>
+template <int XP, int NS, bool kFull>
 __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
     uint16_t* __restrict__ Y, int64_t out, int64_t ldy) {
   constexpr int kPairs = kWaves / 2;
-  __shared__ u32x4 s_x[kPairs][2][kTileSlots];   // X tiles by chunk parity
-  __shared__ u32x4 s_a[kPairs][kTileSlots];      // A tile of each U wave
+  __shared__ u32x4 s_x[kPairs][2][kPadSlots];    // X tiles by chunk parity
+  __shared__ u32x4 s_a[kPairs][kPadSlots];       // A tile of each U wave
   __shared__ u32x4 s_codes[kPairs][kCodeSlots];  // codes of each dequantize wave
   __shared__ f32x4 s_acc[kWaves][64];
   __shared__ float s_b[kRows][17];
@@ -372,16 +382,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
   const uint32_t inu = static_cast<uint32_t>(in), nbu = static_cast<uint32_t>(nb);
 
   const uint32_t wbytes = static_cast<uint32_t>(static_cast<uint64_t>(out) * in / 2);
-  const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(codes), 0, static_cast<int>(wbytes), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(absmax_q), 0, static_cast<int>(wbytes / 32), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(scale), 0, static_cast<int>((wbytes + 8191) / 8192 * 4), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(X), 0, static_cast<int>(static_cast<uint32_t>(T) * inu * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(r) * inu * 2), kBufferWord3);
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(out) * r * 2), kBufferWord3);
 
@@ -429,17 +429,47 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
     // ------------------------------------------------ dequantize waves
     u32x4* tc = s_codes[qtr];
     CodeStage cs[2];
+    // Per-lane offsets of the code rows and absmax bytes.  With whole
+    // chunks the chunk's position is a scalar offset (every byte a live step
+    // reads lies in its row, so the per-lane offset alone keeps the bounds
+    // check meaningful) and a step past the range reads through empty buffer
+    // resources.  Otherwise a partial last chunk reads past its row's end,
+    // so the whole offset stays per lane.
+    const uint32_t rl = static_cast<uint32_t>(r0) + (lane >> 3);
+    const uint32_t cvo0 = rl * (inu / 2) + 16 * (lane & 7), cvo1 = cvo0 + 8 * (inu / 2);
+    const uint32_t qvo = row * nbu + static_cast<uint32_t>(g);
+    const int cbytes = static_cast<int>(wbytes), qbytes = static_cast<int>(wbytes / 32);
+    const int sbytes = static_cast<int>((wbytes + 8191) / 8192 * 4);
     auto load_codes = [&](CodeStage& st, int c) {
-      const uint32_t pe = c < nch ? 0u : kPastEnd;  // uniform, OR-ed into the offsets
-      const uint32_t base = static_cast<uint32_t>(bw0 + 4 * c) * 32 + 16 * (lane & 7);
-      const uint32_t rl = static_cast<uint32_t>(r0) + (lane >> 3);
-      st.c0 = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, (rl * (inu / 2) + base) | pe, 0, kStream));
-      st.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs_codes, ((rl + 8) * (inu / 2) + base) | pe, 0, kStream));
-      const uint32_t bi = row * nbu + static_cast<uint32_t>(bw0 + 4 * c + g);
-      st.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi | pe, 0, 0);
-      st.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, ((bi >> 8) * 4) | pe, 0, 0));
+      const int blk0 = bw0 + 4 * c;  // the chunk's first block in the row (uniform)
+      if constexpr (kFull) {
+        const bool live = c < nch;
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(codes), 0, live ? cbytes : 0, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(absmax_q), 0, live ? qbytes : 0, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(scale), 0, live ? sbytes : 0, kBufferWord3);
+        st.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, cvo0, 32 * blk0, kStream));
+        st.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, cvo1, 32 * blk0, kStream));
+        st.q = __builtin_amdgcn_raw_buffer_load_b8(rq, qvo, blk0, 0);
+        const uint32_t bi = qvo + static_cast<uint32_t>(blk0);
+        st.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, (bi >> 8) * 4, 0, 0));
+      } else {
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(codes), 0, cbytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(absmax_q), 0, qbytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(scale), 0, sbytes, kBufferWord3);
+        const uint32_t pe = c < nch ? 0u : kPastEnd;  // uniform, OR-ed into the offsets
+        const uint32_t cb = 32 * static_cast<uint32_t>(blk0);
+        st.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (cvo0 + cb) | pe, 0, kStream));
+        st.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (cvo1 + cb) | pe, 0, kStream));
+        const uint32_t bi = qvo + static_cast<uint32_t>(blk0);
+        st.q = __builtin_amdgcn_raw_buffer_load_b8(rq, bi | pe, 0, 0);
+        st.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, ((bi >> 8) * 4) | pe, 0, 0));
+      }
     };
     auto step = [&](int c, auto d) {
       CodeStage& st = cs[decltype(d)::value];
@@ -457,11 +487,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
       load_codes(st, c + 2);
       if (c >= 0) {
         __syncthreads();  // X(c) is in its tile
-        const u32x4* tx = s_x[qtr][decltype(d)::value];
+        const u32x4* tx = s_x[qtr][decltype(d)::value] + kPitch * n + 8 * g;
         const Nf4Table tab = make_table(ah);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
+          const u32x4 xf = tx[j];
           const uint32_t cw = j < 4 ? cc0[j] : cc1[j - 4];
           uint32_t w[4];
           lookup8(tab, cw, w);
@@ -475,40 +505,58 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
     // ------------------------------------------------ U waves
     u32x4* ta = s_a[qtr];
     u32x4 xs[2][XP], as[2][8];
-    auto load_rows = [&](auto& reg, const __amdgpu_buffer_rsrc_t& rs, auto npairs, int c) {
-      const uint32_t k0 = static_cast<uint32_t>(bw0 + 4 * c) * 64;
-      // valid k of this chunk: 256, fewer in a partial last chunk, none past the range
-      const int lim = c < nch ? min((bw1 - bw0 - 4 * c) * 64, 256) : 0;
+    // lane (half, piece) of row pair i loads piece `piece` (16 B) of row
+    // 2 i + half of the chunk; rows >= T (X) or >= r (A) lie past the buffer
+    uint32_t voff[8];
 #pragma unroll
-      for (int i = 0; i < decltype(npairs)::value; ++i) {
-        const int t = 2 * i + half, p = piece ^ t;
-        const uint32_t off = 8 * p < lim ? ((t * inu) + k0 + 8 * p) * 2 : kPastEnd;
-        reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    for (int i = 0; i < 8; ++i) voff[i] = ((2 * i + half) * inu + 8 * piece) * 2;
+    auto load_rows = [&](auto& reg, const uint16_t* base, uint32_t bytes, auto npairs, int c) {
+      const int kb = (bw0 + 4 * c) * 128;  // the chunk's first byte in a row (uniform)
+      if constexpr (kFull) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base), 0, c < nch ? static_cast<int>(bytes) : 0, kBufferWord3);
+#pragma unroll
+        for (int i = 0; i < decltype(npairs)::value; ++i)
+          reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], kb, 0));
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base), 0, static_cast<int>(bytes), kBufferWord3);
+        // valid k of this chunk: 256, fewer in a partial last chunk, none past the range
+        const int lim = c < nch ? min((bw1 - bw0 - 4 * c) * 64, 256) : 0;
+#pragma unroll
+        for (int i = 0; i < decltype(npairs)::value; ++i) {
+          const uint32_t off = 8 * piece < lim ? voff[i] : kPastEnd;
+          reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, kb, 0));
+        }
       }
     };
+    const uint32_t xbytes = static_cast<uint32_t>(T) * inu * 2, abytes = static_cast<uint32_t>(r) * inu * 2;
+    const int wslot = kPitch * half + piece;  // + 2 kPitch i for row pair i
     // token rows that no chunk writes stay zero in both X tiles
 #pragma unroll
     for (int i = XP; i < 8; ++i) {
-      s_x[qtr][0][64 * i + lane] = zero4;
-      s_x[qtr][1][64 * i + lane] = zero4;
+      s_x[qtr][0][wslot + 2 * kPitch * i] = zero4;
+      s_x[qtr][1][wslot + 2 * kPitch * i] = zero4;
     }
     auto step = [&](int c, auto d) {
       constexpr int kD = decltype(d)::value;
       u32x4* tx = s_x[qtr][kD];
       if (c >= 0) {
 #pragma unroll
-        for (int i = 0; i < XP; ++i) tx[64 * i + lane] = xs[kD][i];
+        for (int i = 0; i < XP; ++i) tx[wslot + 2 * kPitch * i] = xs[kD][i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ta[64 * i + lane] = as[kD][i];
+        for (int i = 0; i < 8; ++i) ta[wslot + 2 * kPitch * i] = as[kD][i];
       }
-      load_rows(xs[kD], rs_x, std::integral_constant<int, XP>{}, c + 2);
-      load_rows(as[kD], rs_a, std::integral_constant<int, 8>{}, c + 2);  // ranks >= r read zeros
+      load_rows(xs[kD], X, xbytes, std::integral_constant<int, XP>{}, c + 2);
+      load_rows(as[kD], A, abytes, std::integral_constant<int, 8>{}, c + 2);  // ranks >= r read zeros
       if (c >= 0) {
         __syncthreads();  // X(c) is in tx for the partner
+        const u32x4* fx = tx + kPitch * n + 8 * g;
+        const u32x4* fa = ta + kPitch * n + 8 * g;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
-          const u32x4 af = ta[tile_slot(n, 8 * g + j)];
+          const u32x4 xf = fx[j];
+          const u32x4 af = fa[j];
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc, 0, 0, 0);
         }
       }
@@ -570,14 +618,22 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, cons
     const int64_t steps = round_up((ceil_div(in / 64, 4) + 3) / 4, 2);
     const int ns = steps == 4 ? 4 : steps == 8 ? 8 : 0;
     const int xp = T <= 2 ? 1 : T <= 4 ? 2 : T <= 8 ? 4 : 8;
-#define QLORA_SPLIT(XPV, NSV)                                                                     \
-  hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV>), grid, block, 0, st, codes, absmax_q, scale, in, X, \
-                     iT, A, B, ir, s, Y, out, ldy)
-#define QLORA_SPLIT_NS(XPV)        \
-  do {                             \
-    if (ns == 4) QLORA_SPLIT(XPV, 4); \
-    else if (ns == 8) QLORA_SPLIT(XPV, 8); \
-    else QLORA_SPLIT(XPV, 0);      \
+    // whole chunks in every wave's block range: 16 | in / 64
+    const bool full = (in / 64) % 16 == 0;
+#define QLORA_SPLIT(XPV, NSV, FV)                                                                  \
+  hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV, FV>), grid, block, 0, st, codes, absmax_q, scale, in, \
+                     X, iT, A, B, ir, s, Y, out, ldy)
+#define QLORA_SPLIT_NS(XPV)                                  \
+  do {                                                       \
+    if (full) {                                              \
+      if (ns == 4) QLORA_SPLIT(XPV, 4, true);                \
+      else if (ns == 8) QLORA_SPLIT(XPV, 8, true);           \
+      else QLORA_SPLIT(XPV, 0, true);                        \
+    } else {                                                 \
+      if (ns == 4) QLORA_SPLIT(XPV, 4, false);               \
+      else if (ns == 8) QLORA_SPLIT(XPV, 8, false);          \
+      else QLORA_SPLIT(XPV, 0, false);                       \
+    }                                                        \
   } while (0)
     if (xp == 1) QLORA_SPLIT_NS(1);
     else if (xp == 2) QLORA_SPLIT_NS(2);

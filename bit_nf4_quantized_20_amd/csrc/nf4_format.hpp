@@ -152,7 +152,9 @@ __device__ __forceinline__ Nf4Table make_table(float ahat) {
 }
 
 // Looks up 4 codes, one per byte of `sel` (values 0..7 after masking) with
-// `pick` = 0x03020100 | (bit3 of each code << 2) per byte.
+// `pick` = 0x03020100 | (bit3 of each code << 2) per byte.  The pick is one
+// v_bitop3 ((x & 0x04040404) | 0x03020100, truth table 0xEA) on the shifted
+// codes instead of an and + or.
 __device__ __forceinline__ uint32_t lookup_plane(const uint32_t (&plane)[4], uint32_t sel, uint32_t pick) {
   const uint32_t a = perm(plane[1], plane[0], sel);
   const uint32_t b = perm(plane[3], plane[2], sel);
@@ -163,11 +165,10 @@ __device__ __forceinline__ uint32_t lookup_plane(const uint32_t (&plane)[4], uin
 // Output order "split": out[0] = (w0, w2), out[1] = (w4, w6), out[2] = (w1, w3),
 // out[3] = (w5, w7) -- each dword is two bf16, lower element in bits 0-15.
 __device__ __forceinline__ void lookup8_split(const Nf4Table& t, uint32_t c, uint32_t out[4]) {
-  const uint32_t c4 = c >> 4;
   const uint32_t sel_e = c & 0x07070707u;
-  const uint32_t pick_e = 0x03020100u | ((c >> 1) & 0x04040404u);
-  const uint32_t sel_o = c4 & 0x07070707u;
-  const uint32_t pick_o = 0x03020100u | ((c4 >> 1) & 0x04040404u);
+  const uint32_t pick_e = __builtin_amdgcn_bitop3_b32(c >> 1, 0x04040404u, 0x03020100u, 0xEA);
+  const uint32_t sel_o = (c >> 4) & 0x07070707u;
+  const uint32_t pick_o = __builtin_amdgcn_bitop3_b32(c >> 5, 0x04040404u, 0x03020100u, 0xEA);
   const uint32_t el = lookup_plane(t.lo, sel_e, pick_e);  // byte i = lo(w_{2i})
   const uint32_t eh = lookup_plane(t.hi, sel_e, pick_e);
   const uint32_t ol = lookup_plane(t.lo, sel_o, pick_o);  // byte i = lo(w_{2i+1})

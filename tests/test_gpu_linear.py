@@ -304,6 +304,25 @@ def test_small_token_lora_only(T):
     _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, f"W=0 T={T}")
 
 
+@pytest.mark.parametrize("T,n_out,n_in,r", [
+    (3, 256, 4096, 16),    # two token-row pairs, four unrolled chunk steps, whole chunks
+    (6, 256, 4096, 8),     # four token-row pairs
+    (11, 128, 8192, 16),   # eight token-row pairs, eight unrolled steps
+    (2, 192, 3136, 16),    # four unrolled steps, a partial last chunk in every wave
+    (13, 64, 2048, 12),    # the step loop, whole chunks
+    (7, 64, 1600, 5),      # the step loop, a partial last chunk
+])
+def test_small_token_split_variants(T, n_out, n_in, r):
+    # the r <= 16 kernel's variants: token-row pairs, unrolled or looped chunk
+    # steps, whole or partial chunks per wave
+    q = require_gpu()
+    banner(f"small-token split T={T} out={n_out} in={n_in} r={r}")
+    alpha = 2.0 * r
+    h = _make(14, T, T, n_out, n_in, r)
+    W, w_hat = _quantize(q, h["w"])
+    _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, f"T={T} in={n_in}")
+
+
 @pytest.mark.parametrize("T", [1, 16])
 def test_small_token_more_workgroups_than_cus(T):
     # 8B MLP gate shape at decode size: 896 workgroups of 16 rows, more than
