@@ -264,6 +264,9 @@ def main():
     # ------------------------------------------------------ adapter merge
     extra["merge_8b_gate"] = merge_leg(q, synth, dev, bf)
 
+    # ------------------------------------------- q|k|v at decode sizes
+    extra["qkv8b_decode"] = qkv_decode_leg(q, synth, dev, bf)
+
     # ------------------------------------------- large-token fwd + bwd
     if not args.no_train:
         extra["mlp8b_fwd_bwd"] = train_leg(q, synth, dev, bf)
@@ -298,6 +301,64 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def qkv_decode_leg(q, synth, dev, bf, P=24, n=192):
+    """The 8B attention q|k|v projections (4096 -> 4096, 1024, 1024; r = 16,
+    alpha = 32) at T = 1 and T = 16: one multi-projection call (a single
+    small-token launch over all three weights) against three single-projection
+    calls.  Each is captured as a graph of n back-to-back calls cycling
+    through P copies of the weights (P x 13 MB, past the 256 MB last-level
+    cache) and replayed; microseconds per q|k|v forward."""
+    import torch
+    wl = synth.WORKLOADS[4]
+    r, alpha = wl.r, wl.alpha
+    projs = wl.projections[:3]
+    n_in = projs[0].in_features
+    outs = [p.out_features for p in projs]
+    base = [q.nf4_quantize_weight(torch.from_numpy(synth.weight(4, i, p.out_features, n_in)).to(dev))
+            for i, p in enumerate(projs)]
+    pool = [[q.NF4Weight(W.codes.clone(), W.absmax_q.clone(), W.absmax_scale.clone(), W.rows, W.cols)
+             for W in base] for _ in range(P)]
+    As = [bf(synth.lora_A(4, i, r, n_in)) for i in range(3)]
+    Bs = [bf(synth.lora_B(4, i, p.out_features, r)) for i, p in enumerate(projs)]
+    res = {"outs": outs, "in": n_in, "r": r}
+    for T in (1, 16):
+        X = bf(synth.activations(4, 0, T, n_in))
+        Y = torch.empty(T, sum(outs), dtype=torch.bfloat16, device=dev)
+        Ys = [torch.empty(T, o, dtype=torch.bfloat16, device=dev) for o in outs]
+
+        def multi(i):
+            q.qlora_linear_fwd_multi(pool[i % P], X, As, Bs, r, alpha, Y=Y)
+
+        def single(i):
+            for W, A, B, Yi in zip(pool[i % P], As, Bs, Ys):
+                q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Yi)
+
+        def graph_us(fn):
+            for i in range(4):
+                fn(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fn(i)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        us_m, us_s = graph_us(multi), graph_us(single)
+        # X counted once: the three projections share it
+        nbytes = sum(decode_call_bytes(o, n_in, T, r) for o in outs) - 2 * 2 * T * n_in
+        res[f"T{T}"] = {"multi_us": round(us_m, 2), "three_calls_us": round(us_s, 2),
+                        "multi_GB_per_s": round(nbytes / (us_m * 1e-6) / 1e9, 1),
+                        "algorithmic_bytes": nbytes}
+    return res
 
 
 def merge_leg(q, synth, dev, bf):

@@ -143,9 +143,25 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* absmax_q, const flo
 constexpr int64_t kDecodeMaxT = 16;
 constexpr int64_t kDecodeMaxRank = 64;
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
-hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
-                             int64_t in, int64_t out, const uint16_t* X, int64_t T,
-                             const uint16_t* A, const uint16_t* B, int64_t r, float s,
-                             uint16_t* Y, int64_t ldy, hipStream_t st);
+// One projection of the small-token forward: its NF4 weight [out][in] and
+// LoRA factors A [r][in], B [out][r].
+struct DecodeProj {
+  const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
+  const uint16_t* A; const uint16_t* B;
+  int64_t out;
+};
+// The projections of one launch (kernel argument): workgroup ranges and the
+// output columns of each, Y = the first projection's column 0.
+struct DecodeSet {
+  DecodeProj proj[kMaxProj];
+  int wg0[kMaxProj];
+  int64_t col0[kMaxProj];
+  uint16_t* Y;
+  int n;
+};
+// n (1..kMaxProj) projections sharing X, outputs side by side in Y [T][ldy]
+// (projection i from column sum_{j<i} out_j); one launch for r <= 16.
+hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const uint16_t* X, int64_t T,
+                             int64_t r, float s, uint16_t* Y, int64_t ldy, hipStream_t st);
 
 }  // namespace qlora

@@ -350,12 +350,26 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
 // Each load's per-lane offset (row and piece) is fixed for the whole kernel
 // and the chunk's position goes into the scalar offset.
 // ---------------------------------------------------------------------------
+// Several projections that share X (q|k|v) run as one launch: workgroups
+// [wg0[p], wg0[p + 1]) take projection p's rows, written to columns
+// [col0[p], col0[p] + out[p]) of Y.
 template <int XP, int NS, bool kFull>
-__global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
-    const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
-    uint16_t* __restrict__ Y, int64_t out, int64_t ldy) {
+__global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int64_t in,
+                                                               const uint16_t* __restrict__ X, int T, int r,
+                                                               float s, int64_t ldy) {
+  // this workgroup's projection (uniform)
+  int pj = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i)
+    if (i < P.n && static_cast<int>(blockIdx.x) >= P.wg0[i]) pj = i;
+  const uint8_t* __restrict__ codes = P.proj[pj].codes;
+  const uint8_t* __restrict__ absmax_q = P.proj[pj].absmax_q;
+  const float* __restrict__ scale = P.proj[pj].scale;
+  const uint16_t* __restrict__ A = P.proj[pj].A;
+  const uint16_t* __restrict__ B = P.proj[pj].B;
+  const int64_t out = P.proj[pj].out;
+  uint16_t* __restrict__ Y = P.Y + P.col0[pj];
+  const int wg = static_cast<int>(blockIdx.x) - P.wg0[pj];  // row block within the projection
   constexpr int kPairs = kWaves / 2;
   __shared__ u32x4 s_x[kPairs][2][kPadSlots];    // X tiles by chunk parity
   __shared__ u32x4 s_a[kPairs][kPadSlots];       // A tile of each U wave
@@ -370,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(
   const int qtr = dq_wave ? wv : wv - kPairs;
   const int n = lane & 15, g = lane >> 4;
   const int half = lane >> 5, piece = lane & 31;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int64_t r0 = static_cast<int64_t>(wg) * kRows;
   const int64_t nb = in / 64;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
@@ -600,19 +614,28 @@ bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r) {
          in % 64 == 0 && in <= (int64_t(1) << 24) && out * in < (int64_t(1) << 32);
 }
 
-hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
-                             int64_t in, int64_t out, const uint16_t* X, int64_t T,
-                             const uint16_t* A, const uint16_t* B, int64_t r, float s,
-                             uint16_t* Y, int64_t ldy, hipStream_t st) {
-  if (!decode_fits(T, in, out, r)) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(out / kRows));
+hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const uint16_t* X, int64_t T,
+                             int64_t r, float s, uint16_t* Y, int64_t ldy, hipStream_t st) {
+  if (n < 1 || n > kMaxProj) return hipErrorInvalidValue;
+  for (int i = 0; i < n; ++i)
+    if (!decode_fits(T, in, proj[i].out, r)) return hipErrorInvalidValue;
   const dim3 block(kThreads);
   const int rt = static_cast<int>(ceil_div(r, 16));
   const int iT = static_cast<int>(T), ir = static_cast<int>(r);
-#define QLORA_DEC(RTV)                                                                            \
-  hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, codes, absmax_q, scale, in, X, iT, \
-                     A, B, ir, s, Y, out, ldy)
   if (rt <= 1) {
+    // all projections in one launch
+    DecodeSet set{};
+    set.n = n;
+    set.Y = Y;
+    int64_t wgs = 0, col = 0;
+    for (int i = 0; i < n; ++i) {
+      set.proj[i] = proj[i];
+      set.wg0[i] = static_cast<int>(wgs);
+      set.col0[i] = col;
+      wgs += proj[i].out / kRows;
+      col += proj[i].out;
+    }
+    const dim3 grid(static_cast<uint32_t>(wgs));
     // chunk steps per wave: fully unrolled when they number 4 (in <= 4096)
     // or 8 (in <= 8192), a loop otherwise
     const int64_t steps = round_up((ceil_div(in / 64, 4) + 3) / 4, 2);
@@ -620,9 +643,8 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, cons
     const int xp = T <= 2 ? 1 : T <= 4 ? 2 : T <= 8 ? 4 : 8;
     // whole chunks in every wave's block range: 16 | in / 64
     const bool full = (in / 64) % 16 == 0;
-#define QLORA_SPLIT(XPV, NSV, FV)                                                                  \
-  hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV, FV>), grid, block, 0, st, codes, absmax_q, scale, in, \
-                     X, iT, A, B, ir, s, Y, out, ldy)
+#define QLORA_SPLIT(XPV, NSV, FV) \
+  hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV, FV>), grid, block, 0, st, set, in, X, iT, ir, s, ldy)
 #define QLORA_SPLIT_NS(XPV)                                  \
   do {                                                       \
     if (full) {                                              \
@@ -641,10 +663,24 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* absmax_q, cons
     else QLORA_SPLIT_NS(8);
 #undef QLORA_SPLIT_NS
 #undef QLORA_SPLIT
-  } else if (rt <= 2) QLORA_DEC(2);
-  else QLORA_DEC(4);
+    return hipGetLastError();
+  }
+  // 16 < r <= 64: one launch per projection
+  int64_t col = 0;
+  for (int i = 0; i < n; ++i) {
+    const DecodeProj& p = proj[i];
+    const dim3 grid(static_cast<uint32_t>(p.out / kRows));
+#define QLORA_DEC(RTV)                                                                                \
+  hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, p.codes, p.absmax_q, p.scale, in, X, iT, \
+                     p.A, p.B, ir, s, Y + col, p.out, ldy)
+    if (rt <= 2) QLORA_DEC(2);
+    else QLORA_DEC(4);
 #undef QLORA_DEC
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    col += p.out;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qlora

@@ -79,7 +79,8 @@ int64_t total_out(const int64_t* outs, int n) {
   return N;
 }
 
-// the small-token forward takes each projection on its own and needs no workspace
+// the small-token forward (all projections in one launch for r <= 16) needs
+// no workspace; it takes the call when every projection fits it
 bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
   for (int i = 0; i < n; ++i)
     if (!decode_fits(T, in, outs[i], r)) return false;
@@ -300,14 +301,10 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   const float scale = alpha / static_cast<float>(r);
   const int64_t N = total_out(outs, n);
   if (!dropout && fwd_uses_decode(T, in, outs, n, r)) {
-    int64_t off = 0;
-    for (int i = 0; i < n; ++i) {
-      const hipError_t e = launch_decode_fwd(W[i].codes, W[i].absmax_q, W[i].absmax_scale, in, outs[i],
-                                             X, T, A[i], B[i], r, scale, Y + off, N, s);
-      if (e != hipSuccess) return launched(e);
-      off += outs[i];
-    }
-    return QLORA_OK;
+    DecodeProj proj[kMaxProj];
+    for (int i = 0; i < n; ++i)
+      proj[i] = DecodeProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, A[i], B[i], outs[i]};
+    return launched(launch_decode_fwd(n, proj, in, X, T, r, scale, Y, N, s));
   }
 
   const int64_t rp = padded_rank(r);
