@@ -6,6 +6,8 @@
 // so products with them carry ~16 bits of the fp32 value; all accumulation is
 // fp32.  Also the zero-padding / transposition of the small LoRA matrices
 // into the layouts the GEMM's extra K-steps read.
+#include <type_traits>
+
 #include "common.hpp"
 #include "nf4_format.hpp"
 
@@ -48,6 +50,7 @@ __device__ __forceinline__ u32x4 keep_bf16x8(u32x4 v, uint32_t b) {
 // ---------------------------------------------------------------------------
 constexpr int kDownTok = 128;   // tokens per workgroup
 constexpr int kDownRanks = 64;  // ranks per workgroup
+constexpr uint32_t kDownPastEnd = 0x80000000u;  // past every buffer (all < 2^31 bytes)
 constexpr int kDownBufWord3 = 0x00020000;
 
 namespace {
@@ -100,8 +103,10 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
     const int id = tid + 256 * i, row = id >> 3, q = id & 7;
     poff[i] = static_cast<uint32_t>((row * K + q * 8) * 2);
   }
-  u32x4 xv[4], pv[2];
-  uint32_t kb[4];
+  // two register sets (steps alternate): two steps' loads in flight while a
+  // third is computed
+  u32x4 xv[2][4], pv[2][2];
+  uint32_t kb[2][4];
   // keep bytes of this workgroup's token rows (rows past T read zero)
   const uint64_t kbytes = kMask ? static_cast<uint64_t>(T > t0 ? T - t0 : 0) * ldk : 0;
   const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
@@ -113,32 +118,37 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
     const int id = tid + 256 * i, row = id >> 3, q = id & 7;
     koff[i] = static_cast<uint32_t>(row * ldk + q);
   }
-  auto load = [&](int st) {
-    const int so = static_cast<int>((kbeg + 64 * static_cast<int64_t>(st)) * 2);
+  // Steps past the chunk (the loop runs an even number) read zeros through
+  // past-the-end offsets and add nothing.
+  auto load = [&](int st, auto setc) {
+    constexpr int S = decltype(setc)::value;
+    const uint32_t pe = st < nsteps ? 0u : kDownPastEnd;  // uniform
+    const int so = static_cast<int>((kbeg + 64 * static_cast<int64_t>(st < nsteps ? st : 0)) * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xoff[i], so, 0));
+      xv[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xoff[i] | pe, so, 0));
     if constexpr (kMask) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        kb[i] = __builtin_amdgcn_raw_buffer_load_b8(rs_k, koff[i], static_cast<int>(so / 16), 0);
+        kb[S][i] = __builtin_amdgcn_raw_buffer_load_b8(rs_k, koff[i] | pe, static_cast<int>(so / 16), 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, poff[i], so, 0));
+      pv[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, poff[i] | pe, so, 0));
   };
-  auto store = [&](int b) {
+  auto store = [&](int b, auto setc) {
+    constexpr int S = decltype(setc)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int id = tid + 256 * i, row = id >> 3, q = id & 7;
-      u32x4 v = xv[i];
-      if constexpr (kMask) v = keep_bf16x8(v, kb[i]);
+      u32x4 v = xv[S][i];
+      if constexpr (kMask) v = keep_bf16x8(v, kb[S][i]);
       *reinterpret_cast<u32x4*>(&s_x[b][row * 64 + down_swz(row, q) * 8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int id = tid + 256 * i, row = id >> 3, q = id & 7;
-      *reinterpret_cast<u32x4*>(&s_p[b][row * 64 + down_swz(row, q) * 8]) = pv[i];
+      *reinterpret_cast<u32x4*>(&s_p[b][row * 64 + down_swz(row, q) * 8]) = pv[S][i];
     }
   };
   auto frag = [&](const uint16_t* base, int row, int chunk) {
@@ -151,18 +161,20 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
 
-  if (nsteps > 0) {
-    load(0);
-    store(0);
-    if (nsteps > 1) load(1);
-  }
-  for (int st = 0; st < nsteps; ++st) {
-    const int b = st & 1;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  load(0, I0{});
+  store(0, I0{});
+  load(1, I1{});
+  load(2, I0{});
+  // step st: stage st % 2 holds step st; register set (st + 1) % 2 holds
+  // step st + 1, goes to the other stage and is reloaded with step st + 3
+  auto body = [&](int st, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    using Next = std::integral_constant<int, b ^ 1>;
     __syncthreads();  // stage b complete, stage b ^ 1 free
-    if (st + 1 < nsteps) {
-      store(b ^ 1);
-      if (st + 2 < nsteps) load(st + 2);
-    }
+    store(b ^ 1, Next{});
+    load(st + 3, Next{});
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int chunk = 2 * j + h;
@@ -171,6 +183,12 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
       for (int c = 0; c < 2; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp, frag(s_x[b], wm * 64 + c * 32 + r32, chunk), acc[c], 0, 0, 0);
     }
+  };
+  int sbeg = 0;
+  __asm__ volatile("" : "+s"(sbeg));  // opaque start: no differently ordered peeled first pass
+  for (int st = sbeg; st < nsteps; st += 2) {
+    body(st, I0{});
+    body(st + 1, I1{});
   }
   // D[rank][token]: lane holds token r32 of tile c, ranks 8 (e/4) + 4 h + e%4
 #pragma unroll
@@ -358,23 +376,29 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
   // Q staging items: column group cg (8 columns), token pairs tp and tp + 16
   const int cg = tid & 15, tp0 = tid >> 4;
   const bool col_ok = c0 + 8 * cg < C;
-  u32x4 qv[4];
-  uint32_t kb[4];
-  u32x4 pv[2 * JT];
+  // two register sets: the loads of step e go to set e % 2, so two steps'
+  // loads are in flight while a third is computed
+  u32x4 qv[2][4];
+  uint32_t kb[2][4];
+  u32x4 pv[2][2 * JT];
   const uint64_t kbytes = kMask ? static_cast<uint64_t>(T - ts) * ldk : 0;
   const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(kMask ? keep + ts * ldk : keep), 0,
       static_cast<int>(kbytes < 0x7fffffffu ? kbytes : 0x7fffffffu), kBufferWord3);
-  auto load = [&](int step) {
+  // Every step issues its loads unconditionally; a step past the slice
+  // (the loop runs an even number of steps) reads zeros and adds nothing.
+  auto load = [&](int step, auto setc) {
+    constexpr int S = decltype(setc)::value;
+    const uint32_t pe = step < nsteps ? 0u : kPastEnd;  // uniform
     const int64_t t0 = ts + 64 * static_cast<int64_t>(step);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t t = t0 - ts + 2 * (tp0 + 16 * (i >> 1)) + (i & 1);  // rows past T read as zero
-      const uint32_t off = col_ok ? static_cast<uint32_t>((t * ldq + c0 + 8 * cg) * 2) : kPastEnd;
-      qv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_q, off, 0, 0));
+      const uint32_t off = col_ok ? static_cast<uint32_t>((t * ldq + c0 + 8 * cg) * 2) | pe : kPastEnd;
+      qv[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_q, off, 0, 0));
       if constexpr (kMask) {
-        const uint32_t koff = col_ok ? static_cast<uint32_t>(t * ldk + (c0 + 8 * cg) / 8) : kPastEnd;
-        kb[i] = __builtin_amdgcn_raw_buffer_load_b8(rs_k, koff, 0, 0);
+        const uint32_t koff = col_ok ? static_cast<uint32_t>(t * ldk + (c0 + 8 * cg) / 8) | pe : kPastEnd;
+        kb[S][i] = __builtin_amdgcn_raw_buffer_load_b8(rs_k, koff, 0, 0);
       }
     }
 #pragma unroll
@@ -382,18 +406,19 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
       const int id = tid + 256 * i, prow = id >> 3, q = id & 7;
       const int64_t grow = prow < 32 * JT ? j0 + prow : rp + j0 + (prow - 32 * JT);
       const int64_t tk = t0 + 8 * q;  // tokens in [T, ldt) are zero in Pt
-      const uint32_t off = tk < ldt ? static_cast<uint32_t>((grow * ldt + tk) * 2) : kPastEnd;
-      pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, off, 0, 0));
+      const uint32_t off = tk < ldt ? static_cast<uint32_t>((grow * ldt + tk) * 2) | pe : kPastEnd;
+      pv[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, off, 0, 0));
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, auto setc) {
+    constexpr int S = decltype(setc)::value;
     if constexpr (kMask) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qv[i] = keep_bf16x8(qv[i], kb[i]);
+      for (int i = 0; i < 4; ++i) qv[S][i] = keep_bf16x8(qv[S][i], kb[S][i]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const u32x4 a = qv[2 * i], b = qv[2 * i + 1];
+      const u32x4 a = qv[S][2 * i], b = qv[S][2 * i + 1];
       const int w = tp0 + 16 * i;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -404,7 +429,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 2 * JT; ++i) {
       const int id = tid + 256 * i, prow = id >> 3, q = id & 7;
-      *reinterpret_cast<u32x4*>(&s_p[buf][kGradPitch * prow + 4 * q]) = pv[i];
+      *reinterpret_cast<u32x4*>(&s_p[buf][kGradPitch * prow + 4 * q]) = pv[S][i];
     }
   };
 
@@ -414,19 +439,21 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[jt][e] = 0.f;
 
-  if (nsteps > 0) {
-    load(0);
-    store(0);
-    if (nsteps > 1) load(1);
-  }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  load(0, I0{});
+  store(0, I0{});
+  load(1, I1{});
+  load(2, I0{});
   const int c = 32 * wv + r32;
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
+  // step e: stage e % 2 holds step e; registers of set (e + 1) % 2 hold step
+  // e + 1, are stored to the other stage and then reloaded with step e + 3
+  auto body = [&](int step, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    using Next = std::integral_constant<int, buf ^ 1>;
     __syncthreads();  // stage buf complete, stage buf ^ 1 free
-    if (step + 1 < nsteps) {
-      store(buf ^ 1);
-      if (step + 2 < nsteps) load(step + 2);
-    }
+    store(buf ^ 1, Next{});
+    load(step + 3, Next{});
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int w0 = 8 * s4 + 4 * h;
@@ -444,6 +471,12 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
         }
       }
     }
+  };
+  int sbeg = 0;
+  __asm__ volatile("" : "+s"(sbeg));  // opaque start: no differently ordered peeled first pass
+  for (int step = sbeg; step < nsteps; step += 2) {
+    body(step, I0{});
+    body(step + 1, I1{});
   }
   if constexpr (kJC) {
     // D[j][c]: lane holds column c, rows j = 8*(e/4) + 4*h + e%4
