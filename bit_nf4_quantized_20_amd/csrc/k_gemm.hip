@@ -616,17 +616,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   };
 
   const int64_t s0 = p.K0 / kBK, s1 = p.K1 / kBK;
-  // LoRA extension segment (a few steps): copy, barrier, compute
+  // LoRA extension segment (a few steps): two steps copied into the two
+  // stages at once, one barrier, then both computed
   auto lora_seg = [&]() {
     if (s1 <= 0) return;
     DtlTile<BM, NW> ta1;
     DtlTile<BN, NW> tw1;
     ta1.init(p.nseg > 0 ? seg_of(p, n0).act1 : p.act1, p.lda1, m0, p.M, wv, lane);
     tw1.init(p.wt1, p.ldw1, n0, p.N, wv, lane);
-    for (int64_t e = 0; e < s1; ++e) {
-      __syncthreads();  // every wave is done reading stage 0
+    for (int64_t e = 0; e < s1; e += 2) {
+      const bool two = e + 1 < s1;
+      __syncthreads();  // every wave is done reading both stages
       ta1.load(s_act0, wv, e * kBK);
       tw1.load(s_wt0, wv, e * kBK);
+      if (two) {
+        ta1.load(s_act1, wv, (e + 1) * kBK);
+        tw1.load(s_wt1, wv, (e + 1) * kBK);
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
 #pragma unroll
@@ -634,6 +640,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
         Frags f;
         read_frags(f, s_wt0, s_act0, j);
         mfmas(f);
+      }
+      if (two) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Frags f;
+          read_frags(f, s_wt1, s_act1, j);
+          mfmas(f);
+        }
       }
     }
   };
