@@ -574,6 +574,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       };
       copy(e + 1, na, nw);
       wfetch(wr[C], e + 3);
+      __builtin_amdgcn_s_setprio(1);  // the MFMA phase issues ahead of the other wave's loads
       if constexpr (kRegW) tab = TW::table(nxt);
       part(0);
       read_frags(f1, sw, sa, 1);
@@ -590,6 +591,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       part(3);
       mfmas(f1);
       interleave();
+      __builtin_amdgcn_s_setprio(0);
       // stage B^1 complete and stage B free: wait for this wave's copies and
       // LDS writes (the code loads issued after the copies, 3 instructions,
       // may stay in flight), then the barrier
