@@ -441,6 +441,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
 
   if (dq_wave) {
     // ------------------------------------------------ dequantize waves
+    // the vector-ALU-bound waves issue ahead of the U wave on their SIMD
+    __builtin_amdgcn_s_setprio(1);
     u32x4* tc = s_codes[qtr];
     CodeStage cs[2];
     // Per-lane offsets of the code rows and absmax bytes.  With whole
@@ -579,6 +581,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
   }
 
   // ---------------- epilogue: waves 0-3 hold D[row][token], 4-7 D[rank][token]
+  __builtin_amdgcn_s_setprio(0);
   s_acc[wv][lane] = acc;
   if (tid < kRows * 16) s_b[tid >> 4][tid & 15] = __builtin_bit_cast(float, braw << 16);
   __syncthreads();
