@@ -673,23 +673,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   }
   if (p.keep == nullptr) lora_seg();
 
-  // epilogue: D[n][m] -> C[m][n]; lane holds m = r32, n = 8*(e/4) + 4*half + e%4
+  // Epilogue: D[n][m] -> C[m][n].  A lane holds m = r32 and four
+  // consecutive n per (a, c, g): written straight out, every store
+  // instruction would put 32 rows' 16-byte pieces into flight.  Instead each
+  // wave parks its 128 x 64 bf16 block in LDS (16 KB, rows of eight 16-byte
+  // pieces, piece k of row r at slot k ^ (r % 8)) and stores it back eight
+  // whole 128-byte rows per instruction.
+  __syncthreads();  // every wave is done reading the stages
+  uint16_t* const s_c = (wv < 2 ? s_act0 : wv < 4 ? s_act1 : wv < 6 ? s_wt0 : s_wt1) + (wv & 1) * (WM * WN);
 #pragma unroll
   for (int c = 0; c < FM; ++c) {
-    const int64_t m = m0 + wm * WM + c * 32 + r32;
-    if (m >= p.M) continue;
+    const int row = c * 32 + r32;
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * WN + a * 32 + 8 * g + 4 * half;
-        if (n < p.N) {
-          const uint32_t p0 = pack_bf16x2(acc[a][c][4 * g + 0], acc[a][c][4 * g + 1]);
-          const uint32_t p1 = pack_bf16x2(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(p.C + m * p.ldc + n) = u32x2{p0, p1};
-        }
+        const uint32_t p0 = pack_bf16x2(acc[a][c][4 * g + 0], acc[a][c][4 * g + 1]);
+        const uint32_t p1 = pack_bf16x2(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
+        const int piece = 4 * a + g;
+        *reinterpret_cast<u32x2*>(s_c + row * WN + ((piece ^ (row & 7)) * 8) + 4 * half) = u32x2{p0, p1};
       }
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's block is in LDS
+#pragma unroll
+  for (int i = 0; i < WM / 8; ++i) {
+    const int row = 8 * i + (lane >> 3), piece = lane & 7;
+    const int64_t m = m0 + wm * WM + row;
+    const int64_t n = n0 + wn * WN + 8 * piece;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s_c + row * WN + ((piece ^ (row & 7)) * 8));
+    if (m < p.M && n < p.N) *reinterpret_cast<u32x4*>(p.C + m * p.ldc + n) = v;
   }
 }
 
