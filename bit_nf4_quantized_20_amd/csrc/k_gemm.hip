@@ -702,7 +702,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
     const int64_t m = m0 + wm * WM + row;
     const int64_t n = n0 + wn * WN + 8 * piece;
     const u32x4 v = *reinterpret_cast<const u32x4*>(s_c + row * WN + ((piece ^ (row & 7)) * 8));
-    if (m < p.M && n < p.N) *reinterpret_cast<u32x4*>(p.C + m * p.ldc + n) = v;
+    if (m < p.M && n < p.N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.C + m * p.ldc + n));
   }
 }
 
