@@ -267,6 +267,9 @@ def main():
     # ------------------------------------------- q|k|v at decode sizes
     extra["qkv8b_decode"] = qkv_decode_leg(q, synth, dev, bf)
 
+    # ------------------------------ MLP-sized weights at decode sizes
+    extra["mlp_weights_decode"] = mlp_decode_leg(q, synth, dev, bf)
+
     # ------------------------------------------- large-token fwd + bwd
     if not args.no_train:
         extra["mlp8b_fwd_bwd"] = train_leg(q, synth, dev, bf)
@@ -358,6 +361,58 @@ def qkv_decode_leg(q, synth, dev, bf, P=24, n=192):
         res[f"T{T}"] = {"multi_us": round(us_m, 2), "three_calls_us": round(us_s, 2),
                         "multi_GB_per_s": round(nbytes / (us_m * 1e-6) / 1e9, 1),
                         "algorithmic_bytes": nbytes}
+    return res
+
+
+def mlp_decode_leg(q, synth, dev, bf, n=96):
+    """The small-token forward on the MLP weights of the 8B and 70B shapes
+    (8B gate 14336 x 4096 and down 4096 x 14336, 70B gate 28672 x 8192; their
+    r = 64 and alpha) at T = 1 and T = 16: how close the weight stream comes
+    to the HBM peak once the weight, not the launch, dominates.  Graph replay
+    of n back-to-back calls cycling through copies of the weight that together
+    exceed the 256 MB last-level cache; microseconds per call."""
+    import torch
+    cases = [(3, 0, "8b_gate"), (3, 2, "8b_down"), (5, 0, "70b_gate")]
+    res = {}
+    for wid, pi, name in cases:
+        wl = synth.WORKLOADS[wid]
+        p = wl.projections[pi]
+        n_out, n_in, r, alpha = p.out_features, p.in_features, wl.r, wl.alpha
+        w = torch.from_numpy(synth.weight(wid, pi, n_out, n_in)).to(dev)
+        W0 = q.nf4_quantize_weight(w)
+        del w
+        copies = max(2, -(-320 * 2**20 // int(n_out * n_in * NF4_BYTES_PER_WEIGHT)))
+        pool = [W0] + [q.NF4Weight(W0.codes.clone(), W0.absmax_q.clone(), W0.absmax_scale.clone(),
+                                   W0.rows, W0.cols) for _ in range(copies - 1)]
+        A = bf(synth.lora_A(wid, pi, r, n_in))
+        B = bf(synth.lora_B(wid, pi, n_out, r))
+        entry = {"out": n_out, "in": n_in, "r": r, "copies": copies}
+        for T in (1, 16):
+            X = bf(synth.activations(wid, pi, T, n_in))
+            Y = torch.empty(T, n_out, dtype=torch.bfloat16, device=dev)
+            for i in range(copies):
+                q.qlora_linear_fwd(pool[i], X, A, B, r, alpha, Y=Y)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    q.qlora_linear_fwd(pool[i % copies], X, A, B, r, alpha, Y=Y)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            nbytes = decode_call_bytes(n_out, n_in, T, r)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            entry[f"T{T}"] = {"us_per_call": round(us, 2), "GB_per_s": round(gbs, 1),
+                              "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 3)}
+            del g
+        res[name] = entry
+        del pool, W0
+        torch.cuda.empty_cache()
     return res
 
 

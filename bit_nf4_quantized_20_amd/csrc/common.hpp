@@ -138,9 +138,14 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* absmax_q, const flo
                         int64_t out, int64_t in, const uint16_t* Bp, const uint16_t* Atp,
                         int64_t ldp, int64_t rp, float s, uint16_t* w_out, hipStream_t st);
 
-// Fused small-token forward (T <= 16, r <= 64): Y = X W_hat^T + s (X A^T) B^T
-// in one launch, no workspace.  decode_fits() lists the shapes it takes.
+// Small-token forward (T <= 16, r <= 64): Y = X W_hat^T + s (X A^T) B^T.
+// decode_fits() lists the shapes it takes.  For r <= 16 and at most
+// kDecodeFusedMaxWgs workgroups (16 output rows each) it is one launch with
+// no workspace, every workgroup computing U = X A^T itself; otherwise
+// (decode_pre_u) U is computed once into a workspace of decode_u_bytes()
+// first, which saves each workgroup reading all of A.
 constexpr int64_t kDecodeMaxT = 16;
+constexpr int64_t kDecodeFusedMaxWgs = 512;
 constexpr int64_t kDecodeMaxRank = 64;
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
 // One projection of the small-token forward: its NF4 weight [out][in] and
@@ -159,9 +164,12 @@ struct DecodeSet {
   uint16_t* Y;
   int n;
 };
+bool decode_pre_u(int n, const int64_t* outs, int64_t r);
+inline size_t decode_u_bytes(int n, int64_t T, int64_t r) { return static_cast<size_t>(n * T * r * 4); }
 // n (1..kMaxProj) projections sharing X, outputs side by side in Y [T][ldy]
-// (projection i from column sum_{j<i} out_j); one launch for r <= 16.
+// (projection i from column sum_{j<i} out_j), all in one launch (two with
+// decode_pre_u, which needs u_ws of decode_u_bytes(n, T, r)).
 hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const uint16_t* X, int64_t T,
-                             int64_t r, float s, uint16_t* Y, int64_t ldy, hipStream_t st);
+                             int64_t r, float s, uint16_t* Y, int64_t ldy, float* u_ws, hipStream_t st);
 
 }  // namespace qlora

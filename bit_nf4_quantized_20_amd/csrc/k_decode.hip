@@ -68,259 +68,6 @@ struct CodeStage {
 };
 }  // namespace
 
-template <int RT>  // rank tiles of 16 (r <= 16 * RT)
-__global__ __launch_bounds__(kThreads) void k_decode_fwd(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
-    const float* __restrict__ scale, int64_t in, const uint16_t* __restrict__ X, int T,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
-    uint16_t* __restrict__ Y, int64_t out, int64_t ldy) {
-  // staging tiles during the main loop; reused for the epilogue afterwards
-  __shared__ u32x4 s_tiles[kWaves][2][kTileSlots];
-  __shared__ u32x4 s_codes[kWaves][kCodeSlots];
-  __shared__ float s_b[kRows][RT * 16 + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  // wave index as a scalar: everything derived from it (the wave's block
-  // range, chunk count, partial-chunk test) stays in scalar registers and
-  // branches
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const int half = lane >> 5, piece = lane & 31;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
-  const int64_t nb = in / 64;  // blocks per row
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-
-  const int bw0 = static_cast<int>(nb * wv / kWaves), bw1 = static_cast<int>(nb * (wv + 1) / kWaves);
-  const int nch = (bw1 - bw0 + 3) / 4;
-  const uint32_t row = static_cast<uint32_t>(r0) + n;
-  const uint32_t inu = static_cast<uint32_t>(in), nbu = static_cast<uint32_t>(nb);
-  const int xpairs = (T + 1) / 2;
-
-  // Buffer resources: a load whose offset lies past the end returns zeros
-  // without a branch.  This zero-fills token rows >= T, rank rows >= r and
-  // block indices past the last row (sizes are checked on the host to fit
-  // 32-bit offsets).
-  const uint32_t wbytes = static_cast<uint32_t>(static_cast<uint64_t>(out) * in / 2);
-  const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(codes), 0, static_cast<int>(wbytes), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(absmax_q), 0, static_cast<int>(wbytes / 32), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(scale), 0, static_cast<int>((wbytes + 8191) / 8192 * 4), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(X), 0, static_cast<int>(static_cast<uint32_t>(T) * inu * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(r) * inu * 2), kBufferWord3);
-
-  // B rows of this workgroup: raw bits loaded now (nothing waits for them),
-  // converted and written to LDS in the epilogue
-  constexpr int kBPer = (kRows * RT * 16 + kThreads - 1) / kThreads;
-  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(out) * r * 2), kBufferWord3);
-  uint32_t braw[kBPer];
-#pragma unroll
-  for (int e = 0; e < kBPer; ++e) {
-    const int idx = tid + e * kThreads;
-    const int rr = idx / (RT * 16), j = idx % (RT * 16);
-    const uint32_t off = (rr < kRows && j < r) ? ((static_cast<uint32_t>(r0) + rr) * r + j) * 2 : kPastEnd;
-    braw[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
-  }
-
-  // The chunk's codes (16 rows x 128 B) are loaded contiguously, eight rows
-  // per instruction: lane l takes piece l%8 of row l/8 (c0) and of row
-  // 8 + l/8 (c1); the chunk routine moves them to their owners through LDS.
-  // Blocks past the wave's range read a neighbouring block (or zeros past
-  // the end): finite values that meet zero activations.
-  auto load_codes = [&](CodeStage& cs, int c) {
-    const uint32_t base = static_cast<uint32_t>(bw0 + 4 * c) * 32 + 16 * (lane & 7);
-    const uint32_t rl = static_cast<uint32_t>(r0) + (lane >> 3);
-    cs.c0 = __builtin_bit_cast(u32x4,
-                               __builtin_amdgcn_raw_buffer_load_b128(rs_codes, rl * (inu / 2) + base, 0, kStream));
-    cs.c1 = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_codes, (rl + 8) * (inu / 2) + base, 0, kStream));
-    const uint32_t blk = static_cast<uint32_t>(bw0 + 4 * c + g);
-    const uint32_t bi = row * nbu + blk;
-    cs.q = __builtin_amdgcn_raw_buffer_load_b8(rs_q, bi, 0, 0);
-    cs.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (bi >> 8) * 4, 0, 0));
-  };
-  // Rows 2i + l/32 (first row `row0`) of a chunk (256 k), piece (l%32) ^ row:
-  // contiguous 512 B per row.  Pieces past the wave's block range (only in
-  // its last chunk) are redirected past the end and read as zero.
-  // Only the npairs instructions that hold existing rows are issued: the
-  // address unit spends the same time on a lane whether or not it is in
-  // range.
-  auto load_rows = [&](u32x4 (&reg)[8], const __amdgpu_buffer_rsrc_t& rs, uint32_t row0, int npairs,
-                       int c) {
-    const uint32_t k0 = static_cast<uint32_t>(bw0 + 4 * c) * 64;
-    const int kvalid = (bw1 - bw0 - 4 * c) * 64;
-    if (kvalid >= 256) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i >= npairs) break;
-        const int t = 2 * i + half, p = piece ^ t;
-        const uint32_t off = ((row0 + t) * inu + k0 + 8 * p) * 2;
-        reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i >= npairs) break;
-        const int t = 2 * i + half, p = piece ^ t;
-        const uint32_t off = 8 * p < kvalid ? ((row0 + t) * inu + k0 + 8 * p) * 2 : kPastEnd;
-        reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-      }
-    }
-  };
-  auto a_pairs = [&](int rt) {
-    const int rows = r - 16 * rt;
-    return rows >= 16 ? 8 : (rows + 1) / 2;
-  };
-  auto load_x = [&](u32x4 (&reg)[8], int c) { load_rows(reg, rs_x, 0, xpairs, c); };
-  auto load_a = [&](u32x4 (&reg)[8], int c, int rt) { load_rows(reg, rs_a, 16 * rt, a_pairs(rt), c); };
-
-  u32x4* tx = s_tiles[wv][0];
-  u32x4* ta = s_tiles[wv][1];
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 au[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // A tile from registers; rows of ranks >= r are zero
-  auto write_a = [&](const u32x4 (&a)[8], int ap) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < ap) ta[64 * i + lane] = a[i];
-      else ta[64 * i + lane] = zero4;
-    }
-  };
-
-  // One chunk from registers: xr holds X(c), a0 holds A(c, tile 0).  Tiles
-  // 1.. of A are loaded here into a1 / a0 in turn (r > 16 only).
-  auto chunk = [&](int c, const CodeStage& cs, const u32x4 (&xr)[8], u32x4 (&a0)[8],
-                   u32x4 (&a1)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < xpairs) tx[64 * i + lane] = xr[i];
-    write_a(a0, a_pairs(0));
-    if constexpr (RT > 1) load_a(a1, c, 1);
-    // codes to their owners: row n, block g = pieces 2g, 2g + 1.  Piece p
-    // of row m sits at slot 8m + (p ^ ((m >> 1) & 7)), so the owners' reads
-    // of 16 rows fall on 16 distinct 4-bank groups.
-    u32x4* tc = s_codes[wv];
-    {
-      const int m = lane >> 3, pc = lane & 7;
-      tc[8 * m + (pc ^ ((m >> 1) & 7))] = cs.c0;
-      tc[8 * (m + 8) + (pc ^ (((m + 8) >> 1) & 7))] = cs.c1;
-    }
-    const u32x4 cc0 = tc[8 * n + ((2 * g) ^ ((n >> 1) & 7))];
-    const u32x4 cc1 = tc[8 * n + ((2 * g + 1) ^ ((n >> 1) & 7))];
-    // base product
-    const Nf4Table tab = make_table(dq_absmax(cs.q, cs.sc));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
-      const uint32_t cw = j < 4 ? cc0[j] : cc1[j - 4];
-      uint32_t w[4];
-      lookup8(tab, cw, w);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
-                                                    as_bf16x8(xf), acc, 0, 0, 0);
-    }
-    // this wave's share of U, rank tile by rank tile through the A tile
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (rt > 0) {
-        u32x4 (&cur)[8] = (rt & 1) ? a1 : a0;
-        u32x4 (&nxt)[8] = (rt & 1) ? a0 : a1;
-        write_a(cur, a_pairs(rt));
-        if (rt + 1 < RT) load_a(nxt, c, rt + 1);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4 xf = tx[tile_slot(n, 8 * g + j)];
-        const u32x4 af = ta[tile_slot(n, 8 * g + j)];
-        au[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), au[rt], 0, 0,
-                                                         0);
-      }
-    }
-  };
-
-  // For r <= 16, two register sets by chunk parity: codes, X and A of chunk
-  // c + 2 are loaded as soon as chunk c has been computed, so two chunks'
-  // loads are always in flight.  Larger ranks need the registers for their
-  // further A tiles and keep one chunk in flight.
-  CodeStage cs0, cs1;
-  u32x4 x0[8], x1[8], p0[8], p1[8], q0[8];
-  // activations and A first: their L2 round trip then overlaps the codes'
-  // longer HBM one
-  auto load_all = [&](CodeStage& cs, u32x4 (&xr)[8], u32x4 (&a)[8], int c) {
-    load_x(xr, c);
-    load_a(a, c, 0);
-    load_codes(cs, c);
-  };
-  // token rows of the X tile that no chunk writes (>= 2 * xpairs) stay zero
-#pragma unroll
-  for (int i = 0; i < 8; ++i) tx[64 * i + lane] = zero4;
-  if constexpr (RT == 1) {
-    if (nch > 0) load_all(cs0, x0, p0, 0);
-    if (nch > 1) load_all(cs1, x1, p1, 1);
-    for (int c = 0; c < nch; c += 2) {
-      chunk(c, cs0, x0, p0, q0);
-      if (c + 2 < nch) load_all(cs0, x0, p0, c + 2);
-      if (c + 1 < nch) {
-        chunk(c + 1, cs1, x1, p1, q0);
-        if (c + 3 < nch) load_all(cs1, x1, p1, c + 3);
-      }
-    }
-  } else {
-    for (int c = 0; c < nch; ++c) {
-      load_all(cs0, x0, p0, c);
-      chunk(c, cs0, x0, p0, q0);
-    }
-  }
-
-  // ---------------- epilogue (tiles reused): per-wave accumulators
-  __syncthreads();
-  f32x4* s_acc = reinterpret_cast<f32x4*>(&s_tiles[0][0][0]);  // [wave][1 + RT][64]
-  s_acc[(wv * (1 + RT)) * 64 + lane] = acc;                     // D[row 4g+i][token n]
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) s_acc[(wv * (1 + RT) + 1 + rt) * 64 + lane] = au[rt];  // D[rank][token]
-#pragma unroll
-  for (int e = 0; e < kBPer; ++e) {
-    const int idx = tid + e * kThreads;
-    if (idx < kRows * RT * 16)
-      s_b[idx / (RT * 16)][idx % (RT * 16)] = __builtin_bit_cast(float, braw[e] << 16);
-  }
-  __syncthreads();
-  // U [t][j] summed over the waves, placed after the accumulators
-  float* s_u = reinterpret_cast<float*>(s_acc + kWaves * (1 + RT) * 64);  // [16][RT*16 + 1]
-  constexpr int kUP = RT * 16 + 1;
-  for (int idx = tid; idx < 16 * RT * 16; idx += kThreads) {
-    const int t = idx / (RT * 16), j = idx % (RT * 16);
-    const int rt = j >> 4, m = j & 15;  // lane 16 (m/4) + t, element m % 4
-    float u = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) u += s_acc[(w * (1 + RT) + 1 + rt) * 64 + 16 * (m >> 2) + t][m & 3];
-    s_u[t * kUP + j] = u;
-  }
-  __syncthreads();
-  // T x 16 outputs, two adjacent rows per thread
-  if (tid < T * (kRows / 2)) {
-    const int t = tid / (kRows / 2), rr = 2 * (tid % (kRows / 2));
-    float y[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int m = rr + e;
-      float base = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) base += s_acc[(w * (1 + RT)) * 64 + 16 * (m >> 2) + t][m & 3];
-      float lora = 0.f;
-      for (int j = 0; j < r; ++j) lora += s_u[t * kUP + j] * s_b[m][j];
-      y[e] = base + s * lora;
-    }
-    *reinterpret_cast<uint32_t*>(Y + static_cast<int64_t>(t) * ldy + r0 + rr) = pack_bf16x2(y[0], y[1]);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // r <= 16: the same decomposition with the two kinds of work on different
 // waves.  Waves 0-3 stream codes and run the dequantize + base MFMA (vector
@@ -353,10 +100,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd(
 // Several projections that share X (q|k|v) run as one launch: workgroups
 // [wg0[p], wg0[p + 1]) take projection p's rows, written to columns
 // [col0[p], col0[p] + out[p]) of Y.
-template <int XP, int NS, bool kFull>
+// kPreU: U = X A^T of every projection was computed beforehand
+// (k_decode_u, fp32 [n][T][r] at Upre, r <= 64): the U waves then only
+// stage X, and no workgroup reads A.  Otherwise r <= 16 and each workgroup
+// computes U itself.
+template <int XP, int NS, bool kFull, bool kPreU>
 __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int64_t in,
                                                                const uint16_t* __restrict__ X, int T, int r,
-                                                               float s, int64_t ldy) {
+                                                               float s, int64_t ldy,
+                                                               const float* __restrict__ Upre) {
   // this workgroup's projection (uniform)
   int pj = 0;
 #pragma unroll
@@ -374,9 +126,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
   __shared__ u32x4 s_x[kPairs][2][kPadSlots];    // X tiles by chunk parity
   __shared__ u32x4 s_a[kPairs][kPadSlots];       // A tile of each U wave
   __shared__ u32x4 s_codes[kPairs][kCodeSlots];  // codes of each dequantize wave
-  __shared__ f32x4 s_acc[kWaves][64];
-  __shared__ float s_b[kRows][17];
-  __shared__ float s_u[16][17];
+  // The epilogue's arrays reuse the X tiles' memory once the chunk steps
+  // are done, which keeps the kPreU kernel under half the CU's LDS (two
+  // workgroups per CU).
+  constexpr int kRU = kPreU ? 64 : 16;  // ranks held by the epilogue
+  static_assert(sizeof(f32x4) * kWaves * 64 + sizeof(float) * (kRows + 16) * (kRU + 1) <= sizeof(s_x));
+  f32x4(*s_acc)[64] = reinterpret_cast<f32x4(*)[64]>(&s_x[0][0][0]);
+  float(*s_b)[kRU + 1] = reinterpret_cast<float(*)[kRU + 1]>(&s_acc[kWaves][0]);
+  float(*s_u)[kRU + 1] = s_b + kRows;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar wave index
@@ -399,14 +156,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(out) * r * 2), kBufferWord3);
 
-  // B rows of this workgroup (16 x r <= 256 values), converted in the
-  // epilogue; every thread loads (past the end for tid >= 256), so no branch
-  // makes the compiler wait for this load before the main loop
-  uint32_t braw;
-  {
-    const int rr = tid >> 4, j = tid & 15;
+  // B rows of this workgroup (16 x kRU values, ranks >= r zero), converted
+  // in the epilogue; every thread loads (past the end where there is no
+  // value), so no branch makes the compiler wait for this load before the
+  // main loop
+  constexpr int kBLoads = kRows * kRU / kThreads > 0 ? kRows * kRU / kThreads : 1;
+  uint32_t braw[kBLoads];
+#pragma unroll
+  for (int i = 0; i < kBLoads; ++i) {
+    const int idx = tid + kThreads * i, rr = idx / kRU, j = idx % kRU;
     const uint32_t off = (rr < kRows && j < r) ? ((static_cast<uint32_t>(r0) + rr) * r + j) * 2 : kPastEnd;
-    braw = __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
+    braw[i] = __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -560,12 +320,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
       if (c >= 0) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) tx[wslot + 2 * kPitch * i] = xs[kD][i];
+        if constexpr (!kPreU) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ta[wslot + 2 * kPitch * i] = as[kD][i];
+          for (int i = 0; i < 8; ++i) ta[wslot + 2 * kPitch * i] = as[kD][i];
+        }
       }
       load_rows(xs[kD], X, xbytes, std::integral_constant<int, XP>{}, c + 2);
-      load_rows(as[kD], A, abytes, std::integral_constant<int, 8>{}, c + 2);  // ranks >= r read zeros
-      if (c >= 0) {
+      if constexpr (!kPreU)
+        load_rows(as[kD], A, abytes, std::integral_constant<int, 8>{}, c + 2);  // ranks >= r read zeros
+      if constexpr (kPreU) {
+        if (c >= 0) __syncthreads();  // X(c) is in tx for the partner
+      } else if (c >= 0) {
         __syncthreads();  // X(c) is in tx for the partner
         const u32x4* fx = tx + kPitch * n + 8 * g;
         const u32x4* fa = ta + kPitch * n + 8 * g;
@@ -582,24 +347,37 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
 
   // ---------------- epilogue: waves 0-3 hold D[row][token], 4-7 D[rank][token]
   __builtin_amdgcn_s_setprio(0);
+  __syncthreads();  // every wave is done with the X tiles
   s_acc[wv][lane] = acc;
-  if (tid < kRows * 16) s_b[tid >> 4][tid & 15] = __builtin_bit_cast(float, braw << 16);
-  __syncthreads();
-  if (tid < 256) {
-    const int t = tid >> 4, j = tid & 15;  // U[t][j]: lane 16 (j/4) + t, element j % 4
-    float u = 0.f;
 #pragma unroll
-    for (int w = kPairs; w < kWaves; ++w) u += s_acc[w][16 * (j >> 2) + t][j & 3];
-    s_u[t][j] = u;
+  for (int i = 0; i < kBLoads; ++i) {
+    const int idx = tid + kThreads * i;
+    if (idx < kRows * kRU) s_b[idx / kRU][idx % kRU] = __builtin_bit_cast(float, braw[i] << 16);
+  }
+  if constexpr (kPreU) {
+    const float* __restrict__ up = Upre + static_cast<int64_t>(pj) * T * r;
+    for (int idx = tid; idx < 16 * kRU; idx += kThreads) {
+      const int t = idx / kRU, j = idx % kRU;
+      s_u[t][j] = (t < T && j < r) ? up[t * r + j] : 0.f;
+    }
+  } else {
+    __syncthreads();
+    if (tid < 256) {
+      const int t = tid >> 4, j = tid & 15;  // U[t][j]: lane 16 (j/4) + t, element j % 4
+      float u = 0.f;
+#pragma unroll
+      for (int w = kPairs; w < kWaves; ++w) u += s_acc[w][16 * (j >> 2) + t][j & 3];
+      s_u[t][j] = u;
+    }
   }
   __syncthreads();
   // Y = base + s U B^T: four adjacent lanes per output, each summing a quarter
-  // of the 16 ranks (ranks >= r are zero in U and B)
+  // of the kRU ranks (ranks >= r are zero in U and B)
   for (int o = tid; o < T * 64; o += kThreads) {
     const int t = o >> 6, m = (o >> 2) & 15, jq = o & 3;
     float lora = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lora += s_u[t][4 * jq + i] * s_b[m][4 * jq + i];
+    for (int i = 0; i < kRU / 4; ++i) lora += s_u[t][kRU / 4 * jq + i] * s_b[m][kRU / 4 * jq + i];
     lora += __shfl_xor(lora, 1);
     lora += __shfl_xor(lora, 2);
     if (jq == 0) {
@@ -611,43 +389,95 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
   }
 }
 
+// U = X A^T for the small-token forward, computed once per call instead of
+// by every workgroup: U[p][t][k] = sum_i X[t][i] A_p[k][i] in fp32 (the
+// scale s is applied by the consumer).  One workgroup per (rank k, token t,
+// projection p); its 256 threads each take 16-byte pieces of the two rows at
+// a stride of 4 KB, then the partial sums meet in LDS.
+__global__ __launch_bounds__(256) void k_decode_u(DecodeSet P, int64_t in, const uint16_t* __restrict__ X,
+                                                  int T, int r, float* __restrict__ U) {
+  const int k = blockIdx.x, t = blockIdx.y, pj = blockIdx.z;
+  const u32x4* __restrict__ xr = reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(t) * in);
+  const u32x4* __restrict__ ar = reinterpret_cast<const u32x4*>(P.proj[pj].A + static_cast<int64_t>(k) * in);
+  const int npieces = static_cast<int>(in / 8);
+  float sum = 0.f;
+  for (int i = threadIdx.x; i < npieces; i += 256) {
+    const u32x4 xv = xr[i], av = ar[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum = fmaf(__builtin_bit_cast(float, xv[e] << 16), __builtin_bit_cast(float, av[e] << 16), sum);
+      sum = fmaf(__builtin_bit_cast(float, xv[e] & 0xffff0000u), __builtin_bit_cast(float, av[e] & 0xffff0000u), sum);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  __shared__ float s_part[4];
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    U[(static_cast<int64_t>(pj) * T + t) * r + k] = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+}
+
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r) {
   // 32-bit buffer offsets: codes and every row of X and A stay below 2^31 bytes
   return T >= 1 && T <= kDecodeMaxT && r >= 1 && r <= kDecodeMaxRank && out % kRows == 0 &&
          in % 64 == 0 && in <= (int64_t(1) << 24) && out * in < (int64_t(1) << 32);
 }
 
+bool decode_pre_u(int n, const int64_t* outs, int64_t r) {
+  int64_t rows = 0;
+  for (int i = 0; i < n; ++i) rows += outs[i];
+  return r > 16 || rows / kRows > kDecodeFusedMaxWgs;
+}
+
 hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const uint16_t* X, int64_t T,
-                             int64_t r, float s, uint16_t* Y, int64_t ldy, hipStream_t st) {
+                             int64_t r, float s, uint16_t* Y, int64_t ldy, float* u_ws, hipStream_t st) {
   if (n < 1 || n > kMaxProj) return hipErrorInvalidValue;
-  for (int i = 0; i < n; ++i)
+  int64_t outs[kMaxProj];
+  for (int i = 0; i < n; ++i) {
     if (!decode_fits(T, in, proj[i].out, r)) return hipErrorInvalidValue;
+    outs[i] = proj[i].out;
+  }
+  const bool pre_u = decode_pre_u(n, outs, r);
+  if (pre_u && u_ws == nullptr) return hipErrorInvalidValue;
   const dim3 block(kThreads);
-  const int rt = static_cast<int>(ceil_div(r, 16));
   const int iT = static_cast<int>(T), ir = static_cast<int>(r);
-  if (rt <= 1) {
-    // all projections in one launch
-    DecodeSet set{};
-    set.n = n;
-    set.Y = Y;
-    int64_t wgs = 0, col = 0;
-    for (int i = 0; i < n; ++i) {
-      set.proj[i] = proj[i];
-      set.wg0[i] = static_cast<int>(wgs);
-      set.col0[i] = col;
-      wgs += proj[i].out / kRows;
-      col += proj[i].out;
-    }
-    const dim3 grid(static_cast<uint32_t>(wgs));
-    // chunk steps per wave: fully unrolled when they number 4 (in <= 4096)
-    // or 8 (in <= 8192), a loop otherwise
-    const int64_t steps = round_up((ceil_div(in / 64, 4) + 3) / 4, 2);
-    const int ns = steps == 4 ? 4 : steps == 8 ? 8 : 0;
-    const int xp = T <= 2 ? 1 : T <= 4 ? 2 : T <= 8 ? 4 : 8;
-    // whole chunks in every wave's block range: 16 | in / 64
-    const bool full = (in / 64) % 16 == 0;
-#define QLORA_SPLIT(XPV, NSV, FV) \
-  hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV, FV>), grid, block, 0, st, set, in, X, iT, ir, s, ldy)
+  // all projections in one launch
+  DecodeSet set{};
+  set.n = n;
+  set.Y = Y;
+  int64_t wgs = 0, col = 0;
+  for (int i = 0; i < n; ++i) {
+    set.proj[i] = proj[i];
+    set.wg0[i] = static_cast<int>(wgs);
+    set.col0[i] = col;
+    wgs += proj[i].out / kRows;
+    col += proj[i].out;
+  }
+  if (pre_u) {
+    hipLaunchKernelGGL(k_decode_u, dim3(static_cast<uint32_t>(r), static_cast<uint32_t>(T), n), dim3(256),
+                       0, st, set, in, X, iT, ir, u_ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(static_cast<uint32_t>(wgs));
+  // chunk steps per wave: fully unrolled when they number 4 (in <= 4096)
+  // or 8 (in <= 8192), a loop otherwise
+  const int64_t steps = round_up((ceil_div(in / 64, 4) + 3) / 4, 2);
+  const int ns = steps == 4 ? 4 : steps == 8 ? 8 : 0;
+  const int xp = T <= 2 ? 1 : T <= 4 ? 2 : T <= 8 ? 4 : 8;
+  // whole chunks in every wave's block range: 16 | in / 64
+  const bool full = (in / 64) % 16 == 0;
+  const float* upre = u_ws;
+#define QLORA_SPLIT(XPV, NSV, FV)                                                                        \
+  do {                                                                                                   \
+    if (pre_u)                                                                                           \
+      hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV, FV, true>), grid, block, 0, st, set, in, X, iT, ir, \
+                         s, ldy, upre);                                                                  \
+    else                                                                                                 \
+      hipLaunchKernelGGL((k_decode_fwd_split<XPV, NSV, FV, false>), grid, block, 0, st, set, in, X, iT,   \
+                         ir, s, ldy, upre);                                                              \
+  } while (0)
 #define QLORA_SPLIT_NS(XPV)                                  \
   do {                                                       \
     if (full) {                                              \
@@ -660,30 +490,13 @@ hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const ui
       else QLORA_SPLIT(XPV, 0, false);                       \
     }                                                        \
   } while (0)
-    if (xp == 1) QLORA_SPLIT_NS(1);
-    else if (xp == 2) QLORA_SPLIT_NS(2);
-    else if (xp == 4) QLORA_SPLIT_NS(4);
-    else QLORA_SPLIT_NS(8);
+  if (xp == 1) QLORA_SPLIT_NS(1);
+  else if (xp == 2) QLORA_SPLIT_NS(2);
+  else if (xp == 4) QLORA_SPLIT_NS(4);
+  else QLORA_SPLIT_NS(8);
 #undef QLORA_SPLIT_NS
 #undef QLORA_SPLIT
-    return hipGetLastError();
-  }
-  // 16 < r <= 64: one launch per projection
-  int64_t col = 0;
-  for (int i = 0; i < n; ++i) {
-    const DecodeProj& p = proj[i];
-    const dim3 grid(static_cast<uint32_t>(p.out / kRows));
-#define QLORA_DEC(RTV)                                                                                \
-  hipLaunchKernelGGL((k_decode_fwd<RTV>), grid, block, 0, st, p.codes, p.absmax_q, p.scale, in, X, iT, \
-                     p.A, p.B, ir, s, Y + col, p.out, ldy)
-    if (rt <= 2) QLORA_DEC(2);
-    else QLORA_DEC(4);
-#undef QLORA_DEC
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    col += p.out;
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace qlora

@@ -79,8 +79,8 @@ int64_t total_out(const int64_t* outs, int n) {
   return N;
 }
 
-// the small-token forward (all projections in one launch for r <= 16) needs
-// no workspace; it takes the call when every projection fits it
+// the small-token forward takes the call when every projection fits it; it
+// needs a workspace only for the U it computes up front (decode_pre_u)
 bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
   for (int i = 0; i < n; ++i)
     if (!decode_fits(T, in, outs[i], r)) return false;
@@ -92,7 +92,11 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout) {
   FwdLayout l{0, 0, 0, 0, 0};
   Carve c;
-  if (!dropout && fwd_uses_decode(T, in, outs, n, r)) return l;
+  if (!dropout && fwd_uses_decode(T, in, outs, n, r)) {
+    if (decode_pre_u(n, outs, r)) l.u_pad = c.take(decode_u_bytes(n, T, r));  // U [n][T][r] fp32
+    l.total = c.off;
+    return l;
+  }
   const int64_t rp = padded_rank(r), N = total_out(outs, n);
   l.u_pad = c.take(static_cast<size_t>(T * n * rp * 4));  // [T][n 2rp] bf16
   l.b_pad = c.take(static_cast<size_t>(N * n * rp * 4));  // [N][2rp] or [N][n 2rp] bf16
@@ -304,7 +308,8 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
     DecodeProj proj[kMaxProj];
     for (int i = 0; i < n; ++i)
       proj[i] = DecodeProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, A[i], B[i], outs[i]};
-    return launched(launch_decode_fwd(n, proj, in, X, T, r, scale, Y, N, s));
+    float* u_ws = lay.total > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + lay.u_pad) : nullptr;
+    return launched(launch_decode_fwd(n, proj, in, X, T, r, scale, Y, N, u_ws, s));
   }
 
   const int64_t rp = padded_rank(r);

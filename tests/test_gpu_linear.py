@@ -193,15 +193,15 @@ def test_gradients_overwrite_not_accumulate():
     _check_bwd(res, w_hat, h, r, alpha, "overwrite")
 
 
-def test_small_token_forward_under_graph_replay():
-    # The small-token forward hands U = X A^T between workgroups through
-    # ticket counters in the workspace, which every call returns to zero.  A
-    # captured graph replays the same calls on the same workspace, with eager
-    # calls on it in between; every replay must equal the eager result bit
-    # for bit.
+@pytest.mark.parametrize("r", [16, 24])
+def test_small_token_forward_under_graph_replay(r):
+    # A captured graph replays small-token forwards sharing one workspace
+    # (r = 24: U = X A^T goes through it; r = 16: one launch, no workspace),
+    # with eager calls on the same workspace in between; every replay must
+    # equal the eager result bit for bit.
     q = require_gpu()
-    banner("graph replay of the small-token forward")
-    n_out, n_in, r, alpha = 512, 768, 16, 32.0
+    banner(f"graph replay of the small-token forward r={r}")
+    n_out, n_in, alpha = 512, 768, 2.0 * r
     hs = [_make(10, p, T, n_out, n_in, r) for p, T in ((0, 1), (1, 16), (2, 7))]
     W, w_hat = _quantize(q, hs[0]["w"])
     ins = [(dev_bf16(h["X"]), dev_bf16(h["A"]), dev_bf16(h["B"])) for h in hs]
@@ -277,6 +277,14 @@ def test_small_token_forward_needs_no_workspace():
                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 0
     _check_fwd(Y, w_hat, h, r, alpha, "ws=NULL")
+    # r > 16 computes U into the workspace first: NULL is refused, nothing runs
+    r2 = 32
+    h2 = _make(11, 8, 4, n_out, n_in, r2)
+    A2, B2 = dev_bf16(h2["A"]), dev_bf16(h2["B"])
+    st = q._lib.qlora_linear_fwd(ctypes.byref(wc), X.data_ptr(), 4, A2.data_ptr(), B2.data_ptr(), r2,
+                                 ctypes.c_float(64.0), Y.data_ptr(), None, 0,
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == -4  # QLORA_ERR_WORKSPACE
 
 
 # ------------------------------------------------------------------ small-token path
@@ -323,15 +331,27 @@ def test_small_token_split_variants(T, n_out, n_in, r):
     _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, f"T={T} in={n_in}")
 
 
-@pytest.mark.parametrize("T", [1, 16])
-def test_small_token_more_workgroups_than_cus(T):
+@pytest.mark.parametrize("T,r", [(1, 16), (16, 16), (1, 64), (16, 64)])
+def test_small_token_more_workgroups_than_cus(T, r):
     # 8B MLP gate shape at decode size: 896 workgroups of 16 rows, more than
-    # can be resident at once; also checks a repeat call is bit-identical
+    # can be resident at once (U computed up front); also checks a repeat
+    # call is bit-identical
     q = require_gpu()
-    banner(f"small-token 14336x4096 T={T}")
-    h = _make(3, 0, T, 14336, 4096, 16)
+    banner(f"small-token 14336x4096 T={T} r={r}")
+    h = _make(3, 0, T, 14336, 4096, r)
     W, w_hat = _quantize(q, h["w"])
-    Y1 = _fwd(q, W, h, 16, 32.0)
-    _check_fwd(Y1, w_hat, h, 16, 32.0, f"gate T={T}")
-    Y2 = _fwd(q, W, h, 16, 32.0)
+    Y1 = _fwd(q, W, h, r, 2.0 * r)
+    _check_fwd(Y1, w_hat, h, r, 2.0 * r, f"gate T={T} r={r}")
+    Y2 = _fwd(q, W, h, r, 2.0 * r)
     assert torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_small_token_down_shape(T):
+    # 8B MLP down shape (4096 x 14336, r = 64) at decode size: the chunk-step
+    # loop with U computed up front
+    q = require_gpu()
+    banner(f"small-token 4096x14336 T={T} r=64")
+    h = _make(3, 2, T, 4096, 14336, 64)
+    W, w_hat = _quantize(q, h["w"])
+    _check_fwd(_fwd(q, W, h, 64, 128.0), w_hat, h, 64, 128.0, f"down T={T}")
