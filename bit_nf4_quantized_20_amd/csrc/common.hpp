@@ -145,7 +145,7 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* absmax_q, const flo
 // (decode_pre_u) U is computed once into a workspace of decode_u_bytes()
 // first, which saves each workgroup reading all of A.
 constexpr int64_t kDecodeMaxT = 16;
-constexpr int64_t kDecodeFusedMaxWgs = 512;
+constexpr int64_t kDecodeFusedMaxWgs = 256;
 constexpr int64_t kDecodeMaxRank = 64;
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
 // One projection of the small-token forward: its NF4 weight [out][in] and

@@ -153,8 +153,8 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  * the forward's dequantized weight: 2 * out * in bytes).  It needs no
  * initialisation and keeps nothing between calls.  The small-token forward
  * (T <= 16 and r <= 64) uses it only for U = X A^T (n * T * r fp32 values),
- * computed once up front when r > 16 or the projections have more than 8192
- * output rows together; with r <= 16 and at most 8192 rows ws may be NULL.
+ * computed once up front when r > 16 or the projections have more than 4096
+ * output rows together; with r <= 16 and at most 4096 rows ws may be NULL.
  * Calls that
  * overlap in time (different streams) must not share a workspace.
  */

@@ -43,10 +43,10 @@ def _rows(T, n=24):
 @pytest.mark.parametrize("T,n_in,outs,r,alpha", [
     (300, 256, [512, 256], 16, 32.0),              # gate|up-like, ragged T, 128-tiles
     (9, 512, [256, 64, 64], 16, 32.0),             # q|k|v-like at a small-token count
-    (1, 4096, [4096, 1024, 1024], 16, 32.0),       # 8B q|k|v decode: one small-token launch
+    (1, 4096, [4096, 1024, 1024], 16, 32.0),       # 8B q|k|v decode: U up front, one launch
     (16, 4096, [4096, 1024, 1024], 16, 32.0),      # the same at T = 16
     (7, 1024, [128, 64, 192], 24, 48.0),           # r > 16: U computed up front, one launch
-    (5, 1024, [4096, 4096, 1024], 16, 32.0),       # > 8192 rows: U computed up front
+    (5, 1024, [2048, 1024, 1024], 16, 32.0),       # 4096 rows: one fused launch
     (4096, 4096, [4096, 1024, 1024], 16, 32.0),    # 8B q|k|v at T = 4096 (256-tiles)
     (4096, 1024, [4160, 4032], 8, 16.0),           # outputs not multiples of the tile
 ])
