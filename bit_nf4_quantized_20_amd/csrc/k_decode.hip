@@ -5,10 +5,13 @@
 //
 // Decomposition.  Workgroup b owns the 16 output rows [16b, 16b + 16) over
 // the whole reduction dimension, so its part of Y is finished inside the
-// workgroup: no partial sums and no synchronisation cross workgroups, and the
-// kernel needs no workspace.  With out = 4096 the grid is 256 workgroups, one
-// per CU, each streaming 16 rows x in of codes.  Every workgroup computes the
-// small U = X A^T itself from X and A, which stay resident in L2.
+// workgroup: no partial sums and no synchronisation cross workgroups.  With
+// out = 4096 the grid is 256 workgroups, one per CU, each streaming 16 rows x
+// in of codes.  Up to one workgroup per CU (and r <= 16) every workgroup
+// computes the small U = X A^T itself from X and A, which stay resident in
+// L2, and the call is one launch with no workspace.  With more workgroups, or
+// r > 16, reading all of A in every workgroup costs more than a second
+// launch: k_decode_u computes U once into the workspace first.
 //
 // Eight waves split the 64-weight blocks of the 16 rows into contiguous
 // ranges, walked in chunks of four blocks (256 k).  In a chunk, lane
@@ -24,12 +27,8 @@
 // instruction, which the memory pipeline serves several times slower than
 // contiguous requests.  So each wave loads its chunk of X (T tokens x 512 B)
 // and of A (16 ranks x 512 B) contiguously, two rows per instruction, into
-// a private LDS tile, then reads the fragments back.  The tile stores piece
-// p (16 B) of row t at slot 32 t + (p ^ t): writes are contiguous and the
-// fragment reads of 16 rows fall on 16 distinct 4-bank groups.  Rank tiles
-// beyond the first reuse the same A tile in turn (a wave's LDS operations run
-// in order).  For r <= 16 two chunks' global loads (codes, X, A) are in
-// flight at a time.
+// a private LDS tile, then reads the fragments back (padded rows, below).
+// Two chunks' global loads (codes, X, A) are in flight at a time.
 //
 // Epilogue: the eight waves' fp32 accumulators of the base product and of U
 // meet in LDS; Y = base + s U B^T is rounded to bf16 once.
@@ -44,7 +43,6 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 16;
-constexpr int kTileSlots = 16 * 32;  // 16 rows x 32 pieces of 16 B (8 KB)
 constexpr int kCodeSlots = 16 * 8;   // 16 rows x 8 pieces: one chunk of codes (2 KB)
 // Split kernel tiles: rows of 32 pieces padded to 33, so piece p of row t
 // sits at slot 33 t + p.  A fragment read (16 rows at one piece) then falls
@@ -57,8 +55,6 @@ constexpr int kStream = 2;               // cache policy nt: streamed once
 constexpr uint32_t kPastEnd = 0x80000000u;  // past every buffer (all < 2^31 bytes)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ int tile_slot(int row, int piece) { return 32 * row + (piece ^ row); }
 
 // This lane's block of codes in one chunk, with its absmax code and scale.
 struct CodeStage {
