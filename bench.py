@@ -296,7 +296,7 @@ def main():
                                "256), fwd at T=1 and T=16, LoRA r=16 alpha=32, 64-weight pool",
                    "out_features": n_out, "in_features": n_in, "tokens": [1, 16], "r": r,
                    "alpha": alpha, "weight_pool": P},
-        "roofline": {"bound": "hbm", "kernel": "k_decode_fwd (T=16)", "achieved": round(ach16, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_decode_fwd_split (T=16)", "achieved": round(ach16, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach16 / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic()},
         "cpu_baseline": cpu,
