@@ -13,9 +13,12 @@ value = NF4 weight-stream throughput of the step, in GB/s of algorithmic
 bytes (packed codes + 8-bit absmax + group scales + X + Y + A + B per call).
 
 Also reported ("extra"): nf4_quantize of the 4096 x 4096 fp32 weight and
-fwd+bwd TFLOP/s of the 8B-MLP projections (gate, up 4096 -> 14336, down
-14336 -> 4096; T = 4096, r = 64) -- the large-token half of the metric;
-skipped with --no-train.
+of the flat 2^30-element tensor; fwd+bwd TFLOP/s of every projection of the
+8B MLP (T = 4096, r = 64), the 8B attention projections (T = 8192, r = 16)
+and the 70B MLP (T = 4096, r = 64) -- the large-token half of the metric --
+each with the oracle timed on the host beside it (skipped with --no-train);
+the host's CPU model and thread counts and the GPU shader clock sampled
+during the large-token legs.
 
 The roofline entry is for the dominant kernel, the fused small-token forward
 (one launch per call); its average duration comes from HIP events on the
@@ -51,8 +54,10 @@ def parse():
                     help="only run the T=16 small-token forward over the weight pool and a "
                          "256 MiB copy (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
     ap.add_argument("--mlp-probe", action="store_true",
-                    help="only run the 8B-MLP fwd + bwd leg and print its figures (for rocprofv3 "
-                         "--pmc passes over the large-token GEMMs)")
+                    help="only run the fwd + bwd step of one large-token workload (--probe-workload: "
+                         "3 = 8B MLP, 4 = 8B attention, 5 = 70B MLP) and print its figures (for "
+                         "rocprofv3 --pmc passes over the large-token GEMMs)")
+    ap.add_argument("--probe-workload", type=int, default=3, choices=(3, 4, 5))
     return ap.parse_args()
 
 
@@ -139,7 +144,7 @@ def main():
         return
     if args.mlp_probe:
         del pool
-        print(json.dumps(train_leg(q, synth, dev, bf)), flush=True)
+        print(json.dumps(large_step_leg(q, synth, dev, bf, args.probe_workload, steps=5)), flush=True)
         return
 
     b1 = decode_call_bytes(n_out, n_in, 1, r)
@@ -270,14 +275,28 @@ def main():
     # ------------------------------ MLP-sized weights at decode sizes
     extra["mlp_weights_decode"] = mlp_decode_leg(q, synth, dev, bf)
 
+    # ---------------------------------------- flat 2^30-element quantize
+    del pool
+    torch.cuda.empty_cache()
+    extra["quantize_flat_2pow30"] = flat_quantize_leg(q, synth, dev, not args.no_cpu_baseline)
+
     # ------------------------------------------- large-token fwd + bwd
     if not args.no_train:
-        extra["mlp8b_fwd_bwd"] = train_leg(q, synth, dev, bf)
+        sampler = SclkSampler()
+        sampler.start()
+        for wid, key in ((3, "mlp8b_fwd_bwd"), (4, "attn8b_fwd_bwd"), (5, "mlp70b_fwd_bwd")):
+            extra[key] = large_step_leg(q, synth, dev, bf, wid, steps=10 if wid < 5 else 5)
+        extra["mlp8b_variants"] = train_leg(q, synth, dev, bf, extra["mlp8b_fwd_bwd"])
+        extra["gpu_sclk_mhz"] = sampler.stop()
+        if not args.no_cpu_baseline:
+            for wid, key in ((3, "mlp8b_fwd_bwd"), (4, "attn8b_fwd_bwd"), (5, "mlp70b_fwd_bwd")):
+                extra[key]["oracle"] = oracle_step_timing(synth, wid)
+    extra["host"] = host_info()
 
     # --------------------------------------------------------- cpu baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w_host, pool[0], n_out, n_in, r, alpha, X1, X16, A, B, b1 + b16)
+        cpu = cpu_baseline(n_out, n_in, r, alpha, X1, X16, A, B, b1 + b16)
 
     out = {
         "metric": METRIC,
@@ -301,7 +320,7 @@ def main():
                      "traffic": recorded_traffic()},
         "cpu_baseline": cpu,
         "extra": extra,
-        "wall_s_timed_region": round(wall, 3),
+        "wall_s_timed_region": round(wall, 6),
     }
     print(json.dumps(out), flush=True)
 
@@ -465,15 +484,17 @@ def counters_probe(q, pool, X, Y, A, B, r, alpha, ws, dev):
                       "sources_sha256": decode_fingerprint()}), flush=True)
 
 
-def train_leg(q, synth, dev, bf):
-    """fwd + bwd of the 8B-MLP projections (gate and up 4096 -> 14336, down
-    14336 -> 4096; T = 4096, r = 64, alpha = 128): per projection and for the
-    three together.  Each call is warmed up, then timed over 20 calls."""
+def train_leg(q, synth, dev, bf, plain):
+    """Variants of the 8B-MLP step (gate and up 4096 -> 14336, down
+    14336 -> 4096; T = 4096, r = 64, alpha = 128), next to its plain figures
+    `plain` (large_step_leg): every projection with LoRA dropout p = 0.05;
+    gate and up as one multi-projection call each way; and the forward of
+    gate|up at T = 1792, where the dequantization stays inside the GEMM's LDS
+    staging.  Each call is warmed up, then timed over 20 calls."""
     import torch
     wl = synth.WORKLOADS[3]
     T, r, alpha = wl.tokens[0], wl.r, wl.alpha
-    res = {"T": T, "r": r, "alpha": alpha}
-    tot_flop, tot_ms, tot_dms = 0.0, 0.0, 0.0
+    res = {}
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -485,6 +506,7 @@ def train_leg(q, synth, dev, bf):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    tot_dms = 0.0
     for pi, p in enumerate(wl.projections):
         n_out, n_in = p.out_features, p.in_features
         w = torch.from_numpy(synth.weight(3, pi, n_out, n_in)).to(dev)
@@ -498,32 +520,9 @@ def train_leg(q, synth, dev, bf):
         dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
         dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
         dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
-        wsf = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, False), dev)
-        wsb = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
-
-        def fwd():
-            q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=wsf)
-
-        def bwd():
-            q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX=dX, dA=dA, dB=dB, ws=wsb)
-
-        for _ in range(8):
-            fwd()
-            bwd()
-        ms_f = timed(fwd, 20)
-        ms_b = timed(bwd, 20)
-        flop_f = 2 * T * n_in * n_out + 2 * T * r * (n_in + n_out)
-        flop_b = 2 * T * n_in * n_out + 4 * T * r * (n_in + n_out)
-        res[p.name] = {"out": n_out, "in": n_in, "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
-                       "fwd_TFLOPs": round(flop_f / (ms_f * 1e-3) / 1e12, 1),
-                       "bwd_TFLOPs": round(flop_b / (ms_b * 1e-3) / 1e12, 1),
-                       "fwd_bwd_TFLOPs": round((flop_f + flop_b) / ((ms_f + ms_b) * 1e-3) / 1e12, 1)}
-        tot_flop += flop_f + flop_b
-        tot_ms += ms_f + ms_b
-
-        # the same step with LoRA dropout (p = 0.05, a fresh seeded keep mask)
         keep = torch.from_numpy(synth.keep_mask(synth.seed_for(3, pi, "keep"), T, n_in, DROPOUT_P)).to(dev)
         wdf = q.make_workspace(q.qlora_workspace_bytes_dropout(T, n_in, n_out, r, False), dev)
+        wsb = q.make_workspace(q.qlora_workspace_bytes_dropout(T, n_in, n_out, r, True), dev)
 
         def dfwd():
             q.qlora_linear_fwd_dropout(W, X, keep, DROPOUT_P, A, B, r, alpha, Y=Y, ws=wdf)
@@ -532,19 +531,15 @@ def train_leg(q, synth, dev, bf):
             q.qlora_linear_bwd_dropout(W, X, dY, keep, DROPOUT_P, A, B, r, alpha, dX=dX, dA=dA, dB=dB,
                                        ws=wsb)
 
-        for _ in range(8):
+        for _ in range(4):
             dfwd()
             dbwd()
         dms_f = timed(dfwd, 20)
         dms_b = timed(dbwd, 20)
-        res[p.name]["dropout_fwd_ms"] = round(dms_f, 3)
-        res[p.name]["dropout_bwd_ms"] = round(dms_b, 3)
+        res[f"dropout_{p.name}"] = {"fwd_ms": round(dms_f, 3), "bwd_ms": round(dms_b, 3)}
         tot_dms += dms_f + dms_b
-        del W, X, dY, Y, dX, wsf, wsb, wdf, keep
-    tf = tot_flop / (tot_ms * 1e-3) / 1e12
-    res["mlp_fwd_bwd_ms"] = round(tot_ms, 3)
-    res["mlp_fwd_bwd_TFLOPs"] = round(tf, 1)
-    res["frac_of_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        del W, X, dY, Y, dX, wdf, wsb, keep
+    tot_flop = plain["step_flop"]
     res["mlp_dropout"] = {"p": DROPOUT_P, "fwd_bwd_ms": round(tot_dms, 3),
                           "fwd_bwd_TFLOPs": round(tot_flop / (tot_dms * 1e-3) / 1e12, 1)}
 
@@ -576,7 +571,7 @@ def train_leg(q, synth, dev, bf):
     def bwd2():
         q.qlora_linear_bwd_multi(Ws, X, dY, As, Bs, r, alpha, dX=dX, dAs=dAs, dBs=dBs, ws=wsb)
 
-    for _ in range(8):
+    for _ in range(4):
         fwd2()
         bwd2()
     ms_f = timed(fwd2, 20)
@@ -586,7 +581,7 @@ def train_leg(q, synth, dev, bf):
     res["gate_up_fused"] = {"fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
                             "fwd_TFLOPs": round(flop_f / (ms_f * 1e-3) / 1e12, 1),
                             "bwd_TFLOPs": round(flop_b / (ms_b * 1e-3) / 1e12, 1)}
-    d = res["down"]
+    d = plain["down"]
     fused_ms = ms_f + ms_b + d["fwd_ms"] + d["bwd_ms"]
     tf2 = tot_flop / (fused_ms * 1e-3) / 1e12
     res["mlp_fused_fwd_bwd_ms"] = round(fused_ms, 3)
@@ -603,29 +598,127 @@ def train_leg(q, synth, dev, bf):
     def fwdf():
         q.qlora_linear_fwd_multi(Ws, Xf, As, Bs, r, alpha, Y=Yf, ws=wsff)
 
-    for _ in range(8):
+    for _ in range(4):
         fwdf()
     ms_ff = timed(fwdf, 20)
     flop_ff = 2 * Tf * n_in * N + 2 * Tf * r * (2 * n_in + N)
     tff = flop_ff / (ms_ff * 1e-3) / 1e12
     res["gate_up_fused_nf4_fwd_T1792"] = {"fwd_ms": round(ms_ff, 3), "fwd_TFLOPs": round(tff, 1),
                                           "frac_of_bf16_peak": round(tff / BF16_PEAK_TFLOPS, 4)}
+    del Ws, X, dY, Y, dX, wsf, wsb, wsff
+    torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(w_host, W, n_out, n_in, r, alpha, X1, X16, A, B, step_bytes):
-    """The oracle (NumPy, fp64 BLAS) doing the same step: dequantize one NF4
-    weight and run the T=1 and T=16 forwards; repeated for ~10 s."""
+def blas_threads():
+    try:
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"])
+    except Exception:
+        pass
+    return None
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cores_in_affinity": host_cores(), "blas_threads": blas_threads(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+class SclkSampler:
+    """Samples the GPU shader clock (the active level of pp_dpm_sclk of the
+    device torch uses) every few milliseconds on a host thread while the
+    large-token legs run; reports min / median / max in MHz, or why it could
+    not read them."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.stop_flag = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+        self.path = self._find()
+
+    @staticmethod
+    def _find():
+        import glob
+        try:
+            import torch
+            pr = torch.cuda.get_device_properties(0)
+            bdf = "%04x:%02x:%02x.0" % (getattr(pr, "pci_domain_id", 0), pr.pci_bus_id, pr.pci_device_id)
+            cand = f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk"
+            if os.path.exists(cand):
+                return cand
+        except Exception:
+            pass
+        found = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+        return found[0] if len(found) == 1 else None
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.strip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return int(m.group(1))
+        return None
+
+    def _run(self):
+        while not self.stop_flag.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except OSError:
+                return
+            self.stop_flag.wait(self.period)
+
+    def start(self):
+        if self.path:
+            self.thread.start()
+
+    def stop(self):
+        if not self.path:
+            return {"unavailable": "no readable pp_dpm_sclk for the device"}
+        self.stop_flag.set()
+        self.thread.join()
+        v = sorted(self.samples)
+        if not v:
+            return {"unavailable": f"{self.path} gave no active level"}
+        return {"min": v[0], "median": v[len(v) // 2], "max": v[-1], "samples": len(v),
+                "source": self.path}
+
+
+def cpu_baseline(n_out, n_in, r, alpha, X1, X16, A, B, step_bytes):
+    """The oracle (NumPy, fp64 BLAS) doing the same step on the same workload:
+    dequantize an NF4 weight it quantized itself from the same seeded fp32
+    weight, then the T=1 and T=16 forwards; repeated for ~10 s."""
     import numpy as np
     import torch
-    from oracle import dense, nf4
+    import synth
+    from oracle import dense, native, nf4
 
     def bits(t):
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
-    codes = W.codes.cpu().numpy()
-    aq = W.absmax_q.cpu().numpy()
-    sc = W.absmax_scale.cpu().numpy()
+    codes, aq, sc = nf4.quantize(synth.weight(2, 0, n_out, n_in), nearest=native.nearest_level)
     hx1, hx16, ha, hb = bits(X1), bits(X16), bits(A), bits(B)
     n = 0
     t0 = time.perf_counter()
@@ -638,15 +731,165 @@ def cpu_baseline(w_host, W, n_out, n_in, r, alpha, X1, X16, A, B, step_bytes):
         if time.perf_counter() - t0 > 10.0 or n >= 50:
             break
     dt = time.perf_counter() - t0
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(step_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
+    threads = blas_threads() or host_cores()
+    return {"value": round(step_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n} steps (dequantize + T=1 and T=16 forward, fp64 BLAS) of the same "
-                      f"workload on one weight, {dt:.1f} s"}
+            "sample": f"{n} steps (dequantize + T=1 and T=16 forward, fp64 BLAS on {threads} threads) "
+                      f"of the same workload on one weight, {dt:.1f} s"}
+
+
+def step_flop(T, n_in, n_out, r):
+    """fwd + bwd algorithmic flop of one projection: 4 T in out + 6 T r (in + out)
+    (no weight-gradient GEMM: the NF4 weight is frozen)."""
+    return 4 * T * n_in * n_out + 6 * T * r * (n_in + n_out)
+
+
+def oracle_step_timing(synth, wid, t_rows=256, out_rows=2048):
+    """The oracle's fwd + bwd of every projection of workload `wid`, timed on
+    the host on a bounded sub-problem and scaled to the whole step by
+    operation counts: per projection the oracle quantizes (untimed) the first
+    `out_rows` rows of the seeded fp32 weight, then dequantizes them and runs
+    Y, dX, dA, dB in fp64 for the first `t_rows` tokens (timed).  The GEMM
+    part scales with T * out * in, the dequantization with out * in."""
+    import numpy as np
+    from oracle import dense, native, nf4
+    wl = synth.WORKLOADS[wid]
+    T, r, alpha = wl.tokens[0], wl.r, wl.alpha
+    total_s, total_flop = 0.0, 0
+    for pi, p in enumerate(wl.projections):
+        n_out, n_in = p.out_features, p.in_features
+        ro = min(out_rows, n_out)
+        w = synth.weight(wid, pi, n_out, n_in)[:ro]
+        X = synth.activations(wid, pi, t_rows, n_in)
+        dY = synth.activations(wid, pi, t_rows, ro, "dY")
+        A = synth.lora_A(wid, pi, r, n_in)
+        B = synth.lora_B(wid, pi, n_out, r)[:ro]
+        codes, aq, sc = nf4.quantize(w, nearest=native.nearest_level)
+        t0 = time.perf_counter()
+        w_hat = nf4.dequantize(codes, aq, sc).reshape(ro, n_in)
+        t1 = time.perf_counter()
+        dense.linear_fwd(w_hat, X, A, B, alpha, r)
+        dense.linear_bwd(w_hat, X, dY, A, B, alpha, r)
+        t2 = time.perf_counter()
+        total_s += (t1 - t0) * (n_out / ro) + (t2 - t1) * (T / t_rows) * (n_out / ro)
+        total_flop += step_flop(T, n_in, n_out, r)
+    threads = blas_threads() or host_cores()
+    return {"value": round(total_flop / total_s / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "step_s_estimated": round(total_s, 2),
+            "sample": f"per projection: dequantize of {out_rows} weight rows and fp64 fwd+bwd of "
+                      f"{t_rows} tokens x those rows, scaled to the full step by operation counts"}
+
+
+def flat_quantize_leg(q, synth, dev, with_oracle):
+    """nf4_quantize of a 2^30-element fp32 tensor (N(0, 0.02)): the seeded
+    recipe's first 2^26 draws (seed 5000) repeated 16 times on the device
+    (the quantize cost depends only on the value distribution).  4 B read and
+    0.515869 B written per weight.  Timed over 5 calls after 2 untimed ones;
+    the oracle (NumPy + the plain-C nearest-level search) quantizes a 2^24
+    sample of the same draws on the host, scaled to 2^30 elements."""
+    import numpy as np
+    import torch
+    n = synth.FLAT_QUANTIZE_NUMEL
+    part = synth.normal_f32(synth.FLAT_QUANTIZE_SEED, (1 << 26,), synth.W_STD)
+    w = torch.from_numpy(part).to(dev).repeat(n // part.size)
+    codes, aq, sc = q.nf4_quantize(w)
+    q.nf4_quantize(w, codes, aq, sc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    k = 5
+    for _ in range(k):
+        q.nf4_quantize(w, codes, aq, sc)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / k
+    nbytes = int(n * (4 + NF4_BYTES_PER_WEIGHT))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = {"numel": n, "us_per_call": round(us, 1), "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del w, codes, aq, sc
+    torch.cuda.empty_cache()
+    if with_oracle:
+        from oracle import native, nf4
+        m = 1 << 24
+        t0 = time.perf_counter()
+        nf4.quantize(part[:m], nearest=native.nearest_level)
+        dt = (time.perf_counter() - t0) * (n / m)
+        res["oracle"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+                         "cores": int(os.environ.get("OMP_NUM_THREADS", host_cores())),
+                         "sample": "quantize of 2^24 elements (NumPy fp32 + plain-C nearest level, "
+                                   "OpenMP), scaled to 2^30", "call_s_estimated": round(dt, 1)}
+    return res
+
+
+def large_step_leg(q, synth, dev, bf, wid, steps):
+    """fwd + bwd of every projection of workload `wid` (the 8B attention
+    projections q, k, v, o at T = 8192, r = 16; the 70B MLP gate, up, down at
+    T = 4096, r = 64): a step is each projection's forward then backward, in
+    order, each projection on its own weight, activations and gradients (the
+    step's working set is several times the 256 MB last-level cache).  2
+    untimed steps, then `steps` timed steps with events around every call."""
+    import torch
+    wl = synth.WORKLOADS[wid]
+    T, r, alpha = wl.tokens[0], wl.r, wl.alpha
+    items = []
+    ws_f = ws_b = 0
+    for pi, p in enumerate(wl.projections):
+        n_out, n_in = p.out_features, p.in_features
+        w = torch.from_numpy(synth.weight(wid, pi, n_out, n_in)).to(dev)
+        it = {"name": p.name, "out": n_out, "in": n_in, "W": q.nf4_quantize_weight(w),
+              "X": bf(synth.activations(wid, pi, T, n_in)), "dY": bf(synth.activations(wid, pi, T, n_out, "dY")),
+              "A": bf(synth.lora_A(wid, pi, r, n_in)), "B": bf(synth.lora_B(wid, pi, n_out, r)),
+              "Y": torch.empty(T, n_out, dtype=torch.bfloat16, device=dev),
+              "dX": torch.empty(T, n_in, dtype=torch.bfloat16, device=dev),
+              "dA": torch.empty(r, n_in, dtype=torch.float32, device=dev),
+              "dB": torch.empty(n_out, r, dtype=torch.float32, device=dev)}
+        del w
+        items.append(it)
+        ws_f = max(ws_f, q.qlora_workspace_bytes(T, n_in, n_out, r, False))
+        ws_b = max(ws_b, q.qlora_workspace_bytes(T, n_in, n_out, r, True))
+    wsf, wsb = q.make_workspace(ws_f, dev), q.make_workspace(ws_b, dev)
+
+    def run(evs=None):
+        for j, it in enumerate(items):
+            if evs is not None:
+                evs[j][0].record()
+            q.qlora_linear_fwd(it["W"], it["X"], it["A"], it["B"], r, alpha, Y=it["Y"], ws=wsf)
+            if evs is not None:
+                evs[j][1].record()
+            q.qlora_linear_bwd(it["W"], it["X"], it["dY"], it["A"], it["B"], r, alpha, dX=it["dX"], dA=it["dA"],
+                               dB=it["dB"], ws=wsb)
+            if evs is not None:
+                evs[j][2].record()
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    all_evs = [[(mk(), mk(), mk()) for _ in items] for _ in range(steps)]
+    for k in range(steps):
+        run(all_evs[k])
+    torch.cuda.synchronize()
+    res = {"T": T, "r": r, "alpha": alpha, "steps": steps}
+    tot_flop, tot_ms = 0, 0.0
+    for j, it in enumerate(items):
+        f_ms = sum(all_evs[k][j][0].elapsed_time(all_evs[k][j][1]) for k in range(steps)) / steps
+        b_ms = sum(all_evs[k][j][1].elapsed_time(all_evs[k][j][2]) for k in range(steps)) / steps
+        n_in, n_out = it["in"], it["out"]
+        flop_f = 2 * T * n_in * n_out + 2 * T * r * (n_in + n_out)
+        flop_b = 2 * T * n_in * n_out + 4 * T * r * (n_in + n_out)
+        res[it["name"]] = {"out": n_out, "in": n_in, "fwd_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3),
+                           "fwd_TFLOPs": round(flop_f / (f_ms * 1e-3) / 1e12, 1),
+                           "bwd_TFLOPs": round(flop_b / (b_ms * 1e-3) / 1e12, 1)}
+        tot_flop += flop_f + flop_b
+        tot_ms += f_ms + b_ms
+    step_ms = all_evs[0][0][0].elapsed_time(all_evs[-1][-1][2]) / steps
+    tf = tot_flop / (step_ms * 1e-3) / 1e12
+    res.update({"step_flop": tot_flop, "step_ms": round(step_ms, 3), "sum_of_calls_ms": round(tot_ms, 3),
+                "fwd_bwd_TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+    del items, wsf, wsb
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

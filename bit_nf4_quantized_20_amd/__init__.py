@@ -436,21 +436,3 @@ def nf4_code_thresholds():
     out = (ctypes.c_float * 15)()
     _lib.nf4_code_thresholds(out)
     return [float(v) for v in out]
-
-
-class QLoRALinearFunction(torch.autograd.Function):
-    """Pairs qlora_linear_fwd / qlora_linear_bwd as an autograd function
-    (inputs X, A, B; the NF4 weight gets no gradient)."""
-
-    @staticmethod
-    def forward(ctx, X, A, B, W: NF4Weight, r: int, alpha: float):
-        ctx.save_for_backward(X, A, B)
-        ctx.W, ctx.r, ctx.alpha = W, r, alpha
-        return qlora_linear_fwd(W, X.contiguous(), A.contiguous(), B.contiguous(), r, alpha)
-
-    @staticmethod
-    def backward(ctx, dY):
-        X, A, B = ctx.saved_tensors
-        dX, dA, dB = qlora_linear_bwd(ctx.W, X, dY.contiguous().to(torch.bfloat16), A, B, ctx.r,
-                                      ctx.alpha)
-        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None

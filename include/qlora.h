@@ -164,8 +164,13 @@ size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_feature
 /*
  * qlora_linear_fwd -- F1 + F2: Y = X W_hat^T + (alpha/r) (X A^T) B^T.
  * paperclase "QLoRA", Parte 4, h = W_hat x + (alpha/r) B A x, with
- * W_hat = dq(codes, absmax) rebuilt inside the matmul and never stored.
- * bf16 inputs, fp32 accumulation, one rounding of Y to bf16 at the end.
+ * W_hat = dq(codes, absmax) as nf4_dequantize defines it.  Where W_hat lives
+ * depends on T: up to 16 tokens it is rebuilt in registers right before the
+ * matrix cores use it; from 17 to 2047 tokens it is rebuilt while the
+ * weight tile is staged into on-chip memory; from 2048 tokens on it is
+ * expanded once into the workspace (2 * out * in bytes) and read back by the
+ * GEMM.  bf16 inputs, fp32 accumulation, one rounding of Y to bf16 at the
+ * end.
  *   W   NF4 weight [out, in]; in % 64 == 0, out % 64 == 0
  *   X   [T, in] bf16;  T >= 0 (0 is a no-op; X and Y may then be NULL)
  *   A   [r, in] bf16;  B [out, r] bf16;  1 <= r <= 256;  alpha finite
@@ -218,7 +223,11 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
  *   dB = s dY^T (X A^T)               [out, r] fp32
  * paperclase "QLoRA", Parte 4: dL/dx = (W_hat + (alpha/r) B A)^T dL/dh; no
  * gradient for W_hat (the codes are not parameters); A and B are the only
- * trained tensors.  dA and dB are overwritten, not accumulated.
+ * trained tensors.  dA and dB are overwritten, not accumulated.  They are
+ * sums over token slices added with fp32 atomics, so two identical calls can
+ * differ in the last bits of dA and dB (summation order); Y and dX are
+ * reproducible bit for bit.  The backward expands W_hat^T into the
+ * workspace (2 * out * in bytes) for its dX product.
  *   dY [T, out] bf16; other arguments as in qlora_linear_fwd;
  *   ws of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1)
  * T == 0 writes zeros to dA and dB and nothing else (X, dY, dX may be NULL).

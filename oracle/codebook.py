@@ -5,11 +5,10 @@ a QLoRA", the listing that builds the levels "as bitsandbytes does" and the
 NF4 bullet above it: 16 levels placed at quantiles of the standard normal,
 with an exact zero, normalised to [-1, 1].  Reading of that construction:
 
-* positive levels: the standard-normal quantile function at 8 probabilities,
-  namely 9 evenly spaced points from 0.9677083 down to 0.5 with the 0.5 end
-  left out;
-* negative levels: minus the quantile function at 7 probabilities, namely 8
-  evenly spaced points over the same range with the 0.5 end left out;
+* each non-zero level is a signed quantile of the standard normal: 8 above
+  zero and 7 below, each tail taking its probabilities in equal steps from
+  0.9677083 toward 1/2 (8 and 7 steps; 1/2 itself, whose quantile is zero, is
+  never taken), so the two outermost levels are mirror images;
 * one exact zero; all 16 sorted ascending (so code 7 is the zero, code 0 the
   most negative level: paperclase "QLoRA", Parte 2, "c: un indice de 4 bits,
   de 0 a 15"), then divided by the largest level.
@@ -40,20 +39,28 @@ def _normal_quantiles_fp32(p: torch.Tensor) -> torch.Tensor:
     return torch.erfinv(2 * p - 1) * math.sqrt(2)
 
 
-def _tail_quantiles(p_high: float, n_points: int) -> torch.Tensor:
-    """Quantiles at n_points fp32 probabilities evenly spaced from p_high to
-    0.5, without the 0.5 end (which would duplicate the shared zero)."""
-    probs = torch.linspace(p_high, 0.5, n_points, dtype=torch.float32)
-    return _normal_quantiles_fp32(probs[: n_points - 1])
+def _tail_probabilities(p_high: float, count: int) -> torch.Tensor:
+    """`count` probabilities walking from p_high toward 1/2 in equal steps of
+    (p_high - 1/2) / count, so 1/2 itself (whose quantile is the shared zero)
+    is never reached.  fp32, produced the way the page's listing produces them
+    (an fp32 evenly spaced grid of count + 1 points whose last point, 1/2, is
+    dropped): the canonical levels depend on these exact fp32 values."""
+    return torch.linspace(p_high, 0.5, count + 1, dtype=torch.float32)[:count]
 
 
 def nf4_levels() -> np.ndarray:
-    """The 16 NF4 levels, fp32, ascending; index 7 is exactly +0.0."""
-    positive = _tail_quantiles(NF4_P_HIGH, 9)       # 8 values
-    negative = -_tail_quantiles(NF4_P_HIGH, 8)      # 7 values
-    zero = torch.zeros(1, dtype=torch.float32)
-    levels = torch.sort(torch.cat([negative, zero, positive])).values
-    levels = levels / levels.max()
+    """The 16 NF4 levels, fp32, ascending; index 7 is exactly +0.0.
+
+    Every non-zero level is a signed standard-normal quantile: 8 levels above
+    zero at the 8 probabilities of one tail, 7 below zero at the 7 of the
+    other (both tails start at the same p_high, so the outermost levels are
+    +-Phi^{-1}(p_high)), plus the exact zero.  All are divided by the largest
+    level, then sorted ascending."""
+    n_pos, n_neg = 8, 7
+    probs = torch.cat([_tail_probabilities(NF4_P_HIGH, n_pos), _tail_probabilities(NF4_P_HIGH, n_neg)])
+    signs = torch.cat([torch.ones(n_pos), -torch.ones(n_neg)]).to(torch.float32)
+    signed = torch.cat([signs * _normal_quantiles_fp32(probs), torch.zeros(1, dtype=torch.float32)])
+    levels = torch.sort(signed / signed.max()).values
     out = levels.numpy().astype(np.float32)
     assert out.shape == (16,)
     return out

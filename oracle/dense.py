@@ -36,11 +36,6 @@ def widen(bits_or_f32: np.ndarray) -> np.ndarray:
     return a.astype(np.float64)
 
 
-def lora_down(X, A) -> np.ndarray:
-    """U = X A^T (also V = dY B with (dY, B^T))."""
-    return widen(X) @ widen(A).T
-
-
 def linear_fwd(W_hat, X, A, B, alpha: float, r: int) -> np.ndarray:
     """Y = X W_hat^T + (alpha/r) (X A^T) B^T, fp64."""
     s = float(alpha) / float(r)
