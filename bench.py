@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the small-token legs (the headline, q|k|v and the MLP-sized weights)")
     ap.add_argument("--counters-probe", action="store_true",
                     help="only run the T=16 small-token forward over the weight pool and a "
                          "256 MiB copy (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
@@ -221,6 +223,13 @@ def main():
         "timing": "HIP graph replay of back-to-back calls (events on the library's stream)",
         "weight_pool_bytes": int(P * n_out * n_in * NF4_BYTES_PER_WEIGHT),
     }
+
+    if args.decode_only:
+        extra["qkv8b_decode"] = qkv_decode_leg(q, synth, dev, bf)
+        extra["mlp_weights_decode"] = mlp_decode_leg(q, synth, dev, bf)
+        print(json.dumps({"value": round(value, 2), "ms_per_step": round(ms_per_step, 5), "extra": extra}),
+              flush=True)
+        return
 
     # ------------------------------------------------------------ quantize
     codes, aq, sc = pool[0].codes, pool[0].absmax_q, pool[0].absmax_scale

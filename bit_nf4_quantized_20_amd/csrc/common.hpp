@@ -172,4 +172,20 @@ inline size_t decode_u_bytes(int n, int64_t T, int64_t r) { return static_cast<s
 hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const uint16_t* X, int64_t T,
                              int64_t r, float s, uint16_t* Y, int64_t ldy, float* u_ws, hipStream_t st);
 
+// The persistent weight-stream form of the small-token forward
+// (k_decode_stream.hip): one workgroup per CU over contiguous ranges of
+// 16-row blocks, U = X A^T taken from u_ws.  Shapes it takes: in % 4096 == 0,
+// T * in <= kStreamMaxTokElems (the tokens' X fits in LDS), r <= 64, 2 to 8
+// row blocks per CU and at most two projections per workgroup.
+constexpr int64_t kStreamMaxTokElems = 65536;
+bool stream_fits(int n, const int64_t* outs, int64_t in, int64_t T, int64_t r, int num_cus);
+hipError_t launch_decode_stream(const DecodeSet& set, int64_t in, const uint16_t* X, int64_t T, int64_t r,
+                                float s, int64_t ldy, const float* u_ws, int total_rb, int num_cus,
+                                hipStream_t st);
+// U[p][t][k] = sum_i X[t][i] A_p[k][i] (fp32) for the n projections of set
+hipError_t launch_decode_u(const DecodeSet& set, int64_t in, const uint16_t* X, int64_t T, int64_t r,
+                           float* u_ws, hipStream_t st);
+// compute units of the current device (cached per device)
+int device_cus();
+
 }  // namespace qlora

@@ -426,6 +426,26 @@ bool decode_pre_u(int n, const int64_t* outs, int64_t r) {
   return r > 16 || rows / kRows > kDecodeFusedMaxWgs;
 }
 
+hipError_t launch_decode_u(const DecodeSet& set, int64_t in, const uint16_t* X, int64_t T, int64_t r,
+                           float* u_ws, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_u, dim3(static_cast<uint32_t>(r), static_cast<uint32_t>(T), set.n), dim3(256), 0,
+                     st, set, in, X, static_cast<int>(T), static_cast<int>(r), u_ws);
+  return hipGetLastError();
+}
+
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const uint16_t* X, int64_t T,
                              int64_t r, float s, uint16_t* Y, int64_t ldy, float* u_ws, hipStream_t st) {
   if (n < 1 || n > kMaxProj) return hipErrorInvalidValue;
@@ -434,10 +454,6 @@ hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const ui
     if (!decode_fits(T, in, proj[i].out, r)) return hipErrorInvalidValue;
     outs[i] = proj[i].out;
   }
-  const bool pre_u = decode_pre_u(n, outs, r);
-  if (pre_u && u_ws == nullptr) return hipErrorInvalidValue;
-  const dim3 block(kThreads);
-  const int iT = static_cast<int>(T), ir = static_cast<int>(r);
   // all projections in one launch
   DecodeSet set{};
   set.n = n;
@@ -450,10 +466,21 @@ hipError_t launch_decode_fwd(int n, const DecodeProj* proj, int64_t in, const ui
     wgs += proj[i].out / kRows;
     col += proj[i].out;
   }
+  // With a workspace for U, the shapes the weight-stream kernel takes go
+  // there: U = X A^T first, then the stream.
+  const int cus = device_cus();
+  if (u_ws != nullptr && cus > 0 && stream_fits(n, outs, in, T, r, cus)) {
+    hipError_t e = launch_decode_u(set, in, X, T, r, u_ws, st);
+    if (e == hipSuccess)
+      e = launch_decode_stream(set, in, X, T, r, s, ldy, u_ws, static_cast<int>(wgs), cus, st);
+    return e;
+  }
+  const bool pre_u = decode_pre_u(n, outs, r);
+  if (pre_u && u_ws == nullptr) return hipErrorInvalidValue;
+  const dim3 block(kThreads);
+  const int iT = static_cast<int>(T), ir = static_cast<int>(r);
   if (pre_u) {
-    hipLaunchKernelGGL(k_decode_u, dim3(static_cast<uint32_t>(r), static_cast<uint32_t>(T), n), dim3(256),
-                       0, st, set, in, X, iT, ir, u_ws);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_decode_u(set, in, X, T, r, u_ws, st);
     if (e != hipSuccess) return e;
   }
   const dim3 grid(static_cast<uint32_t>(wgs));

@@ -93,7 +93,7 @@ FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
   FwdLayout l{0, 0, 0, 0, 0};
   Carve c;
   if (!dropout && fwd_uses_decode(T, in, outs, n, r)) {
-    if (decode_pre_u(n, outs, r)) l.u_pad = c.take(decode_u_bytes(n, T, r));  // U [n][T][r] fp32
+    l.u_pad = c.take(decode_u_bytes(n, T, r));  // U [n][T][r] fp32
     l.total = c.off;
     return l;
   }
@@ -297,7 +297,12 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   if (int st = check_dropout(keep, p)) return st;
   if (T == 0) return QLORA_OK;
   const FwdLayout lay = fwd_layout(T, in, outs, n, r, dropout);
-  if (lay.total > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
+  // The small-token forward also runs without a workspace where U need not
+  // be computed up front (r <= 16, at most 4096 output rows): ws = NULL
+  // selects its single-launch form.
+  const bool decode_no_ws = !dropout && ws == nullptr && fwd_uses_decode(T, in, outs, n, r) &&
+                            !decode_pre_u(n, outs, r);
+  if (!decode_no_ws && lay.total > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
 
@@ -308,7 +313,7 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
     DecodeProj proj[kMaxProj];
     for (int i = 0; i < n; ++i)
       proj[i] = DecodeProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, A[i], B[i], outs[i]};
-    float* u_ws = lay.total > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + lay.u_pad) : nullptr;
+    float* u_ws = ws != nullptr ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + lay.u_pad) : nullptr;
     return launched(launch_decode_fwd(n, proj, in, X, T, r, scale, Y, N, u_ws, s));
   }
 
