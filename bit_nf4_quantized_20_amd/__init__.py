@@ -10,6 +10,7 @@ Names and semantics follow include/qlora.h:
     nf4_quantize_nodq, nf4_dequantize_nodq,
     qlora_linear_fwd, qlora_linear_bwd, qlora_workspace_bytes_multi, qlora_linear_fwd_multi,
     qlora_linear_bwd_multi, qlora_merge_workspace_bytes, qlora_merge,
+    qlora_noalloc_scratch_bytes, qlora_linear_fwd_noalloc,
     nf4_codebook, nf4_code_thresholds, qlora_status_string
 """
 
@@ -89,6 +90,11 @@ _lib.qlora_linear_fwd_dropout.restype = ctypes.c_int
 _lib.qlora_linear_bwd_dropout.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, ctypes.c_float,
                                           _p, _p, _i64, ctypes.c_float, _p, _p, _p, _p, _sz, _p]
 _lib.qlora_linear_bwd_dropout.restype = ctypes.c_int
+_lib.qlora_noalloc_scratch_bytes.argtypes = []
+_lib.qlora_noalloc_scratch_bytes.restype = _sz
+_lib.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _i64, _p, _p, _i64, ctypes.c_float,
+                                          _p, _p]
+_lib.qlora_linear_fwd_noalloc.restype = ctypes.c_int
 _lib.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
 _lib.nf4_codebook.restype = None
 _lib.nf4_code_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -249,6 +255,24 @@ def qlora_linear_fwd(W: NF4Weight, X, A, B, r: int, alpha: float, Y=None, ws=Non
     wc = W._c()
     _check(_lib.qlora_linear_fwd(ctypes.byref(wc), _ptr(X), T, _ptr(A), _ptr(B), r, float(alpha),
                                  _ptr(Y), _ptr(ws), ws_bytes, _stream(X.device)), "qlora_linear_fwd")
+    return Y
+
+
+def qlora_noalloc_scratch_bytes() -> int:
+    return int(_lib.qlora_noalloc_scratch_bytes())
+
+
+def qlora_linear_fwd_noalloc(W: NF4Weight, X, A, B, r: int, alpha: float, Y):
+    """qlora_linear_fwd on the library's static scratch: Y must be given (the
+    call allocates nothing); calls that overlap on one GPU race."""
+    T = X.shape[0]
+    _need(X, torch.bfloat16, "X", T * W.cols)
+    _need(A, torch.bfloat16, "A", r * W.cols)
+    _need(B, torch.bfloat16, "B", W.rows * r)
+    _need(Y, torch.bfloat16, "Y", T * W.rows)
+    wc = W._c()
+    _check(_lib.qlora_linear_fwd_noalloc(ctypes.byref(wc), _ptr(X), T, _ptr(A), _ptr(B), r, float(alpha),
+                                         _ptr(Y), _stream(X.device)), "qlora_linear_fwd_noalloc")
     return Y
 
 

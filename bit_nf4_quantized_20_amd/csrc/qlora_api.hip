@@ -33,6 +33,27 @@ int check_device() {
   return state == 1 ? QLORA_OK : QLORA_ERR_DEVICE;
 }
 
+// Scratch of qlora_linear_fwd_noalloc: the library's own device memory,
+// sized for the forward's workspace up to kNoAllocScratchBytes.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address of each GPU's copy comes from hipGetSymbolAddress (once per
+// device, cached below) and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr if it cannot be found.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int launched(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
@@ -462,6 +483,23 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
                      const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
                      qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream) {
   return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, ws, ws_bytes, stream);
+}
+
+size_t qlora_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T, const qlora_bf16* A,
+                             const qlora_bf16* B, int64_t r, float alpha, qlora_bf16* Y, qlora_stream stream) {
+  // the size check comes first, before any HIP call: a call whose workspace
+  // would not fit in the library's scratch is refused without side effects
+  if (W == nullptr) return QLORA_ERR_NULL;
+  const size_t need = qlora_workspace_bytes(T, W->cols, W->rows, r, 0);
+  if (need == 0) return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, nullptr, 0, stream);  // shape error
+  if (need > kNoAllocScratchBytes) return QLORA_ERR_WORKSPACE;
+  if (T == 0) return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, nullptr, 0, stream);
+  if (int st = check_device()) return st;
+  void* ws = device_scratch();
+  if (ws == nullptr) return QLORA_ERR_DEVICE;
+  return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, ws, kNoAllocScratchBytes, stream);
 }
 
 int qlora_linear_fwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64_t T,

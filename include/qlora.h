@@ -187,6 +187,31 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
                      qlora_bf16* Y, void* ws, size_t ws_bytes, qlora_stream stream);
 
 /*
+ * qlora_linear_fwd_noalloc -- qlora_linear_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and arguments
+ * without a workspace.  It uses the library's own scratch instead: a static
+ * device array of qlora_noalloc_scratch_bytes() bytes (16 MiB), one copy per
+ * GPU, held until the process ends; the call itself allocates nothing.
+ *   Calls whose workspace (qlora_workspace_bytes(T, in, out, r, 0)) exceeds
+ *   the scratch are refused with QLORA_ERR_WORKSPACE before any HIP call.
+ *   The small-token path (T <= 16) needs at most T x r x 4 bytes and always
+ *   fits; from 2048 tokens on the workspace also holds the dequantized
+ *   weight (2 bytes per weight), so weights above about 8 M elements do not
+ *   fit there: such calls take qlora_linear_fwd with a caller workspace.
+ *   Every call on one GPU shares that GPU's scratch (it needs no
+ *   initialisation and keeps nothing between calls): calls that overlap in
+ *   time on one GPU (different streams, or different host threads without
+ *   ordering) race on it and must not be issued.
+ * Errors: as qlora_linear_fwd, plus WORKSPACE as above and DEVICE if the
+ * scratch cannot be located on the current device.
+ */
+size_t qlora_noalloc_scratch_bytes(void);
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
+                             const qlora_bf16* A, const qlora_bf16* B, int64_t r, float alpha,
+                             qlora_bf16* Y, qlora_stream stream);
+
+/*
  * Multi-projection forms: n (1..8) projections that share the input X and
  * the rank r / alpha, e.g. q|k|v or gate|up (coddykit "LoRA y QLoRA": the
  * adapters go on several target modules of the same layer; ultralytics
