@@ -12,114 +12,230 @@
 namespace qlora {
 
 // ---------------------------------------------------------------------------
-// Quantize: one workgroup per double-quant group (256 blocks = 16384 fp32 =
-// 64 KiB), 256 threads, single HBM pass.  Thread t loads float4 chunks
-// f = i*256 + t (i = 0..15): each load instruction covers 1 KiB contiguous per
-// wave, and the 16 chunks of one 64-weight block sit in 16 adjacent lanes,
-// so the block absmax is a 16-lane DPP max.
+// Quantize: persistent workgroups of 1024 threads, one per CU, each walking
+// double-quant groups g, g + G, g + 2G, ... (G workgroups; a group is 256
+// blocks = 16384 fp32 = 64 KiB).  The next group's loads are issued before
+// the current group's arithmetic, so every CU keeps a group of loads in
+// flight while it computes: one HBM pass, read 4 B and write 0.516 B per
+// weight.
+//
+// Within a group, thread t holds float4 chunks f = i*1024 + t (i = 0..3):
+// each load instruction covers 1 KiB contiguous per wave, and the 16 chunks
+// of one 64-weight block sit in 16 adjacent lanes, so the block absmax is a
+// 16-lane DPP max (on the fp32 bit patterns of |w|, whose unsigned order is
+// the order of the values).
+//
+// Per-block work is spread over the lanes instead of repeated in each of a
+// block's 16: a wave holds 16 blocks (4 chunks x 4 lane groups), and lane
+// l < 16 takes block (i = l % 4, lane group l / 4) for the block reciprocal,
+// the 8-bit absmax code and the absmax store; the reciprocals go back to the
+// lanes through LDS.  The group scale is needed only for the absmax codes,
+// so the codes are stored before the workgroup barrier that forms it.
 // ---------------------------------------------------------------------------
+constexpr int kQThreads = 1024;
+constexpr int kQWaves = kQThreads / 64;
+constexpr int kQChunks = kGroupElems / 4 / kQThreads;  // float4 chunks per thread
+constexpr int kQBlocksPerWave = kQChunks * 4;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+constexpr int kStreamOnce = 2;            // cache policy nt: each weight is read once
+static_assert(kQChunks == 4, "one float4 of block values per lane group");
+
+// the bucket table of the code lookup, copied into LDS by each workgroup
+__constant__ BucketTable kBucketTableDev = kBucketTable;
+
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __builtin_bit_cast(uint32_t, v) & 0x7fffffffu; }
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  return max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xf, 0xf,
+                                                                  false)));
+}
+
+// orders this wave's LDS writes before its later LDS reads
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// floor(X) as an integer (v_cvt_flr_i32_f32; NaN gives 0)
+__device__ __forceinline__ int floor_to_int(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// 4 codes of one chunk from X = 16 w / a, packed into 16 bits
+__device__ __forceinline__ uint32_t bucket_codes(const uint2* s_bucket, const float (&X)[4]) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint2 bk = s_bucket[floor_to_int(X[k]) + 16];
+    const uint32_t c = bk.y + (X[k] > __builtin_bit_cast(float, bk.x) ? 1u : 0u);
+    packed |= c << (4 * k);
+  }
+  return packed;
+}
+
+// Group g's chunks of this thread through a buffer resource over the group:
+// chunks past numel (a ragged last group, or g past the last group) read as
+// zero, without a branch, so the waits for these loads are counted exactly.
+__device__ __forceinline__ void load_group(const float* w, int64_t numel, int64_t g, int t,
+                                           f32x4 (&v)[kQChunks]) {
+  const int64_t rem = numel - g * kGroupElems;
+  const int bytes = rem <= 0 ? 0 : (rem >= kGroupElems ? kGroupElems * 4 : static_cast<int>(rem) * 4);
+  const float* gp = rem > 0 ? w + g * kGroupElems : w;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(gp), 0, bytes,
+                                                                      kBufferWord3);
+#pragma unroll
+  for (int i = 0; i < kQChunks; ++i)
+    v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i * kQThreads + t) * 16, 0,
+                                                                           kStreamOnce));
+}
+
 // kDQ = false: no double quantization; absmax_q and scale are unused and
 // the exact fp32 block absmax goes to absmax[numel/64] (4.5 bits per weight).
 template <bool kDQ>
-__global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ w, int64_t numel,
-                                                      uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ absmax_q,
-                                                      float* __restrict__ scale,
-                                                      float* __restrict__ absmax) {
-  __shared__ float wave_max[4];
-  const int t = threadIdx.x;
-  const int64_t g = blockIdx.x;
-  const int64_t base = g * kGroupElems;
+__global__ __launch_bounds__(kQThreads) void k_nf4_quantize(const float* __restrict__ w, int64_t numel,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ absmax_q,
+                                                            float* __restrict__ scale,
+                                                            float* __restrict__ absmax) {
+  __shared__ uint32_t wave_max[2][kQWaves];  // by group parity: a fast wave may start the next group
+  __shared__ uint2 s_bucket[kBuckets];
+  // per wave: its blocks' absmax values, then their reciprocals; block
+  // (chunk i, lane group q) at slot q * kQChunks + i
+  __shared__ __attribute__((aligned(16))) float s_blk[kQWaves][kQBlocksPerWave];
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int64_t groups = (numel + kGroupElems - 1) / kGroupElems;
+  const int64_t full_groups = numel / kGroupElems;
+  const int64_t stride = gridDim.x;
 
-  f32x4 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t e = base + static_cast<int64_t>(i * 256 + t) * 4;
-    if (e < numel)
-      v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w + e));
-    else
-      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  f32x4 v[kQChunks], vn[kQChunks];
+  int64_t g = blockIdx.x;
+  load_group(w, numel, g, t, v);
+  if (t < 2 * kBuckets) reinterpret_cast<uint32_t*>(s_bucket)[t] = kBucketTableDev.word[t];
+  __syncthreads();
 
-  // Q1: block absmax (exact max of |w|), replicated over the block's 16 lanes
-  float am[16];
-  float tmax = 0.f;
+  for (int par = 0; g < groups; g += stride, par ^= 1) {
+    load_group(w, numel, g + stride, t, vn);  // the next group, in flight during this one
+    const int64_t base = g * kGroupElems;
+    const bool full = g < full_groups;  // every chunk in range (all groups but a ragged last)
+
+    // Q1: block absmax (exact max of |w|), replicated over the block's 16 lanes
+    float am[kQChunks];
+    uint32_t tmax = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float m = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-    m = max16(m);
-    am[i] = m;
-    tmax = fmaxf(tmax, m);
-  }
-  if constexpr (!kDQ) {
-    if ((t & 15) == 0) {
+    for (int i = 0; i < kQChunks; ++i) {
+      uint32_t m = max(max(abs_bits(v[i].x), abs_bits(v[i].y)), max(abs_bits(v[i].z), abs_bits(v[i].w)));
+      m = dpp_max_u32<kDppQuadXor1>(m);
+      m = dpp_max_u32<kDppQuadXor2>(m);
+      m = dpp_max_u32<kDppRowHalfMirror>(m);
+      m = dpp_max_u32<kDppRowMirror>(m);
+      am[i] = __builtin_bit_cast(float, m);
+      tmax = max(tmax, m);
+    }
+    if ((lane & 15) == 0)
+      *reinterpret_cast<f32x4*>(&s_blk[wv][(lane >> 4) * kQChunks]) = f32x4{am[0], am[1], am[2], am[3]};
+    wave_lds_sync();
+    // lane l < 16 owns slot l: chunk i = l % 4 of lane group l / 4, block
+    // i * (kQThreads / 16) + 4 wv + l / 4 of the group (lanes >= 16 repeat it)
+    const int slot = lane % kQBlocksPerWave;
+    const float a_own = s_blk[wv][slot];
+    const int own_blk = (slot % kQChunks) * (kQThreads / 16) + 4 * wv + slot / kQChunks;
+    const bool own_valid = lane < kQBlocksPerWave && base + static_cast<int64_t>(own_blk) * kBlock < numel;
+    const bool own_fast = a_own >= kFastAbsmaxMin && a_own <= kFastAbsmaxMax;
+    const float y_own = 1.0f / (a_own * 0.0625f);
+    wave_lds_sync();  // every lane has read its a_own before the reciprocals overwrite them
+    if (lane < kQBlocksPerWave) s_blk[wv][slot] = y_own;
+    if constexpr (!kDQ) {
+      if (own_valid) absmax[(base >> 6) + own_blk] = a_own;
+    }
+    // the reciprocal path for the whole wave when it covers all its blocks
+    const bool wave_fast = full && __builtin_amdgcn_ballot_w64(!own_fast) == 0;
+    wave_lds_sync();
+    const f32x4 y4 = *reinterpret_cast<const f32x4*>(&s_blk[wv][(lane >> 4) * kQChunks]);
+    wave_lds_sync();  // read before the next group's absmax values overwrite them
+
+    // Q3 + Q4: the code of x = fl32(w / a) = #{j : x > t_j}, taken as the
+    // bucket lookup on X = 16 x, X from the block reciprocal with the exact
+    // correction (both in nf4_format.hpp).  A zero block has X = 0 (code 7).
+    // X stays within [-16, 16] (or is NaN, which converts to bucket 16), so
+    // the bucket index is in 0..32.  4 codes -> 16 bits per chunk.
+    uint16_t* const code_t = reinterpret_cast<uint16_t*>(codes + (base >> 1)) + t;  // chunk i at [i * kQThreads]
+    if (wave_fast) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t e = base + static_cast<int64_t>(i * 256 + t) * 4;
-        if (e < numel) absmax[e >> 6] = am[i];
+      for (int i = 0; i < kQChunks; ++i) {
+        const float b = am[i] * 0.0625f, y = y4[i];
+        const float X[4] = {div_by_reciprocal(v[i].x, b, y), div_by_reciprocal(v[i].y, b, y),
+                            div_by_reciprocal(v[i].z, b, y), div_by_reciprocal(v[i].w, b, y)};
+        code_t[i * kQThreads] = static_cast<uint16_t>(bucket_codes(s_bucket, X));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQChunks; ++i) {
+        if (base + static_cast<int64_t>(i * kQThreads + t) * 4 < numel) {
+          const float a = am[i];
+          float X[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          if (a >= kFastAbsmaxMin && a <= kFastAbsmaxMax) {
+            const float b = a * 0.0625f, y = y4[i];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) X[k] = div_by_reciprocal(X[k], b, y);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) X[k] = a > 0.f ? (X[k] / a) * 16.0f : 0.f;
+          }
+          code_t[i * kQThreads] = static_cast<uint16_t>(bucket_codes(s_bucket, X));
+        }
       }
     }
-  }
-  // group scale s_g = max over the 256 blocks
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  if ((t & 63) == 0) wave_max[t >> 6] = tmax;
-  __syncthreads();
-  const float sg = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
 
-  // Q2: 8-bit absmax codes, q = rne(fl32(fl32(a / s) * 255)); zero group -> 0
-  if (kDQ && (t & 15) == 0) {
+    if constexpr (kDQ) {
+      // group scale s_g = max over the 256 blocks
+      tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), 16)));
+      tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), 32)));
+      if (lane == 0) wave_max[par][wv] = tmax;
+      __syncthreads();
+      uint32_t gm = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t e = base + static_cast<int64_t>(i * 256 + t) * 4;
-      if (e < numel) {
+      for (int k = 0; k < kQWaves; ++k) gm = max(gm, wave_max[par][k]);
+      const float sg = __builtin_bit_cast(float, gm);
+      // Q2: 8-bit absmax codes, q = rne(fl32(fl32(a / s) * 255)); zero group -> 0
+      if (own_valid) {
         uint32_t q = 0;
         if (sg > 0.f) {
-          const float ratio = am[i] / sg;
+          const float ratio = a_own / sg;
           const float scaled = ratio * 255.0f;
           q = static_cast<uint32_t>(__builtin_rintf(scaled));
         }
-        absmax_q[e >> 6] = static_cast<uint8_t>(q);
+        absmax_q[(base >> 6) + own_blk] = static_cast<uint8_t>(q);
       }
+      if (t == 0) scale[g] = sg;
     }
-  }
-  if (kDQ && t == 0) scale[g] = sg;
-
-  // Q3 + Q4: codes from x = fl32(w / a) and the 15 thresholds; a zero block
-  // has x = 0 everywhere (code 7).  4 codes -> 16 bits per chunk.
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t e = base + static_cast<int64_t>(i * 256 + t) * 4;
-    if (e < numel) {
-      const float a = am[i];
-      uint32_t c0, c1, c2, c3;
-      if (a > 0.f) {
-        c0 = nf4_code(v[i].x / a);
-        c1 = nf4_code(v[i].y / a);
-        c2 = nf4_code(v[i].z / a);
-        c3 = nf4_code(v[i].w / a);
-      } else {
-        c0 = c1 = c2 = c3 = 7u;
-      }
-      const uint16_t packed = static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-      *reinterpret_cast<uint16_t*>(codes + (e >> 1)) = packed;
-    }
+    for (int i = 0; i < kQChunks; ++i) v[i] = vn[i];
   }
+}
+
+// one workgroup per CU (fewer for small tensors)
+static uint32_t quantize_grid(int64_t numel) {
+  const int64_t groups = ceil_div(numel, kGroupElems);
+  const int cus = device_cus();
+  const int64_t g = cus > 0 && groups > cus ? cus : groups;
+  return static_cast<uint32_t>(g);
 }
 
 hipError_t launch_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
                                float* scale, hipStream_t s) {
-  const int64_t groups = ceil_div(numel, kGroupElems);
-  hipLaunchKernelGGL(k_nf4_quantize<true>, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, w,
-                     numel, codes, absmax_q, scale, nullptr);
+  hipLaunchKernelGGL(k_nf4_quantize<true>, dim3(quantize_grid(numel)), dim3(kQThreads), 0, s, w, numel, codes,
+                     absmax_q, scale, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
                                     hipStream_t s) {
-  const int64_t groups = ceil_div(numel, kGroupElems);
-  hipLaunchKernelGGL(k_nf4_quantize<false>, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, w,
-                     numel, codes, nullptr, nullptr, absmax);
+  hipLaunchKernelGGL(k_nf4_quantize<false>, dim3(quantize_grid(numel)), dim3(kQThreads), 0, s, w, numel, codes,
+                     nullptr, nullptr, absmax);
   return hipGetLastError();
 }
 

@@ -76,13 +76,81 @@ static_assert(kThresholds.t[6] < 0.0f && kThresholds.t[7] > 0.0f, "zero must be 
 static_assert(__builtin_bit_cast(uint32_t, kThresholds.t[0]) == 0xbf591cd9u, "t0");
 static_assert(__builtin_bit_cast(uint32_t, kThresholds.t[14]) == 0x3f5c89d9u, "t14");
 
-// code(x) for x = fl32(w / absmax), |x| <= 1
-__device__ __forceinline__ uint32_t nf4_code(float x) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < 15; ++j) c += (x > kThresholds.t[j]) ? 1u : 0u;
-  return c;
+// ---------------------------------------------------------------------------
+// The quantizer's per-weight arithmetic without a division or 15 comparisons.
+//
+// Quotient.  The code depends on x = fl32(w / a) only through comparisons
+// with the thresholds, so the kernel needs x exactly.  It works on
+// X = fl32(w / b) with b = a / 16, which is 16 x exactly (scaling by a power
+// of two commutes with rounding away from underflow), and with the block's
+// y = fl32(1 / b), one IEEE division per block:
+//   q0 = fl(w y) is within 1.5 ulp of w / b;
+//   q1 = fl(q0 + fl(w - b q0) y) is then a faithful quotient;
+//   with y correctly rounded and q1 faithful, w - b q1 is exact (one fma)
+//   and fl(q1 + (w - b q1) y) is the correctly rounded w / b (Markstein's
+//   theorem on division by fused multiply-add, as given in Muller et al.,
+//   Handbook of Floating-Point Arithmetic, chapter on FMA-based division).
+// The theorem needs y normal and the remainder representable: for
+// 2^-90 <= a <= 2^120 and |X| >= 1/2 (all thresholds lie beyond 0.63 in X)
+// the remainder is a multiple of 2^-141, exact even if subnormal; smaller |X|
+// is code 7 whatever its last bits.  Blocks outside that range (far from
+// any real weight block) divide directly.
+//
+// Lookup.  code(X) = #{j : X > 16 t_j}.  The thresholds are at least 0.08
+// apart, more than the 1/16 that one unit of X spans, so each interval
+// [k, k + 1), k = -16..16, holds at most one scaled threshold: with base_k
+// the number below the interval and thr_k the one inside it (+inf if none),
+// code(X) = base_k + (X > thr_k), k = floor(X).  X = 16 (the block maximum)
+// falls in k = 16.
+// ---------------------------------------------------------------------------
+constexpr float kFastAbsmaxMin = 0x1p-90f;
+constexpr float kFastAbsmaxMax = 0x1p120f;
+
+// fl32(w / b) from y = fl32(1 / b), for b and w as above
+__host__ __device__ inline float div_by_reciprocal(float w, float b, float y) {
+  float q = w * y;
+  float r = __builtin_fmaf(-b, q, w);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-b, q, w);
+  return __builtin_fmaf(r, y, q);
 }
+
+constexpr int kBuckets = 33;  // k = -16..16 at index k + 16
+struct BucketTable {
+  uint32_t word[2 * kBuckets];  // entry i: word[2i] = fp32 bits of thr, word[2i + 1] = base
+};
+
+namespace detail {
+constexpr float scaled_threshold(int j) { return 16.0f * kThresholds.t[j]; }
+constexpr BucketTable make_buckets() {
+  BucketTable tb{};
+  for (int i = 0; i < kBuckets; ++i) {
+    const float lo = static_cast<float>(i - 16), hi = lo + 1.0f;
+    uint32_t base = 0;
+    float thr = __builtin_inff();
+    for (int j = 0; j < 15; ++j) {
+      const float T = scaled_threshold(j);
+      if (T < lo) ++base;
+      else if (T < hi) thr = T;
+    }
+    tb.word[2 * i] = __builtin_bit_cast(uint32_t, thr);
+    tb.word[2 * i + 1] = base;
+  }
+  return tb;
+}
+// at most one scaled threshold per unit interval, and scaling by 16 exact
+constexpr bool buckets_hold_one_threshold() {
+  for (int j = 0; j < 15; ++j) {
+    if (j > 0 && scaled_threshold(j) - scaled_threshold(j - 1) <= 1.0f) return false;
+    if (scaled_threshold(j) / 16.0f != kThresholds.t[j]) return false;
+  }
+  return true;
+}
+}  // namespace detail
+
+static_assert(detail::buckets_hold_one_threshold(), "bucket lookup needs thresholds > 1/16 apart");
+constexpr BucketTable kBucketTable = detail::make_buckets();
+static_assert(kBucketTable.word[2 * 32 + 1] == 15 && kBucketTable.word[2 * 16 + 1] == 7, "bucket bases");
 
 // ---------------------------------------------------------------------------
 // bf16 helpers

@@ -587,6 +587,13 @@ void nf4_code_thresholds(float out[15]) {
   for (int j = 0; j < 15; ++j) out[j] = kThresholds.t[j];
 }
 
+void nf4_code_buckets(float thr[33], uint32_t base[33]) {
+  for (int i = 0; i < kBuckets; ++i) {
+    thr[i] = __builtin_bit_cast(float, kBucketTable.word[2 * i]);
+    base[i] = kBucketTable.word[2 * i + 1];
+  }
+}
+
 const char* qlora_status_string(int status) {
   switch (status) {
     case QLORA_OK: return "ok";

@@ -329,6 +329,16 @@ void nf4_codebook(float out[16]);
  */
 void nf4_code_thresholds(float out[15]);
 
+/*
+ * Host copy of the bucket table the quantize kernel looks codes up in.  The
+ * kernel works on X = fl32(16 w / a) = 16 x; for k = floor(X) in -16..16,
+ * entry k + 16 holds base[k + 16], the number of scaled thresholds 16 t[j]
+ * below k, and thr[k + 16], the one scaled threshold in [k, k + 1) (+inf if
+ * none); code = base + (X > thr), which equals the rule above.  Exposed so
+ * that equality can be checked exhaustively on the CPU.
+ */
+void nf4_code_buckets(float thr[33], uint32_t base[33]);
+
 /* Static description of a status code. */
 const char* qlora_status_string(int status);
 

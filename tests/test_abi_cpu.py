@@ -78,8 +78,9 @@ def _thresholds():
 @pytest.mark.slow
 def test_threshold_rule_equals_argmin_on_every_fp32_in_unit_interval():
     # Exhaustive: every fp32 x in [-1, 1] (both signs, ~2.1e9 values).  The
-    # library's rule code = #{j : x > t_j} must equal the oracle's first-argmin
-    # of |fl32(x - L_j)|.
+    # library's rule code = #{j : x > t_j}, and the quantize kernel's bucket
+    # lookup on X = 16 x, must both equal the oracle's first-argmin of
+    # |fl32(x - L_j)|.
     thr = _thresholds()
     assert np.all(np.diff(thr) > 0)
     L = ocodebook.nf4_levels()
@@ -95,6 +96,9 @@ def test_threshold_rule_equals_argmin_on_every_fp32_in_unit_interval():
             got = np.searchsorted(thr, x, side="left").astype(np.uint8)
             bad = np.nonzero(got != ref)[0]
             assert bad.size == 0, (hex(int(bits[bad[0]])), int(got[bad[0]]), int(ref[bad[0]]))
+            got = _bucket_codes(x)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, ("bucket", hex(int(bits[bad[0]])), int(got[bad[0]]), int(ref[bad[0]]))
             start += n
 
 
@@ -109,6 +113,49 @@ def test_threshold_rule_near_every_boundary():
         x = np.arange(lo, lo + 131072, dtype=np.uint64).astype(np.uint32).view(np.float32)
         got = np.searchsorted(thr, x, side="left")
         assert np.array_equal(got, ref)
+
+
+def _buckets():
+    lib = _lib()
+    thr, base = (ctypes.c_float * 33)(), (ctypes.c_uint32 * 33)()
+    lib.nf4_code_buckets(thr, base)
+    return np.frombuffer(thr, dtype=np.float32).copy(), np.frombuffer(base, dtype=np.uint32).copy()
+
+
+def _bucket_codes(x):
+    # the kernel's lookup on X = 16 x (exact: a power-of-two scaling of |x| <= 1)
+    thr, base = _buckets()
+    X = x.astype(np.float32) * np.float32(16)
+    k = np.floor(X).astype(np.int64) + 16
+    return (base[k] + (X > thr[k])).astype(np.uint8)
+
+
+def test_bucket_table_holds_each_threshold_once():
+    thr, base = _buckets()
+    t16 = _thresholds() * np.float32(16)
+    inside = np.isfinite(thr)
+    assert np.array_equal(np.sort(thr[inside]), t16)
+    for i in range(33):
+        lo = i - 16
+        assert base[i] == np.count_nonzero(t16 < lo)
+        if inside[i]:
+            assert lo <= thr[i] < lo + 1
+
+
+def test_bucket_rule_near_every_threshold_and_bucket_edge():
+    # fast version: +-65536 ulps around every threshold and every bucket
+    # edge k / 16
+    L = ocodebook.nf4_levels()
+    points = list(_thresholds()) + [np.float32(k / 16) for k in range(-16, 17)]
+    starts = []
+    for p in points:
+        b = int(np.float32(p).view(np.uint32))
+        starts += [0, 0x80000000] if p == 0 else [b - 65536]
+    for lo in starts:
+        ref = onative.nearest_level_of_bits(lo, 131072, L)
+        x = np.arange(lo, lo + 131072, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        keep = np.abs(x) <= 1
+        assert np.array_equal(_bucket_codes(x[keep]), ref[keep]), hex(lo)
 
 
 # ---------------------------------------------------------------- host validation

@@ -90,6 +90,54 @@ def test_edge_blocks():
     _assert_bits_equal(host_bits(back), onf4.dequantize(rc, raq, rsc), "dequant")
 
 
+def _near_threshold_blocks(seed, absmax):
+    """One 64-weight block per absmax value: w[0] = a (the block maximum), the
+    rest within 3 ulps of fl32(m * a), m the exact midpoint between a code
+    threshold and the next fp32 -- the quotients where fl32(w / a) decides
+    the code -- with random signs of the offsets."""
+    rng = np.random.default_rng(seed)
+    import bit_nf4_quantized_20_amd as q
+    thr = np.array(q.nf4_code_thresholds(), dtype=np.float32)
+    mids = (thr.astype(np.float64) + np.nextafter(thr, np.float32(np.inf)).astype(np.float64)) / 2
+    out = np.zeros((len(absmax), 64), dtype=np.float32)
+    for b, a in enumerate(absmax):
+        a = np.float32(a)
+        j = rng.integers(0, 15, 63)
+        w = (mids[j] * np.float64(a)).astype(np.float32)  # m a exact in fp64, one rounding
+        w = (w.view(np.int32) + rng.integers(-3, 4, 63).astype(np.int32)).view(np.float32)
+        w = np.where(np.abs(w) <= a, w, np.float32(0))
+        out[b, 0] = a
+        out[b, 1:] = w
+    return out.reshape(-1)
+
+
+def test_quantize_near_thresholds_bit_exact():
+    # quotients at the code decision points, absmax across the range the
+    # kernel takes with its reciprocal (2^-90 .. 2^120, both ends) and beyond
+    # it (direct division): 3 full groups plus a ragged one, the out-of-range
+    # blocks in the second group only, so the first group runs the
+    # whole-wave reciprocal path
+    q = require_gpu()
+    banner("quantize near thresholds")
+    rng = np.random.default_rng(21)
+    nblk = 3 * 256 + 37
+    e = rng.integers(-89, 120, nblk).astype(np.float64)
+    absmax = (2.0 ** e * rng.uniform(1, 2, nblk)).astype(np.float32)
+    absmax[0], absmax[1] = np.float32(2.0 ** -90), np.float32(2.0 ** 120)
+    edge = [2.0 ** -91, 2.0 ** -126, 1e-40, 2.0 ** 121, 3e38, 0.0, 0.037, 1.0]
+    absmax[256:256 + len(edge)] = np.array(edge, dtype=np.float32)
+    w = _near_threshold_blocks(22, absmax)  # absmax 0.0: a zero block
+    (codes, aq, sc), (rc, raq, rsc), dev = _quant_both(q, w)
+    _assert_bits_equal(codes, rc, "codes")
+    _assert_bits_equal(aq, raq, "absmax_q")
+    _assert_bits_equal(sc, rsc, "scale")
+    codes2, absmax2 = q.nf4_quantize_nodq(dev_f32(w))
+    torch.cuda.synchronize()
+    rc2, ra2 = onf4.quantize_nodq(w, nearest=onative.nearest_level)
+    _assert_bits_equal(host(codes2), rc2, "nodq codes")
+    _assert_bits_equal(host(absmax2), ra2, "nodq absmax")
+
+
 def test_tiny_absmax_block_gives_signed_zero():
     # a block whose 8-bit absmax code rounds to 0 dequantizes to +-0 (sign of
     # the level), bit-exactly as IEEE multiplication gives it
