@@ -137,6 +137,12 @@ hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* scale,
                         int64_t out, int64_t in, const uint16_t* Bp, const uint16_t* Atp,
                         int64_t ldp, int64_t rp, float s, uint16_t* w_out, hipStream_t st);
+// r <= 64 with r % 8 == 0: B [out][r] and A [r][in] read as they are (no
+// padded copies)
+bool merge_direct(int64_t r);
+hipError_t launch_merge_direct(const uint8_t* codes, const uint8_t* absmax_q, const float* scale, int64_t out,
+                               int64_t in, const uint16_t* B, const uint16_t* A, int64_t r, float s,
+                               uint16_t* w_out, hipStream_t st);
 
 // Small-token forward (T <= 16, r <= 64): Y = X W_hat^T + s (X A^T) B^T.
 // decode_fits() lists the shapes it takes.  For r <= 16 and at most

@@ -568,6 +568,9 @@ int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16
   if (int st = check_device()) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (merge_direct(r))
+    return launched(launch_merge_direct(W->codes, W->absmax_q, W->absmax_scale, out, in, B, A, r,
+                                        alpha / static_cast<float>(r), W_out, s));
   const int64_t rp = padded_rank(r);
   uint16_t* b_pad = static_cast<uint16_t*>(ws);
   uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + round_up(out * rp * 4, 256));

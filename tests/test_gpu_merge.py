@@ -46,6 +46,8 @@ def _run(q, w, A, B, r, alpha):
     (256, 256, 8, 16.0),       # the single-linear shape
     (192, 320, 12, 24.0),      # in not a multiple of the 256-column tile, r not of 16
     (64, 64, 256, 8.0),        # largest rank
+    (320, 448, 24, 48.0),      # A and B read directly (r % 8 == 0), a partly live column strip
+    (128, 512, 72, 144.0),     # padded factors, rank in two 64-wide chunks
     (14336, 4096, 64, 128.0),  # 8B MLP gate at full size
 ])
 def test_merge_matches_oracle(n_out, n_in, r, alpha):
