@@ -306,13 +306,16 @@ size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, in
  *   W_out = bf16(W_hat + (alpha/r) B A)          [out, in] bf16
  * (coddykit "LoRA y QLoRA": the adapter is merged into the base with
  * merge_and_unload; ultralytics glossary "QLoRA", "Compromissos": the 4-bit
- * base must be dequantized to 16 bits first).  Per element one rounding:
- * bf16_rne(fl32(w_hat + fl32(s * sum_j B[m][j] A[j][n]))) with w_hat exactly
- * as nf4_dequantize produces it and the rank-r sum accumulated in fp32.
+ * base must be dequantized to 16 bits first).  Per element:
+ * bf16_rne(fma(s, sum_j B[m][j] A[j][n], w_hat)) with w_hat exactly as
+ * nf4_dequantize produces it, the rank-r sum accumulated in fp32 and added,
+ * scaled, with one fp32 rounding; then one bf16 rounding.
  *   W      NF4 weight [out, in]; in % 64 == 0, out % 64 == 0
  *   A      [r, in] bf16;  B [out, r] bf16;  1 <= r <= 256;  alpha finite
  *   W_out  [out, in] bf16 out (row-major)
  *   ws     workspace of ws_bytes >= qlora_merge_workspace_bytes(in, out, r)
+ *          (zero-padded copies of B and A^T; for r <= 64 with r % 8 == 0 the
+ *          kernel reads A and B as they are and leaves ws untouched)
  * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE, LAUNCH.
  */
 int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16* B, int64_t r,
