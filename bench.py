@@ -40,6 +40,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 DROPOUT_P = 0.05  # the lora_dropout value the pages configure
 NF4_BYTES_PER_WEIGHT = 0.515869140625
+# untimed calls before a standalone timing: short kernels run on clocks that
+# are still ramping for the first tens of milliseconds of sustained load
+WARM_CALLS = 30
 
 
 def parse():
@@ -60,6 +63,10 @@ def parse():
                          "3 = 8B MLP, 4 = 8B attention, 5 = 70B MLP) and print its figures (for "
                          "rocprofv3 --pmc passes over the large-token GEMMs)")
     ap.add_argument("--probe-workload", type=int, default=3, choices=(3, 4, 5))
+    ap.add_argument("--only-leg", choices=("quantize", "merge"),
+                    help="only run one standalone leg (the 2^30 flat quantize, or the 8B and 70B gate "
+                         "merges) and then the 256 MiB copy, and print its figures (for rocprofv3 "
+                         "kernel-trace and --pmc FETCH_SIZE / WRITE_SIZE passes)")
     return ap.parse_args()
 
 
@@ -121,12 +128,23 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[2]
-    proj = wl.projections[0]
-    n_out, n_in, r, alpha = proj.out_features, proj.in_features, wl.r, wl.alpha
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.only_leg:
+        if args.only_leg == "quantize":
+            res = {"quantize_flat_2pow30": flat_quantize_leg(q, synth, dev, False)}
+        else:
+            res = {"merge_8b_gate": merge_leg(q, synth, dev, bf, 3),
+                   "merge_70b_gate": merge_leg(q, synth, dev, bf, 5)}
+        copy_calibration(dev)
+        print(json.dumps(res), flush=True)
+        return
+
+    wl = synth.WORKLOADS[2]
+    proj = wl.projections[0]
+    n_out, n_in, r, alpha = proj.out_features, proj.in_features, wl.r, wl.alpha
 
     # ---------------------------------------------------------------- inputs
     w_host = synth.weight(2, 0, n_out, n_in)
@@ -233,7 +251,7 @@ def main():
 
     # ------------------------------------------------------------ quantize
     codes, aq, sc = pool[0].codes, pool[0].absmax_q, pool[0].absmax_scale
-    for _ in range(3):
+    for _ in range(WARM_CALLS):
         q.nf4_quantize(w_dev, codes, aq, sc)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -250,7 +268,7 @@ def main():
 
     # standalone dequantize (D1) and the format without double quantization
     def per_call_us(fn, n=50):
-        for _ in range(3):
+        for _ in range(WARM_CALLS):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -276,7 +294,8 @@ def main():
                                "dequantize_GB_per_s": round(nw * 2.5625 / (us_dn * 1e-6) / 1e9, 1)}
 
     # ------------------------------------------------------ adapter merge
-    extra["merge_8b_gate"] = merge_leg(q, synth, dev, bf)
+    extra["merge_8b_gate"] = merge_leg(q, synth, dev, bf, 3)
+    extra["merge_70b_gate"] = merge_leg(q, synth, dev, bf, 5)
 
     # ------------------------------------------- q|k|v at decode sizes
     extra["qkv8b_decode"] = qkv_decode_leg(q, synth, dev, bf)
@@ -444,26 +463,26 @@ def mlp_decode_leg(q, synth, dev, bf, n=96):
     return res
 
 
-def merge_leg(q, synth, dev, bf):
-    """qlora_merge of the 8B-MLP gate projection (14336 x 4096 NF4, r = 64):
-    W_merged = bf16(W_hat + (alpha/r) B A), HBM-bound (codes + absmax read,
-    2 B per weight written)."""
+def merge_leg(q, synth, dev, bf, wid):
+    """qlora_merge of an MLP gate projection (8B: 14336 x 4096, 70B:
+    28672 x 8192, NF4, r = 64): W_merged = bf16(W_hat + (alpha/r) B A),
+    HBM-bound (codes + absmax read, 2 B per weight written)."""
     import torch
-    wl = synth.WORKLOADS[3]
+    wl = synth.WORKLOADS[wid]
     p = wl.projections[0]
     r, alpha = wl.r, wl.alpha
     n_out, n_in = p.out_features, p.in_features
-    W = q.nf4_quantize_weight(torch.from_numpy(synth.weight(3, 0, n_out, n_in)).to(dev))
-    A = bf(synth.lora_A(3, 0, r, n_in))
-    B = bf(synth.lora_B(3, 0, n_out, r))
+    W = q.nf4_quantize_weight(torch.from_numpy(synth.weight(wid, 0, n_out, n_in)).to(dev))
+    A = bf(synth.lora_A(wid, 0, r, n_in))
+    B = bf(synth.lora_B(wid, 0, n_out, r))
     out = torch.empty(n_out, n_in, dtype=torch.bfloat16, device=dev)
     ws = q.make_workspace(q.qlora_merge_workspace_bytes(n_in, n_out, r), dev)
-    for _ in range(3):
+    for _ in range(WARM_CALLS):
         q.qlora_merge(W, A, B, r, alpha, out=out, ws=ws)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    n = 20
+    n = 40
     for _ in range(n):
         q.qlora_merge(W, A, B, r, alpha, out=out, ws=ws)
     e1.record()
@@ -483,14 +502,22 @@ def counters_probe(q, pool, X, Y, A, B, r, alpha, ws, dev):
     import torch
     for W in pool:
         q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=ws)
+    copy_calibration(dev)
+    print(json.dumps({"probe": "decode T=16 x %d, copy %d B x 4" % (len(pool), COPY_BYTES),
+                      "sources_sha256": decode_fingerprint()}), flush=True)
+
+
+def copy_calibration(dev):
+    """Four plain 256 MiB fp32 copies (torch.neg into a second buffer:
+    COPY_BYTES read and COPY_BYTES written each), whose FETCH_SIZE /
+    WRITE_SIZE readings calibrate the counters' scale."""
+    import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(4):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"probe": "decode T=16 x %d, copy %d B x 4" % (len(pool), COPY_BYTES),
-                      "sources_sha256": decode_fingerprint()}), flush=True)
 
 
 def train_leg(q, synth, dev, bf, plain):
@@ -793,7 +820,8 @@ def flat_quantize_leg(q, synth, dev, with_oracle):
     """nf4_quantize of a 2^30-element fp32 tensor (N(0, 0.02)): the seeded
     recipe's first 2^26 draws (seed 5000) repeated 16 times on the device
     (the quantize cost depends only on the value distribution).  4 B read and
-    0.515869 B written per weight.  Timed over 5 calls after 2 untimed ones;
+    0.515869 B written per weight.  Timed over 10 calls after 20 untimed
+    ones (the clocks settle under sustained load);
     the oracle (NumPy + the plain-C nearest-level search) quantizes a 2^24
     sample of the same draws on the host, scaled to 2^30 elements."""
     import numpy as np
@@ -802,11 +830,12 @@ def flat_quantize_leg(q, synth, dev, with_oracle):
     part = synth.normal_f32(synth.FLAT_QUANTIZE_SEED, (1 << 26,), synth.W_STD)
     w = torch.from_numpy(part).to(dev).repeat(n // part.size)
     codes, aq, sc = q.nf4_quantize(w)
-    q.nf4_quantize(w, codes, aq, sc)
+    for _ in range(20):
+        q.nf4_quantize(w, codes, aq, sc)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    k = 5
+    k = 10
     for _ in range(k):
         q.nf4_quantize(w, codes, aq, sc)
     e1.record()
