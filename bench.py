@@ -70,14 +70,23 @@ def parse():
     return ap.parse_args()
 
 
-# Sources that define the small-token forward kernel; the HBM traffic recorded
-# from hardware counters is reported only while they are unchanged.
+# Sources that define the small-token forward kernel, and the compile flags
+# (bit_nf4_quantized_20_amd/build.py: flags()); the HBM traffic recorded from
+# hardware counters is reported only while they are unchanged.
 DECODE_SOURCES = ("bit_nf4_quantized_20_amd/csrc/k_decode.hip",
                   "bit_nf4_quantized_20_amd/csrc/nf4_format.hpp",
-                  "bit_nf4_quantized_20_amd/csrc/common.hpp",
-                  "bit_nf4_quantized_20_amd/build.py")
+                  "bit_nf4_quantized_20_amd/csrc/common.hpp")
 TRAFFIC_RECORD = "profiles/k_decode_fwd_split_qproj4096x4096_T16_traffic.md"
 COPY_BYTES = 256 << 20
+
+
+def compile_flags():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "qlora_build", os.path.join(ROOT, "bit_nf4_quantized_20_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return " ".join(mod.flags())
 
 
 def decode_fingerprint():
@@ -86,6 +95,7 @@ def decode_fingerprint():
     for rel in DECODE_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(compile_flags().encode())
     return h.hexdigest()
 
 

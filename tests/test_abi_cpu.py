@@ -16,7 +16,8 @@ from oracle import storage as ostorage
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora.h")
-LIB = os.path.join(ROOT, "bit_nf4_quantized_20_amd", "libqlora.so")
+# QLORA_ABI_LIB selects another build of the library (the sanitized one)
+LIB = os.environ.get("QLORA_ABI_LIB") or os.path.join(ROOT, "bit_nf4_quantized_20_amd", "libqlora.so")
 
 
 def _lib():
