@@ -10,7 +10,8 @@ Names and semantics follow include/qlora.h:
     nf4_quantize_nodq, nf4_dequantize_nodq,
     qlora_linear_fwd, qlora_linear_bwd, qlora_workspace_bytes_multi, qlora_linear_fwd_multi,
     qlora_linear_bwd_multi, qlora_merge_workspace_bytes, qlora_merge,
-    qlora_noalloc_scratch_bytes, qlora_linear_fwd_noalloc,
+    qlora_noalloc_scratch_bytes, qlora_linear_fwd_noalloc, qlora_workspace_bytes_flags,
+    nf4_quantize_weight_nodq, nf4_code_buckets,
     nf4_codebook, nf4_code_thresholds, qlora_status_string
 """
 
@@ -46,7 +47,10 @@ _sz = ctypes.c_size_t
 
 class _NF4WeightC(ctypes.Structure):
     _fields_ = [("codes", _p), ("absmax_q", _p), ("absmax_scale", _p), ("rows", _i64),
-                ("cols", _i64)]
+                ("cols", _i64), ("flags", ctypes.c_uint32)]
+
+
+QLORA_NF4_ABSMAX_FP32 = 0x1  # qlora_nf4_weight.flags: the 4.5-bit format (fp32 block absmax)
 
 
 _lib.nf4_storage_bytes.argtypes = [_i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
@@ -90,6 +94,11 @@ _lib.qlora_linear_fwd_dropout.restype = ctypes.c_int
 _lib.qlora_linear_bwd_dropout.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _p, _i64, _p, ctypes.c_float,
                                           _p, _p, _i64, ctypes.c_float, _p, _p, _p, _p, _sz, _p]
 _lib.qlora_linear_bwd_dropout.restype = ctypes.c_int
+_lib.qlora_workspace_bytes_flags.argtypes = [_i64, _i64, ctypes.POINTER(_i64), ctypes.c_int, _i64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_uint32]
+_lib.qlora_workspace_bytes_flags.restype = _sz
+_lib.nf4_code_buckets.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_uint32)]
+_lib.nf4_code_buckets.restype = None
 _lib.qlora_noalloc_scratch_bytes.argtypes = []
 _lib.qlora_noalloc_scratch_bytes.restype = _sz
 _lib.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_NF4WeightC), _p, _i64, _p, _p, _i64, ctypes.c_float,
@@ -134,16 +143,21 @@ def _need(t: torch.Tensor, dtype, name: str, numel: int = None):
 
 @dataclass
 class NF4Weight:
-    """Frozen NF4 weight [rows = out_features, cols = in_features]."""
+    """Frozen NF4 weight [rows = out_features, cols = in_features].  flags 0:
+    double-quantized (absmax_q uint8 per block, absmax_scale fp32 per 256
+    blocks); QLORA_NF4_ABSMAX_FP32: the 4.5-bit format (absmax_q None,
+    absmax_scale the fp32 absmax of each block)."""
     codes: torch.Tensor          # uint8 [rows*cols/2]
-    absmax_q: torch.Tensor       # uint8 [rows*cols/64]
-    absmax_scale: torch.Tensor   # float32 [ceil(rows*cols/16384)]
+    absmax_q: torch.Tensor       # uint8 [rows*cols/64], or None (4.5-bit format)
+    absmax_scale: torch.Tensor   # float32 [ceil(rows*cols/16384)], or [rows*cols/64]
     rows: int
     cols: int
+    flags: int = 0
 
     def _c(self):
-        return _NF4WeightC(self.codes.data_ptr(), self.absmax_q.data_ptr(),
-                           self.absmax_scale.data_ptr(), self.rows, self.cols)
+        q = None if self.absmax_q is None else self.absmax_q.data_ptr()
+        return _NF4WeightC(self.codes.data_ptr(), q, self.absmax_scale.data_ptr(), self.rows, self.cols,
+                           self.flags)
 
 
 def nf4_storage_bytes(numel: int):
@@ -179,6 +193,15 @@ def nf4_quantize_weight(w: torch.Tensor) -> NF4Weight:
         raise ValueError("weight must be 2-D [out, in]")
     c, q, s = nf4_quantize(w)
     return NF4Weight(c, q, s, w.shape[0], w.shape[1])
+
+
+def nf4_quantize_weight_nodq(w: torch.Tensor) -> NF4Weight:
+    """Quantizes a [out, in] fp32 weight into an NF4Weight of the 4.5-bit
+    format (exact fp32 block absmax, no double quantization)."""
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D [out, in]")
+    c, a = nf4_quantize_nodq(w)
+    return NF4Weight(c, None, a, w.shape[0], w.shape[1], QLORA_NF4_ABSMAX_FP32)
 
 
 def nf4_dequantize(codes, absmax_q, absmax_scale, numel: int, out=None):
@@ -229,10 +252,17 @@ def make_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def _workspace(ws, T, n_in, n_out, r, backward, device):
+def qlora_workspace_bytes_flags(T: int, in_features: int, out_features, r: int, backward: bool,
+                                dropout: bool = False, flags: int = 0) -> int:
+    outs = (_i64 * len(out_features))(*[int(o) for o in out_features])
+    return int(_lib.qlora_workspace_bytes_flags(T, in_features, outs, len(out_features), r,
+                                                1 if backward else 0, 1 if dropout else 0, flags))
+
+
+def _workspace(ws, T, n_in, n_out, r, backward, device, flags=0):
     """Caller's workspace, or a cached one per (device, stream) that grows as
     needed (concurrent streams get separate buffers)."""
-    need = qlora_workspace_bytes(T, n_in, n_out, r, backward)
+    need = qlora_workspace_bytes_flags(T, n_in, [n_out], r, backward, False, flags)
     if ws is None:
         key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
         ws = _WS_CACHE.get(key)
@@ -251,7 +281,7 @@ def qlora_linear_fwd(W: NF4Weight, X, A, B, r: int, alpha: float, Y=None, ws=Non
     if Y is None:
         Y = torch.empty(T, W.rows, dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, "Y", T * W.rows)
-    ws, ws_bytes = _workspace(ws, T, W.cols, W.rows, r, False, X.device)
+    ws, ws_bytes = _workspace(ws, T, W.cols, W.rows, r, False, X.device, W.flags)
     wc = W._c()
     _check(_lib.qlora_linear_fwd(ctypes.byref(wc), _ptr(X), T, _ptr(A), _ptr(B), r, float(alpha),
                                  _ptr(Y), _ptr(ws), ws_bytes, _stream(X.device)), "qlora_linear_fwd")
@@ -294,7 +324,7 @@ def qlora_linear_bwd(W: NF4Weight, X, dY, A, B, r: int, alpha: float, dX=None, d
     _need(dX, torch.bfloat16, "dX", T * W.cols)
     _need(dA, torch.float32, "dA", r * W.cols)
     _need(dB, torch.float32, "dB", W.rows * r)
-    ws, ws_bytes = _workspace(ws, T, W.cols, W.rows, r, True, dev)
+    ws, ws_bytes = _workspace(ws, T, W.cols, W.rows, r, True, dev, W.flags)
     wc = W._c()
     _check(_lib.qlora_linear_bwd(ctypes.byref(wc), _ptr(X), _ptr(dY), T, _ptr(A), _ptr(B), r,
                                  float(alpha), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
@@ -307,8 +337,8 @@ def qlora_workspace_bytes_dropout(T: int, in_features: int, out_features: int, r
     return int(_lib.qlora_workspace_bytes_dropout(T, in_features, out_features, r, 1 if backward else 0))
 
 
-def _dropout_ws(ws, T, n_in, n_out, r, backward, device):
-    need = qlora_workspace_bytes_dropout(T, n_in, n_out, r, backward)
+def _dropout_ws(ws, T, n_in, n_out, r, backward, device, flags=0):
+    need = qlora_workspace_bytes_flags(T, n_in, [n_out], r, backward, True, flags)
     if ws is None:
         key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
         ws = _WS_CACHE.get(key)
@@ -330,7 +360,7 @@ def qlora_linear_fwd_dropout(W: NF4Weight, X, keep, p: float, A, B, r: int, alph
     if Y is None:
         Y = torch.empty(T, W.rows, dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, "Y", T * W.rows)
-    ws, ws_bytes = _dropout_ws(ws, T, W.cols, W.rows, r, False, X.device)
+    ws, ws_bytes = _dropout_ws(ws, T, W.cols, W.rows, r, False, X.device, W.flags)
     wc = W._c()
     _check(_lib.qlora_linear_fwd_dropout(ctypes.byref(wc), _ptr(X), T, _ptr(keep), float(p), _ptr(A),
                                          _ptr(B), r, float(alpha), _ptr(Y), _ptr(ws), ws_bytes,
@@ -358,7 +388,7 @@ def qlora_linear_bwd_dropout(W: NF4Weight, X, dY, keep, p: float, A, B, r: int, 
     _need(dX, torch.bfloat16, "dX", T * W.cols)
     _need(dA, torch.float32, "dA", r * W.cols)
     _need(dB, torch.float32, "dB", W.rows * r)
-    ws, ws_bytes = _dropout_ws(ws, T, W.cols, W.rows, r, True, dev)
+    ws, ws_bytes = _dropout_ws(ws, T, W.cols, W.rows, r, True, dev, W.flags)
     wc = W._c()
     _check(_lib.qlora_linear_bwd_dropout(ctypes.byref(wc), _ptr(X), _ptr(dY), T, _ptr(keep), float(p),
                                          _ptr(A), _ptr(B), r, float(alpha), _ptr(dX), _ptr(dA), _ptr(dB),
@@ -393,8 +423,8 @@ def qlora_workspace_bytes_multi(T: int, in_features: int, out_features, r: int, 
                                                 1 if backward else 0))
 
 
-def _multi_ws(ws, T, n_in, outs, r, backward, device):
-    need = qlora_workspace_bytes_multi(T, n_in, outs, r, backward)
+def _multi_ws(ws, T, n_in, outs, r, backward, device, flags=0):
+    need = qlora_workspace_bytes_flags(T, n_in, outs, r, backward, False, flags)
     if ws is None:
         ws = make_workspace(need, device)
     return ws, ws.numel() * ws.element_size()
@@ -418,7 +448,7 @@ def qlora_linear_fwd_multi(Ws, X, As, Bs, r: int, alpha: float, Y=None, ws=None)
     if Y is None:
         Y = torch.empty(T, sum(outs), dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, "Y", T * sum(outs))
-    ws, ws_bytes = _multi_ws(ws, T, n_in, outs, r, False, X.device)
+    ws, ws_bytes = _multi_ws(ws, T, n_in, outs, r, False, X.device, Ws[0].flags)
     wc = (_NF4WeightC * n)(*[W._c() for W in Ws])
     _check(_lib.qlora_linear_fwd_multi(wc, n, _ptr(X), T, _ptr_array(As), _ptr_array(Bs), r,
                                        float(alpha), _ptr(Y), _ptr(ws), ws_bytes, _stream(X.device)),
@@ -442,7 +472,7 @@ def qlora_linear_bwd_multi(Ws, X, dY, As, Bs, r: int, alpha: float, dX=None, dAs
         dAs = [torch.empty(r, n_in, dtype=torch.float32, device=dev) for _ in range(n)]
     if dBs is None:
         dBs = [torch.empty(o, r, dtype=torch.float32, device=dev) for o in outs]
-    ws, ws_bytes = _multi_ws(ws, T, n_in, outs, r, True, dev)
+    ws, ws_bytes = _multi_ws(ws, T, n_in, outs, r, True, dev, Ws[0].flags)
     wc = (_NF4WeightC * n)(*[W._c() for W in Ws])
     _check(_lib.qlora_linear_bwd_multi(wc, n, _ptr(X), _ptr(dY), T, _ptr_array(As), _ptr_array(Bs),
                                        r, float(alpha), _ptr(dX), _ptr_array(dAs), _ptr_array(dBs),
@@ -454,6 +484,13 @@ def nf4_codebook():
     out = (ctypes.c_float * 16)()
     _lib.nf4_codebook(out)
     return [float(v) for v in out]
+
+
+def nf4_code_buckets():
+    """-> (thr [33], base [33]): the quantize kernel's code lookup on X = 16 x."""
+    thr, base = (ctypes.c_float * 33)(), (ctypes.c_uint32 * 33)()
+    _lib.nf4_code_buckets(thr, base)
+    return [float(v) for v in thr], [int(v) for v in base]
 
 
 def nf4_code_thresholds():

@@ -51,9 +51,12 @@ hipError_t launch_nf4_dequantize_nodq(const uint8_t* codes, const float* absmax,
                                       uint16_t* out, hipStream_t s);
 // out[c][r] = W_hat[r][c] for W_hat [rows][cols]; rows % 64 == 0, cols % 64 == 0
 // (out rows have stride ldo elements, ldo >= rows)
+// absmax_fp32: the 4.5-bit format (scale = the fp32 block absmax, one per
+// block; absmax_q unused)
 hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t* absmax_q,
                                             const float* scale, int64_t rows, int64_t cols,
-                                            uint16_t* out, int64_t ldo, hipStream_t s);
+                                            uint16_t* out, int64_t ldo, hipStream_t s,
+                                            bool absmax_fp32 = false);
 
 // Projections that share one input (q|k|v, gate|up) go through one call.
 constexpr int kMaxProj = 8;

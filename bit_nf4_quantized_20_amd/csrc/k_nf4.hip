@@ -312,6 +312,8 @@ hipError_t launch_nf4_dequantize_nodq(const uint8_t* codes, const float* absmax,
 // 8 (l & 7) .. + 7, so each store instruction writes eight full 128-byte
 // row segments.
 // ---------------------------------------------------------------------------
+// kDQ = false: the 4.5-bit format, a_hat = scale[blk] (the fp32 block absmax)
+template <bool kDQ>
 __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ absmax_q,
                                                           const float* __restrict__ scale,
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
   u32x4* tl = tile[wv];
   const int64_t row = r0 + lane;
   const int64_t blk = (row * cols + c0) >> 6;
-  const Nf4Table tab = make_table(dq_absmax(absmax_q[blk], scale[blk >> 8]));
+  const Nf4Table tab = make_table(kDQ ? dq_absmax(absmax_q[blk], scale[blk >> 8]) : scale[blk]);
   const u32x4* src = reinterpret_cast<const u32x4*>(codes + ((row * cols + c0) >> 1));
   const int key = (lane ^ (lane >> 3)) & 7;
 #pragma unroll
@@ -365,10 +367,15 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize_t(const uint8_t* __restr
 
 hipError_t launch_nf4_dequantize_transposed(const uint8_t* codes, const uint8_t* absmax_q,
                                             const float* scale, int64_t rows, int64_t cols,
-                                            uint16_t* out, int64_t ldo, hipStream_t s) {
+                                            uint16_t* out, int64_t ldo, hipStream_t s, bool absmax_fp32) {
   const int64_t tiles = (rows / 64) * (cols / 64);
-  hipLaunchKernelGGL(k_nf4_dequantize_t, dim3(static_cast<uint32_t>(ceil_div(tiles, 4))), dim3(256),
-                     0, s, codes, absmax_q, scale, rows, cols, out, ldo);
+  const dim3 grid(static_cast<uint32_t>(ceil_div(tiles, 4)));
+  if (absmax_fp32)
+    hipLaunchKernelGGL(k_nf4_dequantize_t<false>, grid, dim3(256), 0, s, codes, nullptr, scale, rows, cols, out,
+                       ldo);
+  else
+    hipLaunchKernelGGL(k_nf4_dequantize_t<true>, grid, dim3(256), 0, s, codes, absmax_q, scale, rows, cols, out,
+                       ldo);
   return hipGetLastError();
 }
 

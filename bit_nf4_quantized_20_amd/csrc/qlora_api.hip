@@ -110,10 +110,16 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 
 // dropout: the small-token kernel has no mask, so that call always takes the
 // general path
-FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout) {
+// expanded: the forward dequantizes W_hat into the workspace and runs the
+// bf16 GEMM (from kMaterializeTokens on, and always for the 4.5-bit format,
+// whose fp32 block absmax only the standalone dequantize reads)
+bool fwd_expands(int64_t T, bool absmax_fp32) { return absmax_fp32 || T >= kMaterializeTokens; }
+
+FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout,
+                     bool absmax_fp32 = false) {
   FwdLayout l{0, 0, 0, 0, 0};
   Carve c;
-  if (!dropout && fwd_uses_decode(T, in, outs, n, r)) {
+  if (!dropout && !absmax_fp32 && fwd_uses_decode(T, in, outs, n, r)) {
     l.u_pad = c.take(decode_u_bytes(n, T, r));  // U [n][T][r] fp32
     l.total = c.off;
     return l;
@@ -122,7 +128,7 @@ FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
   l.u_pad = c.take(static_cast<size_t>(T * n * rp * 4));  // [T][n 2rp] bf16
   l.b_pad = c.take(static_cast<size_t>(N * n * rp * 4));  // [N][2rp] or [N][n 2rp] bf16
   l.part = c.take(lora_down_part_bytes(T, in, n * rp));
-  if (T >= kMaterializeTokens) l.w_dq = c.take(static_cast<size_t>(N * in * 2));  // [N][in] bf16
+  if (fwd_expands(T, absmax_fp32)) l.w_dq = c.take(static_cast<size_t>(N * in * 2));  // [N][in] bf16
   l.total = c.off;
   return l;
 }
@@ -171,10 +177,17 @@ bool operands_fit(int64_t T, int64_t in, int64_t N) {
   return bf16_matrix_fits(T, in) && bf16_matrix_fits(T, N) && bf16_matrix_fits(N, in);
 }
 
+bool absmax_fp32(const qlora_nf4_weight& W) { return (W.flags & QLORA_NF4_ABSMAX_FP32) != 0; }
+
+// the descriptor's format and pointers: absmax_q is read only by the
+// double-quantized format
 int check_weight(const qlora_nf4_weight* W) {
-  if (W == nullptr || W->codes == nullptr || W->absmax_q == nullptr || W->absmax_scale == nullptr)
+  if (W == nullptr) return QLORA_ERR_NULL;
+  if ((W->flags & ~QLORA_NF4_FLAGS_KNOWN) != 0) return QLORA_ERR_VALUE;
+  const bool dq = !absmax_fp32(*W);
+  if (W->codes == nullptr || W->absmax_scale == nullptr || (dq && W->absmax_q == nullptr))
     return QLORA_ERR_NULL;
-  if (!aligned16(W->codes) || !aligned16(W->absmax_q) || !aligned16(W->absmax_scale))
+  if (!aligned16(W->codes) || (dq && !aligned16(W->absmax_q)) || !aligned16(W->absmax_scale))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
@@ -256,6 +269,19 @@ size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
 
+size_t qlora_workspace_bytes_flags(int64_t T, int64_t in_features, const int64_t* out_features, int n,
+                                   int64_t r, int backward, int dropout, uint32_t flags) {
+  if ((flags & ~QLORA_NF4_FLAGS_KNOWN) != 0) return 0;
+  if (n < 1 || n > kMaxProj || out_features == nullptr || (dropout && n != 1)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
+  if (!operands_fit(T, in_features, total_out(out_features, n))) return 0;
+  const bool fp32 = (flags & QLORA_NF4_ABSMAX_FP32) != 0;
+  const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r).total
+                               : fwd_layout(T, in_features, out_features, n, r, dropout != 0, fp32).total;
+  return need > kMinWorkspace ? need : kMinWorkspace;
+}
+
 size_t qlora_workspace_bytes_dropout(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                                      int backward) {
   if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;
@@ -278,6 +304,7 @@ int check_projections(const qlora_nf4_weight* W, int n, int64_t T, int64_t r, in
   for (int i = 0; i < n; ++i) {
     if (int st = check_weight(&W[i])) return st;
     if (W[i].cols != W[0].cols) return QLORA_ERR_SHAPE;
+    if (W[i].flags != W[0].flags) return QLORA_ERR_VALUE;
     if (!linear_shapes_ok(T, W[i].cols, W[i].rows, r)) return QLORA_ERR_SHAPE;
     outs[i] = W[i].rows;
   }
@@ -317,11 +344,12 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   const bool dropout = keep != nullptr;
   if (int st = check_dropout(keep, p)) return st;
   if (T == 0) return QLORA_OK;
-  const FwdLayout lay = fwd_layout(T, in, outs, n, r, dropout);
+  const bool fp32 = absmax_fp32(W[0]);
+  const FwdLayout lay = fwd_layout(T, in, outs, n, r, dropout, fp32);
   // The small-token forward also runs without a workspace where U need not
   // be computed up front (r <= 16, at most 4096 output rows): ws = NULL
   // selects its single-launch form.
-  const bool decode_no_ws = !dropout && ws == nullptr && fwd_uses_decode(T, in, outs, n, r) &&
+  const bool decode_no_ws = !dropout && !fp32 && ws == nullptr && fwd_uses_decode(T, in, outs, n, r) &&
                             !decode_pre_u(n, outs, r);
   if (!decode_no_ws && lay.total > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
@@ -330,7 +358,7 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = alpha / static_cast<float>(r);
   const int64_t N = total_out(outs, n);
-  if (!dropout && fwd_uses_decode(T, in, outs, n, r)) {
+  if (!dropout && !fp32 && fwd_uses_decode(T, in, outs, n, r)) {
     DecodeProj proj[kMaxProj];
     for (int i = 0; i < n; ++i)
       proj[i] = DecodeProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, A[i], B[i], outs[i]};
@@ -348,7 +376,7 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   const float uscale = dropout ? scale / (1.f - p) : scale;
   hipError_t e = launch_lora_down(X, in, T, in, A, n, r, uscale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s,
                                   keep, in / 8);
-  if (T >= kMaterializeTokens) {
+  if (fwd_expands(T, fp32)) {
     // W_hat of every projection into [N][in] bf16, then the bf16 GEMM.  The
     // LoRA term runs as extra K-steps: when no tile straddles two projections
     // each tile reads its own projection's sU_i against B_i (stacked [N][2rp]);
@@ -364,8 +392,9 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
       e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * ldb + (per_proj ? 0 : i * 2 * rp), rp, ldb,
                           s);
       if (e == hipSuccess)
-        e = launch_nf4_dequantize(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i] * in,
-                                  w_dq + off * in, s);
+        e = fp32 ? launch_nf4_dequantize_nodq(W[i].codes, W[i].absmax_scale, outs[i] * in, w_dq + off * in, s)
+                 : launch_nf4_dequantize(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i] * in,
+                                         w_dq + off * in, s);
       off += outs[i];
     }
     if (e == hipSuccess) {
@@ -455,7 +484,7 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
     if (e == hipSuccess)
       e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
-                                           w_dq_t + off, N, s);
+                                           w_dq_t + off, N, s, absmax_fp32(W[i]));
     off += outs[i];
   }
   // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
@@ -492,7 +521,7 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const qlora_bf16* X, int
   // the size check comes first, before any HIP call: a call whose workspace
   // would not fit in the library's scratch is refused without side effects
   if (W == nullptr) return QLORA_ERR_NULL;
-  const size_t need = qlora_workspace_bytes(T, W->cols, W->rows, r, 0);
+  const size_t need = qlora_workspace_bytes_flags(T, W->cols, &W->rows, 1, r, 0, 0, W->flags);
   if (need == 0) return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, nullptr, 0, stream);  // shape error
   if (need > kNoAllocScratchBytes) return QLORA_ERR_WORKSPACE;
   if (T == 0) return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, nullptr, 0, stream);
@@ -557,6 +586,7 @@ size_t qlora_merge_workspace_bytes(int64_t in_features, int64_t out_features, in
 int qlora_merge(const qlora_nf4_weight* W, const qlora_bf16* A, const qlora_bf16* B, int64_t r,
                 float alpha, qlora_bf16* W_out, void* ws, size_t ws_bytes, qlora_stream stream) {
   if (int st = check_weight(W)) return st;
+  if (absmax_fp32(*W)) return QLORA_ERR_VALUE;  // the merge reads the double-quantized format only
   const int64_t out = W->rows, in = W->cols;
   if (!linear_shapes_ok(0, in, out, r) || !operands_fit(0, in, out)) return QLORA_ERR_SHAPE;
   if (!A || !B || !W_out) return QLORA_ERR_NULL;

@@ -61,6 +61,13 @@ enum qlora_status {
 #define QLORA_NF4_GROUP 256     /* blocks per double-quantization scale */
 #define QLORA_MAX_RANK 256      /* largest LoRA rank r accepted */
 
+/* qlora_nf4_weight.flags: the weight's format.  0 is the double-quantized
+ * format; QLORA_NF4_ABSMAX_FP32 the 4.5-bit one (an exact fp32 absmax per
+ * block, as nf4_quantize_nodq writes it).  All other bits are reserved and
+ * must be 0. */
+#define QLORA_NF4_ABSMAX_FP32 0x1u
+#define QLORA_NF4_FLAGS_KNOWN 0x1u
+
 /*
  * A frozen NF4 weight W_hat [rows = out_features, cols = in_features].
  * Blocks are 64 consecutive weights of the row-major flattening, so with
@@ -68,10 +75,20 @@ enum qlora_status {
  * 256 consecutive blocks of the same flattening and may cross rows.
  *   codes        [rows*cols/2]  packed 4-bit codes; element 2i in bits 0-3,
  *                               element 2i+1 in bits 4-7 of byte i
+ *   flags        the format (QLORA_NF4_ABSMAX_FP32 or 0; other bits reserved,
+ *                a set reserved bit is QLORA_ERR_VALUE)
+ * flags = 0, double-quantized (4 + 8/64 + 32/16384 bits per weight):
  *   absmax_q     [rows*cols/64] 8-bit double-quantized absmax, one per block
  *   absmax_scale [ceil(rows*cols/16384)] fp32 scale per group of 256 blocks
+ * flags = QLORA_NF4_ABSMAX_FP32 (4 + 32/64 = 4.5 bits per weight, paperclase
+ * "QLoRA", Parte 3, "Bits por parametro"):
+ *   absmax_q     unused (may be NULL)
+ *   absmax_scale [rows*cols/64] the exact fp32 absmax of each block
  * Code c selects level L[c] of the 16-entry codebook (nf4_codebook), with
- * L ascending and L[7] = +0.0.
+ * L ascending and L[7] = +0.0.  The linear calls accept both formats: the
+ * 4.5-bit one runs the dequantize-then-bf16-GEMM route at every token count
+ * (its W_hat is expanded into the workspace, see qlora_workspace_bytes_flags);
+ * qlora_merge takes the double-quantized format only.
  */
 typedef struct {
   const uint8_t* codes;
@@ -79,6 +96,7 @@ typedef struct {
   const float* absmax_scale;
   int64_t rows;
   int64_t cols;
+  uint32_t flags;
 } qlora_nf4_weight;
 
 /*
@@ -135,7 +153,8 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* a
  * w_hat = bf16_rne(fl32(L[c] * a_b)).
  *   codes  [numel/2];  absmax [numel/64] fp32 (out of quantize, in of dequantize)
  *   numel  >= 0, multiple of 64, at most 2^36 (0 is a no-op)
- * The linear calls take the double-quantized format only.
+ * A qlora_nf4_weight with flags = QLORA_NF4_ABSMAX_FP32 and absmax_scale =
+ * this absmax array describes such a weight to the linear calls.
  * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
  */
 int nf4_quantize_nodq(const float* w, int64_t numel, uint8_t* codes, float* absmax,
@@ -160,6 +179,18 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  */
 size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                              int backward);
+
+/*
+ * Workspace bytes for a weight of the given format (qlora_nf4_weight.flags),
+ * for n projections sharing X (out_features[0..n-1], 1 <= n <= 8; n = 1 for
+ * the single-projection calls), with (dropout = 1) or without LoRA dropout
+ * (dropout needs n = 1).  With flags = 0 the result equals the functions
+ * above; with QLORA_NF4_ABSMAX_FP32 the forward also holds the expanded W_hat
+ * (2 * sum(out) * in bytes) at every T.  Returns 0 for invalid arguments
+ * (including reserved flag bits).  Host only.
+ */
+size_t qlora_workspace_bytes_flags(int64_t T, int64_t in_features, const int64_t* out_features, int n,
+                                   int64_t r, int backward, int dropout, uint32_t flags);
 
 /*
  * qlora_linear_fwd -- F1 + F2: Y = X W_hat^T + (alpha/r) (X A^T) B^T.
@@ -223,7 +254,7 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const qlora_bf16* X, int
  *                    [sum_{j<i} out_j, sum_{j<=i} out_j) of Y (and of dY)
  *   dX [T, in] = sum_i (dY_i W_hat_i + s (dY_i B_i) A_i), one rounding
  *   dA[i] [r, in], dB[i] [out_i, r] fp32, overwritten
- *   W[i]  NF4 weights, all with the same cols = in;  A[i], B[i] as above
+ *   W[i]  NF4 weights, all with the same cols = in and the same flags;  A[i], B[i] as above
  * Arguments and errors otherwise as for the single-projection calls; the
  * workspace is sized by qlora_workspace_bytes_multi (0 for invalid shapes,
  * n outside 1..8 or a NULL out_features).  n = 1 is exactly the

@@ -167,7 +167,8 @@ _MISALIGNED = 0x10008
 
 class _W(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
-                ("absmax_scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+                ("absmax_scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("flags", ctypes.c_uint32)]
 
 
 def _api(lib):
@@ -237,6 +238,50 @@ def test_linear_validation():
     assert lib.qlora_workspace_bytes(-1, 256, 128, 8, 1) == 0
     for s in (0, -1, -2, -3, -4, -5, -6, -7, 42):
         assert len(lib.qlora_status_string(s)) > 0
+
+
+def test_format_flags():
+    # qlora_nf4_weight.flags: 0 = double-quantized, 1 = the 4.5-bit format
+    # (fp32 block absmax in absmax_scale, absmax_q unused); other bits reserved
+    lib = _api(_lib())
+    i64, sz, F = ctypes.c_int64, ctypes.c_size_t, _FAKE
+    lib.qlora_workspace_bytes_flags.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_uint32]
+    lib.qlora_workspace_bytes_flags.restype = sz
+    lib.qlora_workspace_bytes_multi.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes_multi.restype = sz
+    lib.qlora_workspace_bytes_dropout.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes_dropout.restype = sz
+    lib.qlora_merge.argtypes = [ctypes.POINTER(_W), ctypes.c_void_p, ctypes.c_void_p, i64, ctypes.c_float,
+                                ctypes.c_void_p, ctypes.c_void_p, sz, ctypes.c_void_p]
+    wsf = lambda T, outs, bwd=0, drop=0, flags=0, r=8: lib.qlora_workspace_bytes_flags(
+        T, 256, (i64 * len(outs))(*outs), len(outs), r, bwd, drop, flags)
+    # flags = 0 gives what the format-blind size functions give
+    for T in (0, 1, 16, 32, 300, 2048, 4096):
+        for b in (0, 1):
+            assert wsf(T, [128], b) == lib.qlora_workspace_bytes(T, 256, 128, 8, b)
+            assert wsf(T, [128], b, 1) == lib.qlora_workspace_bytes_dropout(T, 256, 128, 8, b)
+            assert wsf(T, [128, 64], b) == lib.qlora_workspace_bytes_multi(T, 256, (i64 * 2)(128, 64), 2, 8, b)
+    # the 4.5-bit forward expands W_hat into the workspace at every T
+    for T in (1, 16, 300):
+        assert wsf(T, [128], 0, 0, 1) >= wsf(T, [128]) + 128 * 256 * 2
+        assert wsf(T, [128], 1, 0, 1) == wsf(T, [128], 1)        # the backward expands W_hat^T anyway
+    assert wsf(16, [128, 64], 0, 0, 1) >= 192 * 256 * 2
+    # reserved bits, and dropout with several projections
+    assert wsf(16, [128], 0, 0, 2) == 0 and wsf(16, [128], 0, 0, 0x80000000) == 0
+    assert wsf(16, [128, 64], 0, 1, 0) == 0
+    ws1 = wsf(32, [128], 0, 0, 1)
+    fwd = lambda W, wsb=ws1: lib.qlora_linear_fwd(ctypes.byref(W), F, 32, F, F, 8, 16.0, F, F, wsb, None)
+    assert fwd(_W(F, F, F, 128, 256, 2)) == -7                  # reserved bit
+    assert fwd(_W(None, None, None, 128, 256, 4)) == -7         # checked before the pointers
+    assert fwd(_W(F, None, F, 128, 256, 0)) == -1               # double-quantized needs absmax_q
+    assert fwd(_W(F, None, None, 128, 256, 1)) == -1            # 4.5-bit needs the absmax array
+    # 4.5-bit: absmax_q NULL (or misaligned) is never read; the call gets as
+    # far as the workspace check, which wants the expanded weight
+    assert fwd(_W(F, None, F, 128, 256, 1), ws1 - 1) == -4
+    assert fwd(_W(F, _MISALIGNED, F, 128, 256, 1), ws1 - 1) == -4
+    # the merge reads the double-quantized format only
+    assert lib.qlora_merge(ctypes.byref(_W(F, None, F, 128, 256, 1)), F, F, 8, 16.0, F, F, 1 << 20, None) == -7
 
 
 def test_operand_size_limit():
