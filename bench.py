@@ -63,7 +63,7 @@ def parse():
                          "3 = 8B MLP, 4 = 8B attention, 5 = 70B MLP) and print its figures (for "
                          "rocprofv3 --pmc passes over the large-token GEMMs)")
     ap.add_argument("--probe-workload", type=int, default=3, choices=(3, 4, 5))
-    ap.add_argument("--only-leg", choices=("quantize", "merge"),
+    ap.add_argument("--only-leg", choices=("quantize", "merge", "bwd_small"),
                     help="only run one standalone leg (the 2^30 flat quantize, or the 8B and 70B gate "
                          "merges) and then the 256 MiB copy, and print its figures (for rocprofv3 "
                          "kernel-trace and --pmc FETCH_SIZE / WRITE_SIZE passes)")
@@ -145,9 +145,11 @@ def main():
     if args.only_leg:
         if args.only_leg == "quantize":
             res = {"quantize_flat_2pow30": flat_quantize_leg(q, synth, dev, False)}
-        else:
+        elif args.only_leg == "merge":
             res = {"merge_8b_gate": merge_leg(q, synth, dev, bf, 3),
                    "merge_70b_gate": merge_leg(q, synth, dev, bf, 5)}
+        else:
+            res = {"bwd_small": bwd_small_leg(q, synth, dev, bf)}
         copy_calibration(dev)
         print(json.dumps(res), flush=True)
         return
@@ -306,6 +308,7 @@ def main():
     # ------------------------------------------------------ adapter merge
     extra["merge_8b_gate"] = merge_leg(q, synth, dev, bf, 3)
     extra["merge_70b_gate"] = merge_leg(q, synth, dev, bf, 5)
+    extra["bwd_small"] = bwd_small_leg(q, synth, dev, bf)
 
     # ------------------------------------------- q|k|v at decode sizes
     extra["qkv8b_decode"] = qkv_decode_leg(q, synth, dev, bf)
@@ -470,6 +473,51 @@ def mlp_decode_leg(q, synth, dev, bf, n=96):
         res[name] = entry
         del pool, W0
         torch.cuda.empty_cache()
+    return res
+
+
+def bwd_small_leg(q, synth, dev, bf):
+    """Small-token backward (T = 1 and 16): qlora_linear_bwd, whose dX
+    streams the codes once, against the expanded-weight route of the same
+    call (qlora_linear_bwd_dropout with every element kept and p = 0: W_hat^T
+    expanded into the workspace, then the GEMM), on the 8B q_proj (r = 16)
+    and gate (r = 64) weights.  30 untimed and 50 timed calls each."""
+    import numpy as np
+    import torch
+    res = {}
+    for name, wid, proj in (("q_proj", 2, 0), ("8b_gate", 3, 0)):
+        wl = synth.WORKLOADS[wid]
+        pr = wl.projections[proj]
+        r, alpha = wl.r, wl.alpha
+        n_out, n_in = pr.out_features, pr.in_features
+        W = q.nf4_quantize_weight(torch.from_numpy(synth.weight(wid, proj, n_out, n_in)).to(dev))
+        A, B = bf(synth.lora_A(wid, proj, r, n_in)), bf(synth.lora_B(wid, proj, n_out, r))
+        entry = {"out": n_out, "in": n_in, "r": r}
+        for T in (1, 16):
+            X = bf(synth.activations(wid, proj, T, n_in))
+            dY = bf(synth.activations(wid, proj, T, n_out, "dY"))
+            keep = torch.full((T, n_in // 8), 0xFF, dtype=torch.uint8, device=dev)
+            dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
+            dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
+            dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
+            ws = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
+
+            def timed(fn, n=50):
+                for _ in range(WARM_CALLS):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(n):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / n
+            us_new = timed(lambda: q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX, dA, dB, ws))
+            us_old = timed(lambda: q.qlora_linear_bwd_dropout(W, X, dY, keep, 0.0, A, B, r, alpha, dX, dA, dB,
+                                                              ws))
+            entry[f"T{T}"] = {"streamed_us": round(us_new, 2), "expanded_us": round(us_old, 2)}
+        res[name] = entry
     return res
 
 

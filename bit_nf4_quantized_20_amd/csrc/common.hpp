@@ -159,6 +159,23 @@ constexpr int64_t kDecodeMaxRank = 64;
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
 // One projection of the small-token forward: its NF4 weight [out][in] and
 // LoRA factors A [r][in], B [out][r].
+// Small-token input gradient dX = dY W_hat + (sV) A (T <= kDxSmallMaxT, no
+// dropout), n projections stacked along W's rows: projection i's rows start
+// at row0 (its dY columns).  part: fp32 scratch of part_bytes (the
+// partials of the row splits).
+constexpr int kDxSmallMaxT = 16;
+struct DxProj {
+  const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
+  int64_t row0;
+};
+struct DxSet {
+  DxProj proj[kMaxProj];
+  int n;
+};
+hipError_t launch_dx_small(const DxSet& set, int64_t N, int64_t in, const uint16_t* dY, int T, const DownFactors& A,
+                           int r, const uint16_t* v_pad, int64_t ldv, int64_t rp, uint16_t* dX, float* part,
+                           size_t part_bytes, bool absmax_fp32, hipStream_t s);
+
 struct DecodeProj {
   const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
   const uint16_t* A; const uint16_t* B;

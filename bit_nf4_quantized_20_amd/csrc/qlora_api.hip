@@ -473,6 +473,10 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   const float inv_keep = keep != nullptr ? 1.f / (1.f - p) : 1.f;
   e = launch_lora_down(X, in, T, in, A, n, r, scale * inv_keep, nullptr, 0, ut, tp, rp, part, s, keep,
                        in / 8);
+  // Up to kDxSmallMaxT tokens (no dropout) dX streams the codes once
+  // (k_dx_small: W_hat only in LDS tiles, row-split partials in the W_hat^T
+  // region of the workspace); otherwise W_hat^T is expanded and a GEMM runs.
+  const bool dx_small = T <= kDxSmallMaxT && keep == nullptr;
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     // s V_i = s dY_i B_i with dY_i the projection's columns of dY
@@ -481,18 +485,34 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     if (e == hipSuccess)
       e = launch_lora_down(dY + off, N, T, outs[i], &bt, 1, r, scale, v_pad + i * 2 * rp, n * 2 * rp,
                            vt + i * 2 * rp * tp, tp, rp, part, s);
-    if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
-    if (e == hipSuccess)
-      e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
-                                           w_dq_t + off, N, s, absmax_fp32(W[i]));
+    if (!dx_small) {
+      if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
+      if (e == hipSuccess)
+        e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
+                                             w_dq_t + off, N, s, absmax_fp32(W[i]));
+    }
     off += outs[i];
   }
-  // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
-  // (with dropout the adapter term is masked and scaled by 1 / (1 - p)
-  // before the base is added)
-  if (e == hipSuccess)
+  if (dx_small) {
+    DxSet set{};
+    DownFactors af{};
+    set.n = n;
+    int64_t row0 = 0;
+    for (int i = 0; i < n; ++i) {
+      set.proj[i] = DxProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, row0};
+      af.p[i] = A[i];
+      row0 += outs[i];
+    }
+    if (e == hipSuccess)
+      e = launch_dx_small(set, N, in, dY, static_cast<int>(T), af, static_cast<int>(r), v_pad, n * 2 * rp, rp, dX,
+                          reinterpret_cast<float*>(w_dq_t), static_cast<size_t>(in) * N * 2, absmax_fp32(W[0]), s);
+  } else if (e == hipSuccess) {
+    // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
+    // (with dropout the adapter term is masked and scaled by 1 / (1 - p)
+    // before the base is added)
     e = launch_gemm_nt(T, in, dY, N, w_dq_t, N, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp,
                        dX, in, s, keep, in / 8, inv_keep);
+  }
   off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, dA[i], true, s, keep, in / 8,
