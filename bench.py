@@ -500,7 +500,9 @@ def bwd_small_leg(q, synth, dev, bf):
             dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
             dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
             dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
-            ws = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
+            ws_small = q.qlora_workspace_bytes(T, n_in, n_out, r, True)
+            ws_exp = q.qlora_workspace_bytes_dropout(T, n_in, n_out, r, True)
+            ws = q.make_workspace(max(ws_small, ws_exp), dev)
 
             def timed(fn, n=50):
                 for _ in range(WARM_CALLS):
@@ -516,7 +518,8 @@ def bwd_small_leg(q, synth, dev, bf):
             us_new = timed(lambda: q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX, dA, dB, ws))
             us_old = timed(lambda: q.qlora_linear_bwd_dropout(W, X, dY, keep, 0.0, A, B, r, alpha, dX, dA, dB,
                                                               ws))
-            entry[f"T{T}"] = {"streamed_us": round(us_new, 2), "expanded_us": round(us_old, 2)}
+            entry[f"T{T}"] = {"streamed_us": round(us_new, 2), "expanded_us": round(us_old, 2),
+                              "workspace_bytes": {"streamed": ws_small, "expanded": ws_exp}}
         res[name] = entry
     return res
 

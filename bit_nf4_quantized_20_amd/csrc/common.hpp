@@ -164,6 +164,11 @@ bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
 // at row0 (its dY columns).  part: fp32 scratch of part_bytes (the
 // partials of the row splits).
 constexpr int kDxSmallMaxT = 16;
+// The row splits' partials are sized for this many workgroups (two per CU
+// on a 256-CU device); with more CUs the split count is capped by the space.
+constexpr int kDxSmallTargetWgs = 512;
+// Most row splits the partials of dX can need ([splits][T][in] fp32).
+int dx_small_max_splits(int64_t N, int64_t in);
 struct DxProj {
   const uint8_t* codes; const uint8_t* absmax_q; const float* scale;
   int64_t row0;

@@ -173,13 +173,23 @@ __global__ __launch_bounds__(256) void k_dx_small_fin(const float* __restrict__ 
   }
 }
 
-int dx_small_splits(int64_t N, int64_t in, int T, size_t part_bytes) {
+namespace {
+// row splits for about `target` workgroups over the in / 64 column strips,
+// at most one 64-row chunk each
+int splits_for(int64_t N, int64_t in, int target) {
   const int strips = static_cast<int>(in / 64);
   const int nchunks = static_cast<int>(N / 64);
-  const int cus = device_cus();
-  const int target = 2 * (cus > 0 ? cus : 256);
   int splits = (target + strips - 1) / strips;
   if (splits > nchunks) splits = nchunks;
+  return splits < 1 ? 1 : splits;
+}
+}  // namespace
+
+int dx_small_max_splits(int64_t N, int64_t in) { return splits_for(N, in, kDxSmallTargetWgs); }
+
+int dx_small_splits(int64_t N, int64_t in, int T, size_t part_bytes) {
+  const int cus = device_cus();
+  int splits = splits_for(N, in, 2 * (cus > 0 ? cus : 256));
   const int64_t per = static_cast<int64_t>(T) * in * 4;  // bytes of one split's partial
   if (per > 0 && static_cast<int64_t>(splits) * per > static_cast<int64_t>(part_bytes))
     splits = static_cast<int>(static_cast<int64_t>(part_bytes) / per);

@@ -135,8 +135,15 @@ FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 
 int64_t token_pitch(int64_t T) { return round_up(T, 8); }
 
-BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
+// Up to kDxSmallMaxT tokens without dropout, dX streams the codes once
+// (k_dx_small): no W_hat^T and no padded A^T, and the W_hat^T region holds
+// the fp32 row-split partials instead ([splits][T][in], at most
+// dx_small_max_splits of them).
+bool bwd_small(int64_t T, bool dropout) { return T <= kDxSmallMaxT && !dropout; }
+
+BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout) {
   const int64_t rp = padded_rank(r), N = total_out(outs, n);
+  const bool small = bwd_small(T, dropout);
   int64_t out_max = 0;
   size_t part = lora_down_part_bytes(T, in, n * rp);
   for (int i = 0; i < n; ++i) {
@@ -150,8 +157,9 @@ BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
   l.vt = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));
   l.v_pad = c.take(static_cast<size_t>(T * n * rp * 4));                // [T][n 2rp] bf16
   l.b_t = c.take(static_cast<size_t>(r * out_max * 2));                 // one B^T at a time
-  l.a_t_pad = c.take(static_cast<size_t>(in * n * rp * 4));             // [in][n 2rp] bf16
-  l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));                   // [in][N] bf16
+  l.a_t_pad = c.take(small ? 0 : static_cast<size_t>(in * n * rp * 4));  // [in][n 2rp] bf16
+  l.w_dq_t = c.take(small ? static_cast<size_t>(dx_small_max_splits(N, in) * T * in * 4)
+                          : static_cast<size_t>(in * N * 2));             // [in][N] bf16
   l.part = c.take(part);
   l.total = c.off;
   return l;
@@ -264,7 +272,7 @@ size_t qlora_workspace_bytes_multi(int64_t T, int64_t in_features, const int64_t
   for (int i = 0; i < n; ++i)
     if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
   if (!operands_fit(T, in_features, total_out(out_features, n))) return 0;
-  const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r).total
+  const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r, false).total
                                : fwd_layout(T, in_features, out_features, n, r, false).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
@@ -277,7 +285,7 @@ size_t qlora_workspace_bytes_flags(int64_t T, int64_t in_features, const int64_t
     if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
   if (!operands_fit(T, in_features, total_out(out_features, n))) return 0;
   const bool fp32 = (flags & QLORA_NF4_ABSMAX_FP32) != 0;
-  const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r).total
+  const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r, dropout != 0).total
                                : fwd_layout(T, in_features, out_features, n, r, dropout != 0, fp32).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
@@ -286,7 +294,7 @@ size_t qlora_workspace_bytes_dropout(int64_t T, int64_t in_features, int64_t out
                                      int backward) {
   if (!linear_shapes_ok(T, in_features, out_features, r)) return 0;
   if (!operands_fit(T, in_features, out_features)) return 0;
-  const size_t need = backward ? bwd_layout(T, in_features, &out_features, 1, r).total
+  const size_t need = backward ? bwd_layout(T, in_features, &out_features, 1, r, true).total
                                : fwd_layout(T, in_features, &out_features, 1, r, true).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
@@ -438,7 +446,7 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   if (!aligned16(X) || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
   if (int st = check_dropout(keep, p)) return st;
-  const BwdLayout lay = bwd_layout(T, in, outs, n, r);
+  const BwdLayout lay = bwd_layout(T, in, outs, n, r, keep != nullptr);
   if (T > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
@@ -476,7 +484,8 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   // Up to kDxSmallMaxT tokens (no dropout) dX streams the codes once
   // (k_dx_small: W_hat only in LDS tiles, row-split partials in the W_hat^T
   // region of the workspace); otherwise W_hat^T is expanded and a GEMM runs.
-  const bool dx_small = T <= kDxSmallMaxT && keep == nullptr;
+  const bool dx_small = bwd_small(T, keep != nullptr);
+  const size_t w_dq_t_bytes = lay.part - lay.w_dq_t;
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     // s V_i = s dY_i B_i with dY_i the projection's columns of dY
@@ -505,7 +514,7 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     }
     if (e == hipSuccess)
       e = launch_dx_small(set, N, in, dY, static_cast<int>(T), af, static_cast<int>(r), v_pad, n * 2 * rp, rp, dX,
-                          reinterpret_cast<float*>(w_dq_t), static_cast<size_t>(in) * N * 2, absmax_fp32(W[0]), s);
+                          reinterpret_cast<float*>(w_dq_t), w_dq_t_bytes, absmax_fp32(W[0]), s);
   } else if (e == hipSuccess) {
     // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
     // (with dropout the adapter term is masked and scaled by 1 / (1 - p)

@@ -168,8 +168,11 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  * Returns 0 for invalid shapes and at least 256 otherwise.  Host only.
  *
  * The workspace is scratch for intermediate products (padded LoRA factors,
- * the transposed dequantized weight of the backward and, from T = 2048 on,
- * the forward's dequantized weight: 2 * out * in bytes).  It needs no
+ * the transposed dequantized weight of the backward from T = 17 on or with
+ * dropout, and, from T = 2048 on, the forward's dequantized weight: 2 * out
+ * * in bytes each).  Up to T = 16 without dropout the backward keeps no
+ * dequantized weight: it holds fp32 row-split partials of dX instead
+ * (splits * T * in * 4 bytes, splits <= ceil(512 / (in / 64))).  It needs no
  * initialisation and keeps nothing between calls.  The small-token forward
  * (T <= 16 and r <= 64) uses it only for U = X A^T (n * T * r fp32 values),
  * computed once up front when r > 16 or the projections have more than 4096
@@ -282,8 +285,10 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
  * trained tensors.  dA and dB are overwritten, not accumulated.  They are
  * sums over token slices added with fp32 atomics, so two identical calls can
  * differ in the last bits of dA and dB (summation order); Y and dX are
- * reproducible bit for bit.  The backward expands W_hat^T into the
- * workspace (2 * out * in bytes) for its dX product.
+ * reproducible bit for bit.  From T = 17 on the backward expands W_hat^T
+ * into the workspace (2 * out * in bytes) for its dX product; up to T = 16
+ * it streams the codes once, W_hat existing only in LDS tiles, and sums
+ * fp32 row-split partials of dX in a fixed order (one rounding).
  *   dY [T, out] bf16; other arguments as in qlora_linear_fwd;
  *   ws of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1)
  * T == 0 writes zeros to dA and dB and nothing else (X, dY, dX may be NULL).

@@ -240,6 +240,26 @@ def test_linear_validation():
         assert len(lib.qlora_status_string(s)) > 0
 
 
+def test_small_token_backward_workspace():
+    # up to 16 tokens without dropout the backward keeps no W_hat^T: its
+    # workspace holds the row-split fp32 partials of dX (sized for 512
+    # workgroups over the in / 64 column strips), far below 2 out in bytes;
+    # with dropout, or from 17 tokens on, W_hat^T is expanded as before
+    lib = _api(_lib())
+    i64, sz = ctypes.c_int64, ctypes.c_size_t
+    lib.qlora_workspace_bytes_dropout.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.qlora_workspace_bytes_dropout.restype = sz
+    for n_in, n_out, splits in ((4096, 14336, 8), (14336, 4096, 3), (4096, 4096, 8)):
+        expanded = n_in * n_out * 2
+        for T in (1, 7, 16):
+            small = lib.qlora_workspace_bytes(T, n_in, n_out, 64, 1)
+            assert splits * T * n_in * 4 <= small < expanded // 4, (n_in, n_out, T, small)
+            assert lib.qlora_workspace_bytes_dropout(T, n_in, n_out, 64, 1) > expanded
+        assert lib.qlora_workspace_bytes(17, n_in, n_out, 64, 1) > expanded
+    # a weight with fewer 64-row chunks than splits: one split per chunk
+    assert lib.qlora_workspace_bytes(16, 64, 128, 8, 1) >= 2 * 16 * 64 * 4
+
+
 def test_format_flags():
     # qlora_nf4_weight.flags: 0 = double-quantized, 1 = the 4.5-bit format
     # (fp32 block absmax in absmax_scale, absmax_q unused); other bits reserved

@@ -302,7 +302,8 @@ def test_small_token_ranks(T, r):
 
 @pytest.mark.parametrize("T", [1, 16])
 def test_small_token_lora_only(T):
-    # W = 0: Y = s U B^T, so the U handed between workgroups is all of Y
+    # W = 0: Y = s U B^T, so the U each workgroup computes for itself (r <= 16)
+    # is all of Y
     q = require_gpu()
     banner(f"small-token W=0 T={T}")
     n_out, n_in, r, alpha = 2048, 4096, 16, 32.0
@@ -329,6 +330,19 @@ def test_small_token_split_variants(T, n_out, n_in, r):
     h = _make(14, T, T, n_out, n_in, r)
     W, w_hat = _quantize(q, h["w"])
     _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, f"T={T} in={n_in}")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_small_token_u_up_front_eight_steps(T):
+    # r = 64 with 16 row blocks: U computed up front, then the split kernel
+    # with eight unrolled chunk steps per wave (4096 < in <= 8192), the
+    # variant the 70B gate takes at 16 tokens
+    q = require_gpu()
+    banner(f"small-token U up front, eight steps, T={T}")
+    n_out, n_in, r, alpha = 256, 8192, 64, 128.0
+    h = _make(15, T, T, n_out, n_in, r)
+    W, w_hat = _quantize(q, h["w"])
+    _check_fwd(_fwd(q, W, h, r, alpha), w_hat, h, r, alpha, f"pre-U ns=8 T={T}")
 
 
 @pytest.mark.parametrize("T,r", [(1, 16), (16, 16), (1, 64), (16, 64)])
