@@ -242,6 +242,7 @@ def main():
     us16 = per_launch_us(X16, Y16, 400)
     us1 = per_launch_us(X1, Y1, 400)
     ach16 = b16 / (us16 * 1e-6) / 1e9
+    ceiling = read_ceiling_leg(pool, 400)
 
     extra = {
         "fwd_T1": {"us_per_call": round(us1, 3), "GB_per_s": round(b1 / (us1 * 1e-6) / 1e9, 1),
@@ -250,6 +251,8 @@ def main():
                     "algorithmic_bytes": b16},
         "eager_us_per_call": {"T1": round(eager_us(X1, Y1, 200), 2),
                               "T16": round(eager_us(X16, Y16, 200), 2)},
+        "read_ceiling": dict(ceiling, fwd_T1_frac_of_ceiling=round(b1 / (us1 * 1e-6) / 1e9 / ceiling["GB_per_s"], 3),
+                             fwd_T16_frac_of_ceiling=round(ach16 / ceiling["GB_per_s"], 3)),
         "timing": "HIP graph replay of back-to-back calls (events on the library's stream)",
         "weight_pool_bytes": int(P * n_out * n_in * NF4_BYTES_PER_WEIGHT),
     }
@@ -364,6 +367,48 @@ def main():
         "wall_s_timed_region": round(wall, 6),
     }
     print(json.dumps(out), flush=True)
+
+
+def read_ceiling_leg(pool, n):
+    """The fastest plain read of one pool weight's packed codes (8 MiB) in a
+    single launch: a graph of n back-to-back launches over the pool, as the
+    small-token forward is timed, for each (threads, loads per thread) of a
+    small sweep; the best is the practical ceiling of a one-launch weight
+    stream of this size (launch overhead and memory latency included)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_nf4_quantized_20_amd", "libqlora_bench.so"))
+    fn = lib.qlora_bench_read_ceiling
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    nbytes = pool[0].codes.numel()
+    P = len(pool)
+    sink = torch.empty(nbytes // 16 + 1024, dtype=torch.int32, device=pool[0].codes.device)
+    best = None
+    for threads in (256, 512):
+        for per in (1, 2, 4, 8):
+            def launch(i):
+                st = fn(pool[i % P].codes.data_ptr(), nbytes, threads, per, sink.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"qlora_bench_read_ceiling returned {st}")
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    launch(i)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            if best is None or us < best[0]:
+                best = (us, threads, per)
+    us, threads, per = best
+    return {"bytes": int(nbytes), "us_per_call": round(us, 3), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "threads": threads, "loads_per_thread": per}
 
 
 def qkv_decode_leg(q, synth, dev, bf, P=24, n=192):

@@ -1,6 +1,7 @@
-"""Builds libqlora.so (the HIP kernels + C ABI) in-tree for gfx950.
+"""Builds libqlora.so (the HIP kernels + C ABI) in-tree for gfx950, and the
+bench's measurement-support library libqlora_bench.so (bench_csrc/).
 
-    python bit_nf4_quantized_20_amd/build.py             # libqlora.so
+    python bit_nf4_quantized_20_amd/build.py             # libqlora.so, libqlora_bench.so
     python bit_nf4_quantized_20_amd/build.py --sanitize  # + _build/libqlora_san.so
 
 hipcc cross-compiles for gfx950 without a GPU.  Every HIP source is compiled
@@ -17,6 +18,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlora.so")
+BENCH_CSRC = os.path.join(HERE, "bench_csrc")
+BENCH_LIB = os.path.join(HERE, "libqlora_bench.so")
 ARCH = "gfx950"
 
 
@@ -38,12 +41,17 @@ def flags():
 
 
 def build(verbose: bool = False) -> str:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    _link(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB, verbose)
+    _link(sorted(glob.glob(os.path.join(BENCH_CSRC, "*.hip"))), BENCH_LIB, verbose, prefix="bench_")
+    return LIB
+
+
+def _link(sources, lib, verbose, prefix=""):
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src in sources:
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        obj = os.path.join(objdir, prefix + os.path.basename(src) + ".o")
         cmd = [hipcc(), *flags(), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -55,13 +63,12 @@ def build(verbose: bool = False) -> str:
         if errs.strip() and verbose:
             print(errs, file=sys.stderr)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 # Host-side sanitizers for the validation layer: the C-ABI entry points'
