@@ -35,16 +35,38 @@ constexpr uint32_t kDxPastEnd = 0x80000000u;
 __device__ __forceinline__ bf16x8 dx_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 }  // namespace
 
+// Workgroup -> (strip, split).  A 128-byte line of codes holds one row's
+// blocks of four consecutive strips, so when those four workgroups run on
+// different XCDs (workgroups go to the 8 XCDs round-robin by linear id) each
+// line is fetched from HBM by four L2s.  The mapping puts them on one XCD,
+// dispatched back to back: XCD x runs linear ids x, x + 8, x + 16, ...; its
+// k-th workgroup is member k % 4 of line group k / 4 there.  Needs
+// strips % 4 == 0 and a multiple of 32 workgroups; otherwise the plain
+// order.
+__device__ __forceinline__ void dx_strip_split(int strips, int total, int& strip, int& split) {
+  const int L = static_cast<int>(blockIdx.x);
+  if (strips % 4 == 0 && total % 32 == 0) {
+    const int xcd = L % 8, k = L / 8;
+    const int G = (k / 4) * 8 + xcd;  // line group x split, numbered over all XCDs
+    strip = 4 * (G % (strips / 4)) + k % 4;
+    split = G / (strips / 4);
+  } else {
+    strip = L % strips;
+    split = L / strips;
+  }
+}
+
 template <bool kFp32>
 __global__ __launch_bounds__(256) void k_dx_small_part(DxSet P, int64_t in, const uint16_t* __restrict__ dY,
-                                                       int T, int64_t N, int chunks_per_split,
+                                                       int T, int64_t N, int chunks_per_split, int nsplits,
                                                        float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_w[4][64 * kDxPitch];
   __shared__ f32x4 s_acc[4][4][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int split = blockIdx.y;
+  int strip, split;
+  dx_strip_split(static_cast<int>(in / 64), static_cast<int>(in / 64) * nsplits, strip, split);
+  const int64_t n0 = static_cast<int64_t>(strip) * 64;
   const int nchunks = static_cast<int>(N / 64);
   const int c0 = split * chunks_per_split;
   const int c1 = min(c0 + chunks_per_split, nchunks);
@@ -203,11 +225,11 @@ hipError_t launch_dx_small(const DxSet& set, int64_t N, int64_t in, const uint16
   const int nchunks = static_cast<int>(N / 64);
   const int per = (nchunks + splits - 1) / splits;
   const int used = (nchunks + per - 1) / per;  // splits that get chunks
-  const dim3 grid(static_cast<uint32_t>(in / 64), static_cast<uint32_t>(used));
+  const dim3 grid(static_cast<uint32_t>(in / 64 * used));  // (strip, split) pairs, see dx_strip_split
   if (absmax_fp32)
-    hipLaunchKernelGGL(k_dx_small_part<true>, grid, dim3(256), 0, s, set, in, dY, T, N, per, part);
+    hipLaunchKernelGGL(k_dx_small_part<true>, grid, dim3(256), 0, s, set, in, dY, T, N, per, used, part);
   else
-    hipLaunchKernelGGL(k_dx_small_part<false>, grid, dim3(256), 0, s, set, in, dY, T, N, per, part);
+    hipLaunchKernelGGL(k_dx_small_part<false>, grid, dim3(256), 0, s, set, in, dY, T, N, per, used, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dx_small_fin, dim3(static_cast<uint32_t>(in / 64), static_cast<uint32_t>((T + 3) / 4)),
