@@ -467,11 +467,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   }
 }
 
-// 256 x 256 tiles, 8 waves (see the file comment).  Launch: 512 threads.
-template <bool kNf4>
+// BM x 256 tiles (BM = 256 or 128), 8 waves (see the file comment).
+// Launch: 512 threads.
+template <bool kNf4, int BM>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
-  constexpr int NW = 8, NT = 64 * NW, BM = 256, BN = 256;
-  constexpr int FN = 2, WN = 64, FM = 4, WM = 128;  // wave tile 128 (m) x 64 (n)
+  static_assert(BM == 256 || BM == 128, "tile rows");
+  constexpr int NW = 8, NT = 64 * NW, BN = 256;
+  constexpr int FN = 2, WN = 64, FM = BM / 64, WM = BM / 2;  // wave tile BM/2 (m) x 64 (n)
   __shared__ __attribute__((aligned(1024))) uint16_t s_act0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t s_act1[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t s_wt0[BN * kBK];
@@ -708,18 +710,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
 
 // (explicit instantiations: the host-side launch stubs of these templates are
 // otherwise not always emitted)
-template __global__ void k_gemm_big<false>(GemmArgs);
-template __global__ void k_gemm_big<true>(GemmArgs);
+template __global__ void k_gemm_big<false, 256>(GemmArgs);
+template __global__ void k_gemm_big<true, 256>(GemmArgs);
+template __global__ void k_gemm_big<false, 128>(GemmArgs);
+template __global__ void k_gemm_big<true, 128>(GemmArgs);
 
 namespace {
+// Tile shape of a launch.  The 8-wave kernel takes 256-column tiles of
+// 256 rows when they fill at least one wave of CUs (one tile per CU at a
+// time), else of 128 rows when those do (N = 1024 at T = 8192: 128 tiles of
+// 256 x 256, 256 of 128 x 256); smaller grids take the 4-wave 128 x 128
+// kernel.  (128-row tiles measured slower than 256-row ones also where they
+// would fill the last wave better: the 8B MLP's 896 tiles = 3.5 waves.)
+struct TileChoice {
+  int bm, bn;  // bn 256: k_gemm_big<., bm>; bn 128: k_gemm<128, 128, ...>
+};
+TileChoice choose_tiles(int64_t M, int64_t N) {
+  const int cus0 = device_cus();
+  const int64_t cus = cus0 > 0 ? cus0 : 256;
+  if (ceil_div(M, 256) * ceil_div(N, 256) >= cus) return {256, 256};
+  if (ceil_div(M, 128) * ceil_div(N, 256) >= cus) return {128, 256};
+  return {128, 128};
+}
+
 template <bool kNf4>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
-  // 256 x 256 tiles (8 waves) when they give at least one full wave of
-  // workgroups, else 128 x 128 (4 waves)
-  const int64_t big = ceil_div(a.M, 256) * ceil_div(a.N, 256);
-  if (big >= 256) {
-    dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 256)), static_cast<uint32_t>(ceil_div(a.N, 256)));
-    hipLaunchKernelGGL((k_gemm_big<kNf4>), grid, dim3(512), 0, s, a);
+  const TileChoice tc = choose_tiles(a.M, a.N);
+  if (tc.bn == 256) {
+    dim3 grid(static_cast<uint32_t>(ceil_div(a.M, tc.bm)), static_cast<uint32_t>(ceil_div(a.N, 256)));
+    if (tc.bm == 256) hipLaunchKernelGGL((k_gemm_big<kNf4, 256>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_big<kNf4, 128>), grid, dim3(512), 0, s, a);
   } else {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 128)), static_cast<uint32_t>(ceil_div(a.N, 128)));
     hipLaunchKernelGGL((k_gemm<128, 128, 2, 2, kNf4>), grid, dim3(256), 0, s, a);
@@ -751,7 +771,7 @@ hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const 
   int64_t n = 0;
   for (int i = 0; i < nproj; ++i) n += rows[i];
   a.N = n;
-  const int64_t tile = ceil_div(M, 256) * ceil_div(n, 256) >= 256 ? 256 : 128;
+  const int64_t tile = choose_tiles(M, n).bn;
   for (int i = 0; i + 1 < nproj; ++i)
     if (rows[i] % tile != 0) return hipErrorInvalidValue;  // a tile would straddle two projections
   a.nseg = nproj;
@@ -766,7 +786,7 @@ hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const 
 bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows) {
   int64_t n = 0;
   for (int i = 0; i < nproj; ++i) n += rows[i];
-  const int64_t tile = ceil_div(M, 256) * ceil_div(n, 256) >= 256 ? 256 : 128;
+  const int64_t tile = choose_tiles(M, n).bn;
   for (int i = 0; i + 1 < nproj; ++i)
     if (rows[i] % tile != 0) return false;
   return true;
@@ -783,7 +803,7 @@ hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint
   for (int i = 0; i < nproj; ++i) n += proj[i].rows;
   a.N = n;
   // one launch when no tile straddles two projections, else one per projection
-  const int64_t tile = ceil_div(M, 256) * ceil_div(n, 256) >= 256 ? 256 : 128;
+  const int64_t tile = choose_tiles(M, n).bn;
   bool aligned = true;
   for (int i = 0; i + 1 < nproj; ++i) aligned = aligned && (proj[i].rows % tile == 0);
   if (aligned) {
