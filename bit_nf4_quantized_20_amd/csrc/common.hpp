@@ -157,12 +157,9 @@ constexpr int64_t kDecodeMaxT = 16;
 constexpr int64_t kDecodeFusedMaxWgs = 256;
 constexpr int64_t kDecodeMaxRank = 64;
 bool decode_fits(int64_t T, int64_t in, int64_t out, int64_t r);
-// One projection of the small-token forward: its NF4 weight [out][in] and
-// LoRA factors A [r][in], B [out][r].
-// Small-token input gradient dX = dY W_hat + (sV) A (T <= kDxSmallMaxT, no
-// dropout), n projections stacked along W's rows: projection i's rows start
-// at row0 (its dY columns).  part: fp32 scratch of part_bytes (the
-// partials of the row splits).
+// Small-token backward (T <= kDxSmallMaxT, no dropout): dX, dA and dB of n
+// projections stacked along W's rows (projection i's rows start at row0, its
+// dY columns), in three launches (k_dx_small.hip).
 constexpr int kDxSmallMaxT = 16;
 // The row splits' partials are sized for this many workgroups (two per CU
 // on a 256-CU device); with more CUs the split count is capped by the space.
@@ -177,9 +174,29 @@ struct DxSet {
   DxProj proj[kMaxProj];
   int n;
 };
-hipError_t launch_dx_small(const DxSet& set, int64_t N, int64_t in, const uint16_t* dY, int T, const DownFactors& A,
-                           int r, const uint16_t* v_pad, int64_t ldv, int64_t rp, uint16_t* dX, float* part,
-                           size_t part_bytes, bool absmax_fp32, hipStream_t s);
+// Everything the small-token backward's kernels read, by value.  The host
+// fills the inputs; launch_bwd_small fills the split and chunk counts.
+struct BwdSmallDev {
+  DxSet set;
+  DownFactors A, B;           // A_i [r][in], B_i [out_i][r]
+  int64_t out[kMaxProj];
+  int vc0[kMaxProj + 1];      // first V chunk of each projection
+  int n, T, r, splits, per, nu, gp;
+  int64_t N, in;
+  const uint16_t* X;          // [T][in]
+  const uint16_t* dY;         // [T][N]
+  float* dxp;                 // dX row-split partials [splits][T][in]
+  float* uvp;                 // U and V chunk partials (bwd_small_uv_bytes)
+  float* su;                  // s U_i [n][T][r]
+  float* sv;                  // s V_i [n][T][r]
+  float s;
+  uint16_t* dX;
+  float* dA[kMaxProj];
+  float* dB[kMaxProj];
+};
+// dxp_bytes: the space at dxp (caps the row splits)
+hipError_t launch_bwd_small(BwdSmallDev a, size_t dxp_bytes, bool absmax_fp32, hipStream_t s);
+size_t bwd_small_uv_bytes(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r);
 
 struct DecodeProj {
   const uint8_t* codes; const uint8_t* absmax_q; const float* scale;

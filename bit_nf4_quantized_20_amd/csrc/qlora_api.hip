@@ -88,7 +88,7 @@ struct FwdLayout {
 // costs more than one extra pass of 2.5 bytes per weight.
 constexpr int64_t kMaterializeTokens = 2048;
 struct BwdLayout {
-  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, total;
+  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, uvp, suv, total;
 };
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
@@ -135,10 +135,11 @@ FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 
 int64_t token_pitch(int64_t T) { return round_up(T, 8); }
 
-// Up to kDxSmallMaxT tokens without dropout, dX streams the codes once
-// (k_dx_small): no W_hat^T and no padded A^T, and the W_hat^T region holds
-// the fp32 row-split partials instead ([splits][T][in], at most
-// dx_small_max_splits of them).
+// Up to kDxSmallMaxT tokens without dropout the backward is the three
+// launches of k_dx_small.hip: no W_hat^T, no padded factors; the W_hat^T
+// region holds the fp32 row-split partials of dX instead ([splits][T][in],
+// at most dx_small_max_splits of them), then the U / V chunk partials and
+// sU, sV [n][T][r] fp32.
 bool bwd_small(int64_t T, bool dropout) { return T <= kDxSmallMaxT && !dropout; }
 
 BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout) {
@@ -152,15 +153,20 @@ BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
     part = pv > part ? pv : part;
   }
   Carve c;
-  BwdLayout l;
-  l.ut = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));  // [n][2rp][T'] bf16
-  l.vt = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));
-  l.v_pad = c.take(static_cast<size_t>(T * n * rp * 4));                // [T][n 2rp] bf16
-  l.b_t = c.take(static_cast<size_t>(r * out_max * 2));                 // one B^T at a time
-  l.a_t_pad = c.take(small ? 0 : static_cast<size_t>(in * n * rp * 4));  // [in][n 2rp] bf16
-  l.w_dq_t = c.take(small ? static_cast<size_t>(dx_small_max_splits(N, in) * T * in * 4)
-                          : static_cast<size_t>(in * N * 2));             // [in][N] bf16
-  l.part = c.take(part);
+  BwdLayout l{};
+  if (small) {
+    l.w_dq_t = c.take(static_cast<size_t>(dx_small_max_splits(N, in) * T * in * 4));  // dX partials
+    l.uvp = c.take(bwd_small_uv_bytes(T, in, outs, n, r));
+    l.suv = c.take(static_cast<size_t>(2 * n * T * r * 4));
+  } else {
+    l.ut = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));  // [n][2rp][T'] bf16
+    l.vt = c.take(static_cast<size_t>(n * 2 * rp * token_pitch(T) * 2));
+    l.v_pad = c.take(static_cast<size_t>(T * n * rp * 4));                // [T][n 2rp] bf16
+    l.b_t = c.take(static_cast<size_t>(r * out_max * 2));                 // one B^T at a time
+    l.a_t_pad = c.take(static_cast<size_t>(in * n * rp * 4));             // [in][n 2rp] bf16
+    l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));                   // [in][N] bf16
+    l.part = c.take(part);
+  }
   l.total = c.off;
   return l;
 }
@@ -452,6 +458,37 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   if (int st = check_device()) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = alpha / static_cast<float>(r);
+  const int64_t N = total_out(outs, n);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  if (T > 0 && bwd_small(T, keep != nullptr)) {
+    // three launches; dA and dB are written, not accumulated
+    BwdSmallDev a{};
+    a.set.n = a.n = n;
+    int64_t row0 = 0;
+    for (int i = 0; i < n; ++i) {
+      a.set.proj[i] = DxProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, row0};
+      a.A.p[i] = A[i];
+      a.B.p[i] = B[i];
+      a.out[i] = outs[i];
+      a.dA[i] = dA[i];
+      a.dB[i] = dB[i];
+      row0 += outs[i];
+    }
+    a.T = static_cast<int>(T);
+    a.r = static_cast<int>(r);
+    a.N = N;
+    a.in = in;
+    a.X = X;
+    a.dY = dY;
+    a.dxp = reinterpret_cast<float*>(base + lay.w_dq_t);
+    a.uvp = reinterpret_cast<float*>(base + lay.uvp);
+    a.su = reinterpret_cast<float*>(base + lay.suv);
+    a.sv = a.su + n * T * r;
+    a.s = scale;
+    a.dX = dX;
+    return launched(launch_bwd_small(a, lay.uvp - lay.w_dq_t, absmax_fp32(W[0]), s));
+  }
   // dA_i, dB_i are overwritten: zeroed here (one launch), the gradient
   // kernels then add their token slices
   float* zero_dst[kMaxFill];
@@ -465,9 +502,7 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   hipError_t e = launch_fill_many_f32(zero_dst, zero_n, 2 * n, 0.f, s);
   if (T == 0 || e != hipSuccess) return launched(e);
 
-  const float scale = alpha / static_cast<float>(r);
-  const int64_t rp = padded_rank(r), tp = token_pitch(T), N = total_out(outs, n);
-  uint8_t* base = static_cast<uint8_t*>(ws);
+  const int64_t rp = padded_rank(r), tp = token_pitch(T);
   uint16_t* ut = reinterpret_cast<uint16_t*>(base + lay.ut);
   uint16_t* vt = reinterpret_cast<uint16_t*>(base + lay.vt);
   uint16_t* v_pad = reinterpret_cast<uint16_t*>(base + lay.v_pad);
@@ -481,11 +516,8 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   const float inv_keep = keep != nullptr ? 1.f / (1.f - p) : 1.f;
   e = launch_lora_down(X, in, T, in, A, n, r, scale * inv_keep, nullptr, 0, ut, tp, rp, part, s, keep,
                        in / 8);
-  // Up to kDxSmallMaxT tokens (no dropout) dX streams the codes once
-  // (k_dx_small: W_hat only in LDS tiles, row-split partials in the W_hat^T
-  // region of the workspace); otherwise W_hat^T is expanded and a GEMM runs.
-  const bool dx_small = bwd_small(T, keep != nullptr);
-  const size_t w_dq_t_bytes = lay.part - lay.w_dq_t;
+  // W_hat^T is expanded and a GEMM runs (small token counts without dropout
+  // took the streamed path above)
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     // s V_i = s dY_i B_i with dY_i the projection's columns of dY
@@ -494,28 +526,13 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     if (e == hipSuccess)
       e = launch_lora_down(dY + off, N, T, outs[i], &bt, 1, r, scale, v_pad + i * 2 * rp, n * 2 * rp,
                            vt + i * 2 * rp * tp, tp, rp, part, s);
-    if (!dx_small) {
-      if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
-      if (e == hipSuccess)
-        e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
-                                             w_dq_t + off, N, s, absmax_fp32(W[i]));
-    }
+    if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
+    if (e == hipSuccess)
+      e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
+                                           w_dq_t + off, N, s, absmax_fp32(W[i]));
     off += outs[i];
   }
-  if (dx_small) {
-    DxSet set{};
-    DownFactors af{};
-    set.n = n;
-    int64_t row0 = 0;
-    for (int i = 0; i < n; ++i) {
-      set.proj[i] = DxProj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, row0};
-      af.p[i] = A[i];
-      row0 += outs[i];
-    }
-    if (e == hipSuccess)
-      e = launch_dx_small(set, N, in, dY, static_cast<int>(T), af, static_cast<int>(r), v_pad, n * 2 * rp, rp, dX,
-                          reinterpret_cast<float*>(w_dq_t), w_dq_t_bytes, absmax_fp32(W[0]), s);
-  } else if (e == hipSuccess) {
+  if (e == hipSuccess) {
     // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
     // (with dropout the adapter term is masked and scaled by 1 / (1 - p)
     // before the base is added)

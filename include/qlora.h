@@ -171,8 +171,9 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  * the transposed dequantized weight of the backward from T = 17 on or with
  * dropout, and, from T = 2048 on, the forward's dequantized weight: 2 * out
  * * in bytes each).  Up to T = 16 without dropout the backward keeps no
- * dequantized weight: it holds fp32 row-split partials of dX instead
- * (splits * T * in * 4 bytes, splits <= ceil(512 / (in / 64))).  It needs no
+ * dequantized weight: it holds fp32 row-split partials of dX
+ * (splits * T * in * 4 bytes, splits <= ceil(512 / (in / 64))) and the
+ * rank-r reductions' partials (T * r * 4 bytes per 128 columns / rows).  It needs no
  * initialisation and keeps nothing between calls.  The small-token forward
  * (T <= 16 and r <= 64) uses it only for U = X A^T (n * T * r fp32 values),
  * computed once up front when r > 16 or the projections have more than 4096
@@ -282,13 +283,14 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
  *   dB = s dY^T (X A^T)               [out, r] fp32
  * paperclase "QLoRA", Parte 4: dL/dx = (W_hat + (alpha/r) B A)^T dL/dh; no
  * gradient for W_hat (the codes are not parameters); A and B are the only
- * trained tensors.  dA and dB are overwritten, not accumulated.  They are
- * sums over token slices added with fp32 atomics, so two identical calls can
- * differ in the last bits of dA and dB (summation order); Y and dX are
- * reproducible bit for bit.  From T = 17 on the backward expands W_hat^T
- * into the workspace (2 * out * in bytes) for its dX product; up to T = 16
- * it streams the codes once, W_hat existing only in LDS tiles, and sums
- * fp32 row-split partials of dX in a fixed order (one rounding).
+ * trained tensors.  dA and dB are overwritten, not accumulated.  From
+ * T = 17 on they are sums over token slices added with fp32 atomics, so two
+ * identical calls can differ in their last bits (summation order), and the
+ * backward expands W_hat^T into the workspace (2 * out * in bytes) for its
+ * dX product.  Up to T = 16 it streams the codes once, W_hat existing only
+ * in LDS tiles, sums fp32 row-split partials of dX in a fixed order (one
+ * rounding) and writes each element of dA and dB once (reproducible).  Y
+ * and dX are reproducible bit for bit.
  *   dY [T, out] bf16; other arguments as in qlora_linear_fwd;
  *   ws of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1)
  * T == 0 writes zeros to dA and dB and nothing else (X, dY, dX may be NULL).

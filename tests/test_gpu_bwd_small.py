@@ -1,13 +1,14 @@
-"""GPU parity of the small-token backward (T <= 16, no dropout): dX streams
-the NF4 codes once (k_dx_small_part: row-split partials of dY W_hat with
-W_hat only in LDS, then k_dx_small_fin adds the splits in order and the
-adapter term (sV) A, one rounding) -- against the fp64 oracle at the 8B MLP
-shapes and for a multi-projection call, plus bit-exact one-hot pins through
-the row splits and a repeat-call reproducibility check.
+"""GPU parity of the small-token backward (T <= 16, no dropout), three
+launches: the dX row splits stream the NF4 codes once (W_hat only in LDS)
+next to the chunked rank-r reductions U = X A^T and V = dY B; then sU and
+sV; then dX (the splits added in order plus the adapter term, one rounding),
+dA and dB (each element written once) -- against the fp64 oracle at the 8B
+MLP shapes and for a multi-projection call, plus bit-exact one-hot pins
+through the row splits and a repeat-call reproducibility check.
 
 Acceptance: relative Frobenius error <= 2e-3 on dX, dA, dB (full tensors);
 one-hot dY rows with A = 0 select rows of W_hat bit for bit; a repeated call
-gives the same dX bits."""
+gives the same dX, dA and dB bits."""
 
 import numpy as np
 import pytest
@@ -56,8 +57,10 @@ def test_small_token_bwd_matches_oracle(T, n_in, n_out, r):
             odense.rel_frobenius(host(dB).astype(np.float64), rdB)]
     print(f"  dX={errs[0]:.2e} dA={errs[1]:.2e} dB={errs[2]:.2e}", flush=True)
     assert all(e <= TOL for e in errs), errs
-    dX2, _, _ = q.qlora_linear_bwd(W, Xd, dYd, Ad, Bd, r, alpha)
+    dX2, dA2, dB2 = q.qlora_linear_bwd(W, Xd, dYd, Ad, Bd, r, alpha)
     assert np.array_equal(host_bits(dX2), host_bits(dX))
+    # each element of dA and dB is written once (no atomics): reproducible too
+    assert np.array_equal(host(dA2), host(dA)) and np.array_equal(host(dB2), host(dB))
 
 
 def test_small_token_bwd_multi_projection():
