@@ -181,7 +181,7 @@ struct BwdSmallDev {
   DownFactors A, B;           // A_i [r][in], B_i [out_i][r]
   int64_t out[kMaxProj];
   int vc0[kMaxProj + 1];      // first V chunk of each projection
-  int n, T, r, splits, per, nu, gp;
+  int n, T, r, splits, per, nu, gp, uvw;
   int64_t N, in;
   const uint16_t* X;          // [T][in]
   const uint16_t* dY;         // [T][N]

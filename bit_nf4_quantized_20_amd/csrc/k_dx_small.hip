@@ -150,16 +150,20 @@ __device__ __forceinline__ void uv_part(const BwdSmallDev& a, int q, uint16_t* l
 }
 }  // namespace
 
-// Launch 1: workgroups [0, gp) the dX row splits, then the U and V chunks.
+// Launch 1: workgroups [0, a.uvw) the U and V chunks (first, so that they
+// run beside the dX row splits instead of after them; the count is padded to
+// a multiple of 8, the padding exits at once, so the splits keep their XCD
+// order), then [a.uvw, a.uvw + gp) the dX row splits.
 template <bool kFp32>
 __global__ __launch_bounds__(256) void k_bwd_small_part(BwdSmallDev a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_w[4][64 * kDxPitch];
   __shared__ f32x4 s_acc[4][4][64];
-  const int L = static_cast<int>(blockIdx.x);
-  if (L >= a.gp) {  // (uniform)
-    uv_part(a, L - a.gp, &s_w[0][0]);
+  const int L0 = static_cast<int>(blockIdx.x);
+  if (L0 < a.uvw) {  // (uniform)
+    if (L0 < a.nu + a.vc0[a.n]) uv_part(a, L0, &s_w[0][0]);
     return;
   }
+  const int L = L0 - a.uvw;
   const DxSet& P = a.set;
   const int64_t in = a.in, N = a.N;
   const uint16_t* __restrict__ dY = a.dY;
@@ -324,6 +328,7 @@ __global__ __launch_bounds__(256) void k_bwd_small_fin(BwdSmallDev a) {
     if (tl < nt) {
       const int64_t o = static_cast<int64_t>(t) * in + n0 + col;
       float base = 0.f;
+#pragma unroll 8
       for (int sp = 0; sp < a.splits; ++sp) base += a.dxp[static_cast<int64_t>(sp) * T * in + o];
       a.dX[o] = static_cast<uint16_t>(pack_bf16x2(base + lora, 0.f));
     }
@@ -402,7 +407,8 @@ hipError_t launch_bwd_small(BwdSmallDev a, size_t dxp_bytes, bool absmax_fp32, h
   a.nu = static_cast<int>(ceil_div(a.in, kUvChunk));
   a.vc0[0] = 0;
   for (int i = 0; i < a.n; ++i) a.vc0[i + 1] = a.vc0[i] + static_cast<int>(ceil_div(a.out[i], kUvChunk));
-  const uint32_t g1 = static_cast<uint32_t>(a.gp + a.nu + a.vc0[a.n]);
+  a.uvw = static_cast<int>(round_up(a.nu + a.vc0[a.n], 8));
+  const uint32_t g1 = static_cast<uint32_t>(a.uvw + a.gp);
   if (absmax_fp32) hipLaunchKernelGGL(k_bwd_small_part<true>, dim3(g1), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_bwd_small_part<false>, dim3(g1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
