@@ -86,6 +86,39 @@ def test_small_token_bwd_multi_projection():
     assert err <= TOL
 
 
+@pytest.mark.parametrize("T,n_in,outs,r", [
+    (5, 320, [192], 200),       # ranks in a 64 + 64 + 64 + 8 loop, a 64-wide last U chunk, a 64-row V chunk
+    (1, 64, [64], 1),           # one strip, one 64-row chunk, rank 1
+    (13, 320, [192, 64], 24),   # two projections: V chunks and dB rows per projection
+    (16, 1024, [128, 1024, 64], 256),  # the largest rank
+])
+def test_small_token_bwd_edge_shapes(T, n_in, outs, r):
+    q = require_gpu()
+    banner(f"small-token bwd edges T={T} in={n_in} outs={outs} r={r}")
+    alpha = 1.5 * r
+    ws, As, Bs, X, dY = _case(13000 + T + r, T, n_in, outs, r)
+    Ws = [q.nf4_quantize_weight(dev_f32(w)) for w in ws]
+    if len(outs) == 1:
+        dX, dA, dB = q.qlora_linear_bwd(Ws[0], dev_bf16(X), dev_bf16(dY), dev_bf16(As[0]), dev_bf16(Bs[0]), r,
+                                        alpha)
+        dAs, dBs = [dA], [dB]
+    else:
+        dX, dAs, dBs = q.qlora_linear_bwd_multi(Ws, dev_bf16(X), dev_bf16(dY), [dev_bf16(a) for a in As],
+                                                [dev_bf16(b) for b in Bs], r, alpha)
+    rdX = np.zeros((T, n_in))
+    off = 0
+    for i, (w, A, B) in enumerate(zip(ws, As, Bs)):
+        rX, rA, rB = odense.linear_bwd(_w_hat(w), X, dY[:, off:off + outs[i]], A, B, alpha, r)
+        rdX += rX
+        ea = odense.rel_frobenius(host(dAs[i]).astype(np.float64), rA)
+        eb = odense.rel_frobenius(host(dBs[i]).astype(np.float64), rB)
+        assert ea <= TOL and eb <= TOL, (i, ea, eb)
+        off += outs[i]
+    err = odense.rel_frobenius(onf4.bf16_bits_to_f32(host_bits(dX)).astype(np.float64), rdX)
+    print(f"  dX={err:.2e}", flush=True)
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("T,n_out", [(3, 14336), (16, 2048)])
 def test_small_token_bwd_one_hot_bit_exact(T, n_out):
     # dY rows one-hot, A = 0: dX[t] = W_hat[row_t] exactly, whichever row
