@@ -310,8 +310,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_stream(DecodeSet P, int in,
         issue(cs[d]);
       }
     }
-    // ---- epilogue of the row block: the 8 waves' partials meet in LDS,
-    // Y = base + s U B^T, rounded to bf16 once
+    // ---- epilogue of the row block: the 8 waves' partials meet in LDS;
+    // wave 0 adds s U B^T with four MFMAs (the block's 16 B rows x (s U)^T
+    // as bf16 hi + lo, 2 x 32 ranks) and stores Y, rounded to bf16 once.
+    // The other waves go on with the next row block.
     const int buf = rbl & 1;
     s_part[buf][wv][lane] = acc;
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -327,25 +329,42 @@ __global__ __launch_bounds__(kThreads) void k_decode_stream(DecodeSet P, int in,
     (&s_b[buf][0][0])[tid] = static_cast<uint16_t>(b0);
     (&s_b[buf][0][0])[tid + kThreads] = static_cast<uint16_t>(b1);
     __syncthreads();
-    const int R = __builtin_amdgcn_readfirstlane(rb0 + rbl);
-    const Slot sl = kSingle ? sl0 : pick(R, sl0, sl1);
-    const int rbp = R - sl.wg0;
-    const int slot = R >= sl1.wg0 ? 1 : 0;  // U of the first or second projection
-    uint16_t* __restrict__ Y = sl.Y + 16 * rbp;
-    for (int o = tid; o < T * 64; o += kThreads) {
-      const int t = o >> 6, m = (o >> 2) & 15, jq = o & 3;
-      float lora = 0.f;
+    if (wv == 0) {
+      const int R = __builtin_amdgcn_readfirstlane(rb0 + rbl);
+      const Slot sl = kSingle ? sl0 : pick(R, sl0, sl1);
+      const int rbp = R - sl.wg0;
+      const int slot = R >= sl1.wg0 ? 1 : 0;  // U of the first or second projection
+      // D[row 4 g + e][token n] = sum_j B[row][j] (s U)[n][j]: lane (n, g)
+      // holds B row n's and token n's ranks 32 ks + 8 g .. + 7
+      f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < kRU / 4; ++i)
-        lora += s_u[slot][t][kRU / 4 * jq + i] *
-                __builtin_bit_cast(float, static_cast<uint32_t>(s_b[buf][m][kRU / 4 * jq + i]) << 16);
-      lora += __shfl_xor(lora, 1);
-      lora += __shfl_xor(lora, 2);
-      if (jq == 0) {
-        float base = 0.f;
+      for (int ks = 0; ks < kRU / 32; ++ks) {
+        const u32x4 bf = *reinterpret_cast<const u32x4*>(&s_b[buf][n][32 * ks + 8 * g]);
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) base += s_part[buf][w][16 * (m >> 2) + t][m & 3];
-        Y[static_cast<int64_t>(t) * ldy + m] = static_cast<uint16_t>(pack_bf16x2(base + s * lora, 0.f));
+        for (int e = 0; e < 4; ++e) {
+          const float u0 = s * s_u[slot][n][32 * ks + 8 * g + 2 * e];
+          const float u1 = s * s_u[slot][n][32 * ks + 8 * g + 2 * e + 1];
+          hi[e] = pack_bf16x2(u0, u1);
+          lo[e] = pack_bf16x2(u0 - __builtin_bit_cast(float, hi[e] << 16),
+                              u1 - __builtin_bit_cast(float, hi[e] & 0xffff0000u));
+        }
+        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bf), as_bf16x8(u32x4{hi[0], hi[1], hi[2], hi[3]}),
+                                                       lsum, 0, 0, 0);
+        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bf), as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]}),
+                                                       lsum, 0, 0, 0);
+      }
+      // the waves' partials of the same four outputs, in a fixed order
+      f32x4 base = s_part[buf][0][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        const f32x4 pw = s_part[buf][w][lane];
+        base = f32x4{base[0] + pw[0], base[1] + pw[1], base[2] + pw[2], base[3] + pw[3]};
+      }
+      if (n < T) {
+        uint16_t* __restrict__ Y = sl.Y + static_cast<int64_t>(n) * ldy + 16 * rbp + 4 * g;
+        *reinterpret_cast<u32x2*>(Y) = u32x2{pack_bf16x2(base[0] + lsum[0], base[1] + lsum[1]),
+                                             pack_bf16x2(base[2] + lsum[2], base[3] + lsum[3])};
       }
     }
   }
