@@ -367,21 +367,41 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
     }
   }
   __syncthreads();
-  // Y = base + s U B^T: four adjacent lanes per output, each summing a quarter
-  // of the kRU ranks (ranks >= r are zero in U and B)
-  for (int o = tid; o < T * 64; o += kThreads) {
-    const int t = o >> 6, m = (o >> 2) & 15, jq = o & 3;
-    float lora = 0.f;
+  // Y = base + s U B^T in wave 0: B rows x (s U)^T as bf16 hi + lo on MFMA
+  // (32 ranks per pair of MFMAs; ranks >= r are zero in U and B), added to
+  // the dequantize waves' partials of the same four outputs in a fixed
+  // order; lane (n, g) holds rows 4 g .. + 3 of token n
+  if (wv == 0) {
+    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kRU / 4; ++i) lora += s_u[t][kRU / 4 * jq + i] * s_b[m][kRU / 4 * jq + i];
-    lora += __shfl_xor(lora, 1);
-    lora += __shfl_xor(lora, 2);
-    if (jq == 0) {
-      float base = 0.f;
+    for (int ks = 0; ks < (kRU + 31) / 32; ++ks) {
+      const int j0 = 32 * ks + 8 * g;
+      uint32_t bq[4] = {0u, 0u, 0u, 0u}, hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+      if (j0 < kRU) {
 #pragma unroll
-      for (int w = 0; w < kPairs; ++w) base += s_acc[w][16 * (m >> 2) + t][m & 3];
-      Y[static_cast<int64_t>(t) * ldy + r0 + m] = static_cast<uint16_t>(pack_bf16x2(base + s * lora, 0.f));
+        for (int e = 0; e < 4; ++e) {
+          // B values are bf16 held as fp32: their top halves are exact
+          bq[e] = (__builtin_bit_cast(uint32_t, s_b[n][j0 + 2 * e]) >> 16) |
+                  (__builtin_bit_cast(uint32_t, s_b[n][j0 + 2 * e + 1]) & 0xffff0000u);
+          const float u0 = s * s_u[n][j0 + 2 * e], u1 = s * s_u[n][j0 + 2 * e + 1];
+          hi[e] = pack_bf16x2(u0, u1);
+          lo[e] = pack_bf16x2(u0 - __builtin_bit_cast(float, hi[e] << 16),
+                              u1 - __builtin_bit_cast(float, hi[e] & 0xffff0000u));
+        }
+      }
+      const bf16x8 fb = as_bf16x8(u32x4{bq[0], bq[1], bq[2], bq[3]});
+      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, as_bf16x8(u32x4{hi[0], hi[1], hi[2], hi[3]}), lsum, 0, 0, 0);
+      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]}), lsum, 0, 0, 0);
     }
+    f32x4 base = s_acc[0][lane];
+#pragma unroll
+    for (int w = 1; w < kPairs; ++w) {
+      const f32x4 pw = s_acc[w][lane];
+      base = f32x4{base[0] + pw[0], base[1] + pw[1], base[2] + pw[2], base[3] + pw[3]};
+    }
+    if (n < T)
+      *reinterpret_cast<u32x2*>(Y + static_cast<int64_t>(n) * ldy + r0 + 4 * g) =
+          u32x2{pack_bf16x2(base[0] + lsum[0], base[1] + lsum[1]), pack_bf16x2(base[2] + lsum[2], base[3] + lsum[3])};
   }
 }
 
