@@ -356,15 +356,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
       const int t = idx / kRU, j = idx % kRU;
       s_u[t][j] = (t < T && j < r) ? up[t * r + j] : 0.f;
     }
-  } else {
-    __syncthreads();
-    if (tid < 256) {
-      const int t = tid >> 4, j = tid & 15;  // U[t][j]: lane 16 (j/4) + t, element j % 4
-      float u = 0.f;
-#pragma unroll
-      for (int w = kPairs; w < kWaves; ++w) u += s_acc[w][16 * (j >> 2) + t][j & 3];
-      s_u[t][j] = u;
-    }
   }
   __syncthreads();
   // Y = base + s U B^T in wave 0: B rows x (s U)^T as bf16 hi + lo on MFMA
@@ -372,6 +363,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
   // the dequantize waves' partials of the same four outputs in a fixed
   // order; lane (n, g) holds rows 4 g .. + 3 of token n
   if (wv == 0) {
+    // U[t][j]: up front in s_u, or the U waves' partials D[j][t] (lane
+    // 16 (j / 4) + t, element j % 4 of each), added in a fixed order
+    auto u_at = [&](int t, int j) {
+      if constexpr (kPreU) {
+        return s_u[t][j];
+      } else {
+        float u = 0.f;
+#pragma unroll
+        for (int w = kPairs; w < kWaves; ++w) u += s_acc[w][16 * (j >> 2) + t][j & 3];
+        return u;
+      }
+    };
     f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < (kRU + 31) / 32; ++ks) {
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fwd_split(DecodeSet P, int6
           // B values are bf16 held as fp32: their top halves are exact
           bq[e] = (__builtin_bit_cast(uint32_t, s_b[n][j0 + 2 * e]) >> 16) |
                   (__builtin_bit_cast(uint32_t, s_b[n][j0 + 2 * e + 1]) & 0xffff0000u);
-          const float u0 = s * s_u[n][j0 + 2 * e], u1 = s * s_u[n][j0 + 2 * e + 1];
+          const float u0 = s * u_at(n, j0 + 2 * e), u1 = s * u_at(n, j0 + 2 * e + 1);
           hi[e] = pack_bf16x2(u0, u1);
           lo[e] = pack_bf16x2(u0 - __builtin_bit_cast(float, hi[e] << 16),
                               u1 - __builtin_bit_cast(float, hi[e] & 0xffff0000u));
