@@ -133,6 +133,19 @@ hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const 
 hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,
                            int64_t lda0, int64_t K0, int64_t lda1, const uint16_t* wt1,
                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);
+// dX-shaped product with NF4 weights read transposed: C[M][N] = sum_i
+// act0[m][k_i + k] W_hat_i[k][n] + (LoRA segment, as in launch_gemm_nt), where
+// projection i (proj[i].rows rows of N = in columns, rows % 64 == 0) owns the
+// K range [k_i, k_i + rows) of act0 (row stride lda0), k_i the rows before it.
+// Each weight tile is dequantized and transposed while it is staged into LDS,
+// so W_hat^T never exists in HBM.  proj[i].act1 is not read.  Needs
+// nf4t_fits(rows, in) for every projection (its codes addressed with 32-bit
+// offsets).
+bool nf4t_fits(int64_t rows, int64_t in);
+hipError_t launch_gemm_nf4t(int64_t M, int64_t N, int nproj, const Nf4Proj* proj, const uint16_t* act0,
+                            int64_t lda0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
+                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s,
+                            const uint8_t* keep = nullptr, int64_t ldk = 0, float keep_scale = 1.f);
 
 // W_merged[m][n] = bf16(W_hat[m][n] + s * sum_j Bp[m][j] Atp[n][j]) for the
 // NF4 weight [out][in] (out % 64 == 0, in % 64 == 0); Bp [out][ldp] and Atp

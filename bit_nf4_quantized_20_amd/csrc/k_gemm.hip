@@ -45,6 +45,13 @@ namespace {
 
 constexpr int kBK = 64;
 
+// main-segment weight operand of the GEMM kernels
+constexpr int kWBf16 = 0;  // bf16 matrix [N][K]
+constexpr int kWNf4 = 1;   // NF4 weight [N][K], dequantized while staged
+constexpr int kWNf4T = 2;  // NF4 weight [K][N] (dX), dequantized and transposed while staged
+// row pitch (elements) of a transposed NF4 weight tile in LDS
+constexpr int kPitchT = kBK + 8;
+
 // 16-byte chunk swizzle of a 128-byte LDS row.  A fragment read has 32
 // lanes on 32 consecutive rows at one chunk; the key (row & 7) ^ (row >> 3 & 1)
 // gives every 8 consecutive rows distinct chunks (32-bank view) and every 16
@@ -202,6 +209,18 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chu
   const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kBK + swz(row, chunk) * 8);
   return __builtin_bit_cast(bf16x8, v);
 }
+// The same from a padded tile (rows of kPitchT elements, no swizzle).
+__device__ __forceinline__ bf16x8 lds_frag_pad(const uint16_t* lds, int row, int chunk) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kPitchT + chunk * 8);
+  return __builtin_bit_cast(bf16x8, v);
+}
+// A weight fragment of the main segment (kPad: a transposed NF4 tile) or of
+// the LoRA segment (always swizzled).
+template <bool kPad>
+__device__ __forceinline__ bf16x8 wt_frag(const uint16_t* lds, int row, int chunk) {
+  if constexpr (kPad) return lds_frag_pad(lds, row, chunk);
+  else return lds_frag(lds, row, chunk);
+}
 
 // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
 // XCDs (linear id % 8), and each XCD has its own L2.  The tiles are renumbered
@@ -291,6 +310,88 @@ __device__ __forceinline__ Nf4Seg seg_of(const GemmArgs& p, int64_t n0) {
   return sg;
 }
 
+// Register set of a weight tile staged through registers (none for tiles
+// copied straight into LDS).
+struct NoRegs {};
+template <class T, bool kReg>
+struct RegsOf { using type = NoRegs; };
+template <class T>
+struct RegsOf<T, true> { using type = typename T::Regs; };
+
+// NF4 weights read transposed, for dX = dY W_hat: the tile holds W_hat^T rows
+// [n0, n0 + ROWS) -- columns of W -- by 64 K, and K runs along W's rows (over
+// several projections, the projections' rows one after another: each K-step
+// picks its projection from the table).  The 64-weight blocks run along W's
+// rows, i.e. across the tile's rows, so wave g takes the 32 columns
+// [n0 + 32 g, n0 + 32 g + 32) and lane k row k of each K-step: its 16 code
+// bytes (half a block), the block's absmax code and group scale.  At store
+// time the lane expands its 32 weights with the block's table and writes each
+// one into its column's LDS row, 16 bits at a time.  This tile uses padded
+// rows (kPitchT elements, no XOR swizzle), so (column n, row k) sits at
+// n kPitchT + k: one per-lane base plus an immediate offset per column, and a
+// wave's 64 lanes write one whole 128-byte row per instruction.  Eight
+// consecutive rows of 144 bytes start in distinct 16-byte bank groups, so the
+// fragment reads stay conflict-free.
+template <int ROWS, int NT>
+struct Nf4TileT {
+  static_assert(NT == 2 * ROWS, "one wave per 32 columns");
+  static constexpr int kDw = 4;  // code dwords (8 weights each) per thread
+  struct Regs {
+    uint32_t cw[kDw];
+    uint32_t q;
+    float sg;
+  };
+  const GemmArgs* p;  // projection table: seg[i].n0 = first K row, .rows = rows
+  int64_t in;
+  uint32_t coff, qoff;  // this lane's code byte / absmax code in row 0 of a projection
+  uint32_t bcol;        // its column block
+  uint32_t slot;        // LDS element index of (column 32 g, row k)
+
+  // the tile's first column n0 (columns past `in` load valid data that is never stored)
+  __device__ __forceinline__ void init(const GemmArgs& args, int64_t n0, int tid) {
+    const int k = tid & 63, g = tid >> 6;
+    p = &args;
+    in = args.N;
+    int64_t c0 = n0 + 32 * g;
+    if (c0 >= in) c0 = in - 32;
+    coff = static_cast<uint32_t>(k * (in / 2) + c0 / 2);
+    qoff = static_cast<uint32_t>(k * (in / 64) + c0 / 64);
+    bcol = static_cast<uint32_t>(c0 / 64);
+    slot = static_cast<uint32_t>(32 * g * kPitchT + k);
+  }
+  // K-step starting at row k0 of the stacked projections
+  __device__ __forceinline__ void load(Regs& r, int64_t k0) const {
+    const Nf4Seg sg = seg_of(*p, k0);
+    const int64_t kr = k0 - sg.n0;  // first row of the step within its projection
+    const __amdgpu_buffer_rsrc_t rc = rows_rsrc(sg.codes, in / 2, 0, sg.rows, 1);
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(sg.absmax_q, in / 64, 0, sg.rows, 1);
+    const u32x4 v = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff, static_cast<int>(kr * (in / 2)), kStream));
+    r.cw[0] = v[0]; r.cw[1] = v[1]; r.cw[2] = v[2]; r.cw[3] = v[3];
+    r.q = __builtin_amdgcn_raw_buffer_load_b8(rq, qoff, static_cast<int>(kr * (in / 64)), 0);
+    const int k = static_cast<int>(threadIdx.x & 63);
+    r.sg = sg.scale[((kr + k) * (in / 64) + bcol) >> 8];
+  }
+  __device__ __forceinline__ static Nf4Table table(const Regs& r) { return make_table(dq_absmax(r.q, r.sg)); }
+  // code dword d: the lane's columns 8 d .. 8 d + 7
+  __device__ __forceinline__ void store_part(const Regs& r, const Nf4Table& tab, uint16_t* lds, int, int d) const {
+    uint32_t v[4];
+    lookup8_split(tab, r.cw[d], v);
+    uint16_t* const dst = lds + slot;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = kSplitOrder[q];  // element e of the dword sits at split position q
+      const uint32_t w = v[q >> 1];
+      dst[(8 * d + e) * kPitchT] = static_cast<uint16_t>((q & 1) ? (w >> 16) : w);
+    }
+  }
+  __device__ __forceinline__ void store(const Regs& r, uint16_t* lds, int tid) const {
+    const Nf4Table tab = table(r);
+#pragma unroll
+    for (int d = 0; d < kDw; ++d) store_part(r, tab, lds, tid, d);
+  }
+};
+
 }  // namespace
 
 // WAVES_M x WAVES_N waves; each computes a (BM/WAVES_M) x (BN/WAVES_N) sub-tile.
@@ -300,18 +401,19 @@ __device__ __forceinline__ Nf4Seg seg_of(const GemmArgs& p, int64_t n0) {
 // are dequantized here), load step st + 3's tiles into that register set,
 // compute step st.  The main and LoRA segments run this pipeline one after
 // the other, each with register sets of its own operand types.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool kNf4>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int kW>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / 32, FN = WN / 32;
   __shared__ __attribute__((aligned(16))) uint16_t s_act[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_wt[2][BN * kBK];
+  constexpr bool kPadW = kW == kWNf4T;  // main-segment weight tile in padded rows
+  __shared__ __attribute__((aligned(16))) uint16_t s_wt[2][BN * (kPadW ? kPitchT : kBK)];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv % WAVES_M, wn = wv / WAVES_M;
   // NF4: waves 4-7 (sharing SIMDs with waves 0-3) dequantize after computing
-  const bool late = kNf4 && wv >= 4;
+  const bool late = kW != kWBf16 && wv >= 4;
   int64_t mt, nt;
   xcd_tile(gridDim.x, gridDim.y, mt, nt);
   const int64_t m0 = mt * BM;
@@ -326,7 +428,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  auto compute = [&](int b) {
+  auto compute = [&](int b, auto pad) {
+    constexpr bool P = decltype(pad)::value;
     const uint16_t* sa = s_act[b];
     const uint16_t* sw = s_wt[b];
 #pragma unroll
@@ -334,7 +437,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
       const int chunk = 2 * j + half;
       bf16x8 fw[FN], fa[FM];
 #pragma unroll
-      for (int a = 0; a < FN; ++a) fw[a] = lds_frag(sw, wn * WN + a * 32 + r32, chunk);
+      for (int a = 0; a < FN; ++a) fw[a] = wt_frag<P>(sw, wn * WN + a * 32 + r32, chunk);
 #pragma unroll
       for (int c = 0; c < FM; ++c) fa[c] = lds_frag(sa, wm * WM + c * 32 + r32, chunk);
 #pragma unroll
@@ -348,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   // One K segment [first, last) of global steps; the LDS stage of step st is
   // st % 2 throughout.  Two register sets by step parity; Regs::fetch(r, e)
   // loads segment-relative step e, Regs::stash(r, b) writes stage b.
-  auto segment = [&](auto& r0, auto& r1, int64_t first, int64_t last, auto fetch, auto stash) {
+  auto segment = [&](auto& r0, auto& r1, int64_t first, int64_t last, auto fetch, auto stash, auto pad) {
     const int64_t n = last - first;
     if (n <= 0) return;
     fetch(r0, 0);
@@ -365,7 +468,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
         if (e + 1 < n) stash(nxt, static_cast<int>((first + e + 1) & 1));
         if (e + 3 < n) fetch(nxt, e + 3);
       }
-      compute(static_cast<int>((first + e) & 1));
+      compute(static_cast<int>((first + e) & 1), pad);
       if (late) {
         if (e + 1 < n) stash(nxt, static_cast<int>((first + e + 1) & 1));
         if (e + 3 < n) fetch(nxt, e + 3);
@@ -382,7 +485,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   using TW = Bf16Tile<BN, NT>;
   // main segment over global steps [first, first + s0)
   auto main_seg = [&](int64_t first) {
-    if constexpr (kNf4) {
+    if constexpr (kW == kWNf4T) {
+      using TQ = Nf4TileT<BN, NT>;
+      TA ta;
+      TQ tq;
+      ta.init(p.act0, p.lda0, m0, p.M, tid);
+      tq.init(p, n0, tid);
+      struct R { typename TA::Regs a; typename TQ::Regs w; };
+      R r0, r1;
+      segment(r0, r1, first, first + s0,
+              [&](R& r, int64_t e) {
+                ta.load(r.a, e * kBK);
+                tq.load(r.w, e * kBK);
+              },
+              [&](const R& r, int b) {
+                TA::store(r.a, s_act[b], tid);
+                tq.store(r.w, s_wt[b], tid);
+              }, std::true_type{});
+    } else if constexpr (kW == kWNf4) {
       using TQ = Nf4Tile<BN, NT>;
       TA ta;
       TQ tq;
@@ -399,7 +519,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
               [&](const R& r, int b) {
                 TA::store(r.a, s_act[b], tid);
                 TQ::store(r.w, s_wt[b], tid);
-              });
+              }, std::false_type{});
     } else {
       TA ta;
       TW tw;
@@ -415,7 +535,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
               [&](const R& r, int b) {
                 TA::store(r.a, s_act[b], tid);
                 TW::store(r.w, s_wt[b], tid);
-              });
+              }, std::false_type{});
     }
   };
   // LoRA extension segment over global steps [first, first + s1)
@@ -435,7 +555,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
             [&](const R& r, int b) {
               TA::store(r.a, s_act[b], tid);
               TW::store(r.w, s_wt[b], tid);
-            });
+            }, std::false_type{});
   };
   if (p.keep != nullptr) {
     // dropout: the adapter product alone, masked, then the base on top
@@ -469,15 +589,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
 
 // BM x 256 tiles (BM = 256 or 128), 8 waves (see the file comment).
 // Launch: 512 threads.
-template <bool kNf4, int BM>
+template <int kW, int BM>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   static_assert(BM == 256 || BM == 128, "tile rows");
   constexpr int NW = 8, NT = 64 * NW, BN = 256;
   constexpr int FN = 2, WN = 64, FM = BM / 64, WM = BM / 2;  // wave tile BM/2 (m) x 64 (n)
   __shared__ __attribute__((aligned(1024))) uint16_t s_act0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t s_act1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t s_wt0[BN * kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t s_wt1[BN * kBK];
+  constexpr bool kPadW = kW == kWNf4T;  // main-segment weight tile in padded rows
+  constexpr int kWtElems = BN * (kPadW ? kPitchT : kBK);
+  __shared__ __attribute__((aligned(1024))) uint16_t s_wt0[kWtElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_wt1[kWtElems];
   uint16_t* const s_act[2] = {s_act0, s_act1};
   uint16_t* const s_wt[2] = {s_wt0, s_wt1};
 
@@ -498,10 +620,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.f;
 
   typedef bf16x8 Frags[FN + FM];  // [0, FN) weight rows, [FN, FN + FM) activation rows
-  auto read_frags = [&](Frags& f, const uint16_t* sw, const uint16_t* sa, int j) {
+  // kPad: the weight stage holds a padded (transposed NF4) tile
+  auto read_frags = [&](Frags& f, const uint16_t* sw, const uint16_t* sa, int j, auto pad) {
+    constexpr bool P = decltype(pad)::value;
     const int chunk = 2 * j + half;
 #pragma unroll
-    for (int a = 0; a < FN; ++a) f[a] = lds_frag(sw, wn * WN + a * 32 + r32, chunk);
+    for (int a = 0; a < FN; ++a) f[a] = wt_frag<P>(sw, wn * WN + a * 32 + r32, chunk);
 #pragma unroll
     for (int c = 0; c < FM; ++c) f[FN + c] = lds_frag(sa, wm * WM + c * 32 + r32, chunk);
   };
@@ -528,13 +652,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using PadMain = std::integral_constant<bool, kPadW>;
+  using NoPad = std::integral_constant<bool, false>;
 
-  // Main segment.  TW: DtlTile (bf16 weight) or Nf4Tile (codes in registers).
+  // Main segment.  TW: DtlTile (bf16 weight), Nf4Tile or Nf4TileT (codes in registers).
   auto main_loop = [&](DtlTile<BM, NW>& ta, auto& tw, int64_t steps) {
     using TW = std::remove_reference_t<decltype(tw)>;
     constexpr bool kRegW = !std::is_same_v<TW, DtlTile<BN, NW>>;
-    struct NoRegs { };
-    using WRegs = std::conditional_t<kRegW, typename Nf4Tile<BN, NT>::Regs, NoRegs>;
+    using WRegs = typename RegsOf<TW, kRegW>::type;
     const int64_t last = steps - 1;
     WRegs wr[3];
     auto wfetch = [&](WRegs& r, int64_t e) {  // steps past the end re-read the last one
@@ -549,11 +674,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
     wfetch(wr[1], 1);
     wfetch(wr[2], 2);
     copy(0, s_act0, s_wt0);
-    if constexpr (kRegW) TW::store(wr[0], s_wt0, tid);
+    if constexpr (kRegW) tw.store(wr[0], s_wt0, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     Frags f0, f1;
-    read_frags(f0, s_wt0, s_act0, 0);
+    read_frags(f0, s_wt0, s_act0, 0, PadMain{});
     // Step e: stage B holds step e; code set (C + 1) % 3 holds step e + 1 and
     // set C (step e's, consumed) takes step e + 3.
     auto step = [&](int64_t e, auto bc, auto cc) {
@@ -567,10 +692,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       auto part = [&](int d) {  // a quarter of step e+1's weight tile
         if constexpr (kRegW) {
           if constexpr (TW::kDw == 4) {
-            TW::store_part(nxt, tab, nw, tid, d);
+            tw.store_part(nxt, tab, nw, tid, d);
           } else {
-            TW::store_part(nxt, tab, nw, tid, 2 * d);
-            TW::store_part(nxt, tab, nw, tid, 2 * d + 1);
+            tw.store_part(nxt, tab, nw, tid, 2 * d);
+            tw.store_part(nxt, tab, nw, tid, 2 * d + 1);
           }
         }
       };
@@ -579,15 +704,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       __builtin_amdgcn_s_setprio(1);  // the MFMA phase issues ahead of the other wave's loads
       if constexpr (kRegW) tab = TW::table(nxt);
       part(0);
-      read_frags(f1, sw, sa, 1);
+      read_frags(f1, sw, sa, 1, PadMain{});
       mfmas(f0);
       interleave();
       part(1);
-      read_frags(f0, sw, sa, 2);
+      read_frags(f0, sw, sa, 2, PadMain{});
       mfmas(f1);
       interleave();
       part(2);
-      read_frags(f1, sw, sa, 3);
+      read_frags(f1, sw, sa, 3, PadMain{});
       mfmas(f0);
       interleave();
       part(3);
@@ -600,7 +725,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       if constexpr (kRegW) __builtin_amdgcn_s_waitcnt(0x73);  // vmcnt(3) lgkmcnt(0)
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      read_frags(f0, nw, na, 0);
+      read_frags(f0, nw, na, 0, PadMain{});
     };
     int64_t e = 0;
     for (; e + 6 <= steps; e += 6) {
@@ -642,14 +767,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         Frags f;
-        read_frags(f, s_wt0, s_act0, j);
+        read_frags(f, s_wt0, s_act0, j, NoPad{});
         mfmas(f);
       }
       if (two) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           Frags f;
-          read_frags(f, s_wt1, s_act1, j);
+          read_frags(f, s_wt1, s_act1, j, NoPad{});
           mfmas(f);
         }
       }
@@ -661,14 +786,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
     apply_keep<FN, FM>(acc, p, m0 + wm * WM, n0 + wn * WN, r32, half);
     __syncthreads();  // every wave is done reading stage 0 before the main copies
   }
-  DtlTile<BM, NW> ta;
-  ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
-  if constexpr (kNf4) {
+  if constexpr (kW == kWNf4T) {
+    DtlTile<BM, NW> ta;
+    ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
+    Nf4TileT<BN, NT> tq;
+    tq.init(p, n0, tid);
+    main_loop(ta, tq, s0);
+  } else if constexpr (kW == kWNf4) {
+    DtlTile<BM, NW> ta;
+    ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
     Nf4Tile<BN, NT> tq;
     const Nf4Seg sg = seg_of(p, n0);
     tq.init(sg.codes, sg.absmax_q, sg.scale, p.K0, n0 - sg.n0, sg.rows, tid);
     main_loop(ta, tq, s0);
   } else {
+    DtlTile<BM, NW> ta;
+    ta.init(p.act0, p.lda0, m0, p.M, wv, lane);
     DtlTile<BN, NW> tw;
     tw.init(p.wt0, p.ldw0, n0, p.N, wv, lane);
     main_loop(ta, tw, s0);
@@ -710,10 +843,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
 
 // (explicit instantiations: the host-side launch stubs of these templates are
 // otherwise not always emitted)
-template __global__ void k_gemm_big<false, 256>(GemmArgs);
-template __global__ void k_gemm_big<true, 256>(GemmArgs);
-template __global__ void k_gemm_big<false, 128>(GemmArgs);
-template __global__ void k_gemm_big<true, 128>(GemmArgs);
+template __global__ void k_gemm_big<kWBf16, 256>(GemmArgs);
+template __global__ void k_gemm_big<kWNf4, 256>(GemmArgs);
+template __global__ void k_gemm_big<kWNf4T, 256>(GemmArgs);
+template __global__ void k_gemm_big<kWBf16, 128>(GemmArgs);
+template __global__ void k_gemm_big<kWNf4, 128>(GemmArgs);
+template __global__ void k_gemm_big<kWNf4T, 128>(GemmArgs);
 
 namespace {
 // Tile shape of a launch.  The 8-wave kernel takes 256-column tiles of
@@ -733,16 +868,16 @@ TileChoice choose_tiles(int64_t M, int64_t N) {
   return {128, 128};
 }
 
-template <bool kNf4>
+template <int kW>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
   const TileChoice tc = choose_tiles(a.M, a.N);
   if (tc.bn == 256) {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, tc.bm)), static_cast<uint32_t>(ceil_div(a.N, 256)));
-    if (tc.bm == 256) hipLaunchKernelGGL((k_gemm_big<kNf4, 256>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_big<kNf4, 128>), grid, dim3(512), 0, s, a);
+    if (tc.bm == 256) hipLaunchKernelGGL((k_gemm_big<kW, 256>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_big<kW, 128>), grid, dim3(512), 0, s, a);
   } else {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 128)), static_cast<uint32_t>(ceil_div(a.N, 128)));
-    hipLaunchKernelGGL((k_gemm<128, 128, 2, 2, kNf4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<128, 128, 2, 2, kW>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -757,7 +892,7 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
   a.M = M; a.N = N; a.act0 = act0; a.lda0 = lda0; a.wt0 = wt0; a.ldw0 = ldw0; a.nseg = 0; a.K0 = K0;
   a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1; a.C = C; a.ldc = ldc;
   a.keep = keep; a.ldk = ldk; a.keep_scale = keep_scale;
-  return launch_tiles<false>(a, s);
+  return launch_tiles<kWBf16>(a, s);
 }
 
 hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const uint16_t* const* act1,
@@ -780,7 +915,7 @@ hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const 
     a.seg[i] = Nf4Seg{nullptr, nullptr, nullptr, n0, rows[i], act1[i]};
     n0 += rows[i];
   }
-  return launch_tiles<false>(a, s);
+  return launch_tiles<kWBf16>(a, s);
 }
 
 bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows) {
@@ -814,7 +949,7 @@ hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint
       n0 += proj[i].rows;
     }
     a.C = C;
-    return launch_tiles<true>(a, s);
+    return launch_tiles<kWNf4>(a, s);
   }
   int64_t n0 = 0;
   for (int i = 0; i < nproj; ++i) {
@@ -824,11 +959,33 @@ hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint
     b.seg[0] = Nf4Seg{proj[i].codes, proj[i].absmax_q, proj[i].scale, 0, proj[i].rows, proj[i].act1};
     b.wt1 = wt1 + n0 * ldw1;
     b.C = C + n0;
-    const hipError_t e = launch_tiles<true>(b, s);
+    const hipError_t e = launch_tiles<kWNf4>(b, s);
     if (e != hipSuccess) return e;
     n0 += proj[i].rows;
   }
   return hipSuccess;
 }
+
+hipError_t launch_gemm_nf4t(int64_t M, int64_t N, int nproj, const Nf4Proj* proj, const uint16_t* act0,
+                            int64_t lda0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
+                            int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s,
+                            const uint8_t* keep, int64_t ldk, float keep_scale) {
+  if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.M = M; a.N = N; a.act0 = act0; a.lda0 = lda0; a.nseg = nproj;
+  int64_t k = 0;
+  for (int i = 0; i < nproj; ++i) {
+    if (proj[i].rows <= 0 || proj[i].rows % kBK != 0 || !nf4t_fits(proj[i].rows, N)) return hipErrorInvalidValue;
+    a.seg[i] = Nf4Seg{proj[i].codes, proj[i].absmax_q, proj[i].scale, k, proj[i].rows, act1};
+    k += proj[i].rows;
+  }
+  a.K0 = k;
+  a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1;
+  a.C = C; a.ldc = ldc;
+  a.keep = keep; a.ldk = ldk; a.keep_scale = keep_scale;
+  return launch_tiles<kWNf4T>(a, s);
+}
+
+bool nf4t_fits(int64_t rows, int64_t in) { return rows * (in / 2) <= 0x7fffffff; }
 
 }  // namespace qlora

@@ -142,7 +142,24 @@ int64_t token_pitch(int64_t T) { return round_up(T, 8); }
 // sU, sV [n][T][r] fp32.
 bool bwd_small(int64_t T, bool dropout) { return T <= kDxSmallMaxT && !dropout; }
 
-BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout) {
+// Above that the dX GEMM takes one of two routes (dX bit-identical either
+// way): with a workspace that holds W_hat^T (2 * in * sum(out) bytes) it
+// expands W_hat^T once and runs the bf16 GEMM, the faster route at every
+// measured size; with a smaller one (at least the layout without that region)
+// it reads the NF4 codes and dequantizes each weight tile, transposed, while
+// staging it into LDS, so the backward needs no memory proportional to the
+// weight.  The 4.5-bit format (read by the standalone transposed dequantize
+// only) and codes too large for 32-bit offsets always expand.
+bool bwd_can_fuse(int64_t in, const int64_t* outs, int n, bool absmax_fp32) {
+  if (absmax_fp32) return false;
+  for (int i = 0; i < n; ++i)
+    if (!nf4t_fits(outs[i], in)) return false;
+  return true;
+}
+
+// expand: the layout holds W_hat^T (the general path's expanded route)
+BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout,
+                     bool expand = true) {
   const int64_t rp = padded_rank(r), N = total_out(outs, n);
   const bool small = bwd_small(T, dropout);
   int64_t out_max = 0;
@@ -164,7 +181,7 @@ BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
     l.v_pad = c.take(static_cast<size_t>(T * n * rp * 4));                // [T][n 2rp] bf16
     l.b_t = c.take(static_cast<size_t>(r * out_max * 2));                 // one B^T at a time
     l.a_t_pad = c.take(static_cast<size_t>(in * n * rp * 4));             // [in][n 2rp] bf16
-    l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));                   // [in][N] bf16
+    if (expand) l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));       // [in][N] bf16
     l.part = c.take(part);
   }
   l.total = c.off;
@@ -293,6 +310,18 @@ size_t qlora_workspace_bytes_flags(int64_t T, int64_t in_features, const int64_t
   const bool fp32 = (flags & QLORA_NF4_ABSMAX_FP32) != 0;
   const size_t need = backward ? bwd_layout(T, in_features, out_features, n, r, dropout != 0).total
                                : fwd_layout(T, in_features, out_features, n, r, dropout != 0, fp32).total;
+  return need > kMinWorkspace ? need : kMinWorkspace;
+}
+
+size_t qlora_workspace_bytes_bwd_min(int64_t T, int64_t in_features, const int64_t* out_features, int n,
+                                     int64_t r, int dropout, uint32_t flags) {
+  if ((flags & ~QLORA_NF4_FLAGS_KNOWN) != 0) return 0;
+  if (n < 1 || n > kMaxProj || out_features == nullptr || (dropout && n != 1)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
+  if (!operands_fit(T, in_features, total_out(out_features, n))) return 0;
+  const bool fuse = bwd_can_fuse(in_features, out_features, n, (flags & QLORA_NF4_ABSMAX_FP32) != 0);
+  const size_t need = bwd_layout(T, in_features, out_features, n, r, dropout != 0, !fuse).total;
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
 
@@ -452,8 +481,13 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   if (!aligned16(X) || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_ALIGN;
   if (!std::isfinite(alpha)) return QLORA_ERR_VALUE;
   if (int st = check_dropout(keep, p)) return st;
-  const BwdLayout lay = bwd_layout(T, in, outs, n, r, keep != nullptr);
-  if (T > 0 && (ws == nullptr || ws_bytes < lay.total)) return QLORA_ERR_WORKSPACE;
+  // the expanded route when the workspace holds W_hat^T, else the fused dX
+  const BwdLayout full = bwd_layout(T, in, outs, n, r, keep != nullptr, true);
+  const bool can_fuse = bwd_can_fuse(in, outs, n, absmax_fp32(W[0]));
+  const BwdLayout least = bwd_layout(T, in, outs, n, r, keep != nullptr, !can_fuse);
+  if (T > 0 && (ws == nullptr || ws_bytes < least.total)) return QLORA_ERR_WORKSPACE;
+  const bool fused = can_fuse && ws_bytes < full.total;
+  const BwdLayout lay = fused ? least : full;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (int st = check_device()) return st;
 
@@ -516,8 +550,8 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   const float inv_keep = keep != nullptr ? 1.f / (1.f - p) : 1.f;
   e = launch_lora_down(X, in, T, in, A, n, r, scale * inv_keep, nullptr, 0, ut, tp, rp, part, s, keep,
                        in / 8);
-  // W_hat^T is expanded and a GEMM runs (small token counts without dropout
-  // took the streamed path above)
+  // the dX GEMM dequantizes W_hat^T tile by tile (fused) or reads it expanded
+  // (small token counts without dropout took the streamed path above)
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     // s V_i = s dY_i B_i with dY_i the projection's columns of dY
@@ -527,12 +561,17 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
       e = launch_lora_down(dY + off, N, T, outs[i], &bt, 1, r, scale, v_pad + i * 2 * rp, n * 2 * rp,
                            vt + i * 2 * rp * tp, tp, rp, part, s);
     if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !fused)
       e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
                                            w_dq_t + off, N, s, absmax_fp32(W[i]));
     off += outs[i];
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && fused) {
+    Nf4Proj proj[kMaxProj];
+    for (int i = 0; i < n; ++i) proj[i] = Nf4Proj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], nullptr};
+    e = launch_gemm_nf4t(T, in, n, proj, dY, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp, dX, in, s,
+                         keep, in / 8, inv_keep);
+  } else if (e == hipSuccess) {
     // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
     // (with dropout the adapter term is masked and scaled by 1 / (1 - p)
     // before the base is added)

@@ -170,7 +170,8 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  * The workspace is scratch for intermediate products (padded LoRA factors,
  * the transposed dequantized weight of the backward from T = 17 on or with
  * dropout, and, from T = 2048 on, the forward's dequantized weight: 2 * out
- * * in bytes each).  Up to T = 16 without dropout the backward keeps no
+ * * in bytes each; the backward also runs without that weight in the
+ * smaller workspace of qlora_workspace_bytes_bwd_min).  Up to T = 16 without dropout the backward keeps no
  * dequantized weight: it holds fp32 row-split partials of dX
  * (splits * T * in * 4 bytes, splits <= ceil(512 / (in / 64))) and the
  * rank-r reductions' partials (T * r * 4 bytes per 128 columns / rows).  It needs no
@@ -195,6 +196,21 @@ size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_feature
  */
 size_t qlora_workspace_bytes_flags(int64_t T, int64_t in_features, const int64_t* out_features, int n,
                                    int64_t r, int backward, int dropout, uint32_t flags);
+
+/*
+ * The smallest workspace a backward call accepts (single, multi or dropout
+ * form, for a weight of the given format; arguments as in
+ * qlora_workspace_bytes_flags with backward = 1): the layout without the
+ * expanded W_hat^T, whose dX GEMM dequantizes the weight tiles while it stages
+ * them (paperclase "QLoRA", Parte 4: the dequantized weight is built, used
+ * and discarded; ultralytics glossary "QLoRA", "Compromissos": the memory
+ * saved is paid for in time).  Equal to the full size where no such route
+ * exists (T <= 16 without dropout, where the backward never expands W_hat^T;
+ * the 4.5-bit format, which always expands it).  Returns 0 for invalid
+ * arguments.  Host only.
+ */
+size_t qlora_workspace_bytes_bwd_min(int64_t T, int64_t in_features, const int64_t* out_features, int n,
+                                     int64_t r, int dropout, uint32_t flags);
 
 /*
  * qlora_linear_fwd -- F1 + F2: Y = X W_hat^T + (alpha/r) (X A^T) B^T.
@@ -284,15 +300,23 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
  * paperclase "QLoRA", Parte 4: dL/dx = (W_hat + (alpha/r) B A)^T dL/dh; no
  * gradient for W_hat (the codes are not parameters); A and B are the only
  * trained tensors.  dA and dB are overwritten, not accumulated.  From
- * T = 17 on they are sums over token slices added with fp32 atomics, so two
- * identical calls can differ in their last bits (summation order), and the
- * backward expands W_hat^T into the workspace (2 * out * in bytes) for its
- * dX product.  Up to T = 16 it streams the codes once, W_hat existing only
- * in LDS tiles, sums fp32 row-split partials of dX in a fixed order (one
- * rounding) and writes each element of dA and dB once (reproducible).  Y
- * and dX are reproducible bit for bit.
+ * T = 17 on (or with dropout) they are sums over token slices added with fp32
+ * atomics, so two identical calls can differ in their last bits (summation
+ * order), and the dX product takes one of two routes, chosen by ws_bytes:
+ *   ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1): W_hat^T is expanded
+ *     into the workspace (2 * out * in bytes) and read by a bf16 GEMM (the
+ *     faster route);
+ *   qlora_workspace_bytes_bwd_min(...) <= ws_bytes < that: the GEMM reads
+ *     the codes and dequantizes each weight tile, transposed, while staging
+ *     it into on-chip memory, so W_hat^T is never stored and the workspace
+ *     holds only the rank-r products (megabytes).
+ * Both routes give the same dX bit for bit.  Up to T = 16 without dropout the
+ * backward streams the codes once, W_hat existing only in LDS tiles, sums
+ * fp32 row-split partials of dX in a fixed order (one rounding) and writes
+ * each element of dA and dB once (reproducible); both size functions give
+ * the same size there.  Y and dX are reproducible bit for bit.
  *   dY [T, out] bf16; other arguments as in qlora_linear_fwd;
- *   ws of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1)
+ *   ws of ws_bytes >= qlora_workspace_bytes_bwd_min(T, in, &out, 1, r, 0, flags)
  * T == 0 writes zeros to dA and dB and nothing else (X, dY, dX may be NULL).
  * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE, LAUNCH.
  */

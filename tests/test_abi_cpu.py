@@ -244,7 +244,8 @@ def test_small_token_backward_workspace():
     # up to 16 tokens without dropout the backward keeps no W_hat^T: its
     # workspace holds the row-split fp32 partials of dX (sized for 512
     # workgroups over the in / 64 column strips), far below 2 out in bytes;
-    # with dropout, or from 17 tokens on, W_hat^T is expanded as before
+    # with dropout, or from 17 tokens on, the full size holds the expanded
+    # W_hat^T (the faster dX route)
     lib = _api(_lib())
     i64, sz = ctypes.c_int64, ctypes.c_size_t
     lib.qlora_workspace_bytes_dropout.argtypes = [i64, i64, i64, i64, ctypes.c_int]
@@ -258,6 +259,46 @@ def test_small_token_backward_workspace():
         assert lib.qlora_workspace_bytes(17, n_in, n_out, 64, 1) > expanded
     # a weight with fewer 64-row chunks than splits: one split per chunk
     assert lib.qlora_workspace_bytes(16, 64, 128, 8, 1) >= 2 * 16 * 64 * 4
+
+
+def test_backward_minimum_workspace():
+    # qlora_workspace_bytes_bwd_min: the backward's layout without the expanded
+    # W_hat^T (its dX GEMM then dequantizes the weight tiles while staging them):
+    # no term in out * in from 17 tokens on or with dropout; the full size where
+    # no such route exists (T <= 16 without dropout, the 4.5-bit format)
+    lib = _api(_lib())
+    i64, sz, F = ctypes.c_int64, ctypes.c_size_t, _FAKE
+    lib.qlora_workspace_bytes_bwd_min.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64,
+                                                  ctypes.c_int, ctypes.c_uint32]
+    lib.qlora_workspace_bytes_bwd_min.restype = sz
+    lib.qlora_workspace_bytes_flags.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_uint32]
+    lib.qlora_workspace_bytes_flags.restype = sz
+    outs = lambda *o: (i64 * len(o))(*o)
+    mn = lambda T, n_in, o, r=64, drop=0, flags=0: lib.qlora_workspace_bytes_bwd_min(
+        T, n_in, outs(*o), len(o), r, drop, flags)
+    full = lambda T, n_in, o, r=64, drop=0, flags=0: lib.qlora_workspace_bytes_flags(
+        T, n_in, outs(*o), len(o), r, 1, drop, flags)
+    for n_in, o in ((4096, [14336]), (14336, [4096]), (8192, [28672]), (4096, [4096, 1024, 1024])):
+        weight = 2 * n_in * sum(o)
+        for T in (17, 300, 4096):
+            assert full(T, n_in, o) - mn(T, n_in, o) == weight, (n_in, o, T)
+            assert mn(T, n_in, o) < (weight // 4 if len(o) == 1 else weight)
+            assert mn(T, n_in, o, flags=1) == full(T, n_in, o, flags=1)     # 4.5-bit: always expanded
+        if len(o) == 1:
+            assert full(64, n_in, o, drop=1) - mn(64, n_in, o, drop=1) == weight
+        for T in (1, 16):
+            assert mn(T, n_in, o) == full(T, n_in, o)                       # streamed, no W_hat^T
+    # invalid arguments
+    assert mn(17, 100, [128]) == 0 and mn(17, 256, [128], r=0) == 0
+    assert mn(17, 256, [128], flags=2) == 0 and mn(17, 256, [128, 64], drop=1) == 0
+    # the call accepts the minimum and refuses one byte less (before any HIP call)
+    W = _W(F, F, F, 128, 256)
+    least = mn(300, 256, [128], r=8)
+    bwd = lambda wsb: lib.qlora_linear_bwd(ctypes.byref(W), F, F, 300, F, F, 8, 16.0, F, F, F, F, wsb, None)
+    assert bwd(least - 1) == -4
+    assert bwd(least) == -6       # valid: fails only at the device check
+    assert bwd(full(300, 256, [128], r=8)) == -6
 
 
 def test_format_flags():
@@ -451,7 +492,15 @@ def test_dropout_validation():
                                                    k.get("wsb", wsb), None)
     assert bwd(keep=None) == -1
     assert bwd(p=1.5) == -7
-    assert bwd(wsb=wsb - 1) == -4
+    # the backward also runs in the smaller workspace without W_hat^T
+    i64, sz = ctypes.c_int64, ctypes.c_size_t
+    lib.qlora_workspace_bytes_bwd_min.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64,
+                                                  ctypes.c_int, ctypes.c_uint32]
+    lib.qlora_workspace_bytes_bwd_min.restype = sz
+    least = lib.qlora_workspace_bytes_bwd_min(32, 256, (i64 * 1)(128), 1, 8, 1, 0)
+    assert least == wsb - 256 * 128 * 2
+    assert bwd(wsb=least - 1) == -4
+    assert bwd(wsb=least) == -6 and bwd(wsb=wsb - 1) == -6   # valid: fail only at the device check
 
 
 def test_valid_call_without_gpu_reports_device_error():

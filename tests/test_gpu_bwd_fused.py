@@ -1,0 +1,154 @@
+"""GPU parity of the backward's fused dX route: given a workspace of
+qlora_workspace_bytes_bwd_min (no room for the expanded W_hat^T), the dX GEMM
+reads the NF4 codes and dequantizes each weight tile, transposed, while it
+stages it into LDS (paperclase "QLoRA", Parte 4: dX = (W_hat + s B A)^T dY,
+with W_hat built, used and discarded).
+
+Checks:
+- against the fp64 oracle (relative Frobenius <= 2e-3 for dX, dA, dB) at
+  small ragged shapes, full tensors;
+- against the expanded route on the same inputs: dX bit for bit (both routes
+  feed the same bf16 W_hat values to the same MFMA sequence), dA and dB up to
+  the atomics' summation order, at shapes that run every kernel form (the
+  128 x 128 kernel with a partial column tile, the 256-column kernel with 128-
+  and 256-row tiles), several projections, and dropout;
+- one-hot dY rows select rows of W_hat bit for bit through the fused route."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dense as odense
+from oracle import native as onative
+from oracle import nf4 as onf4
+
+from gpu_util import TOL, banner, dev_bf16, dev_f32, host, host_bits, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, T, n_in, outs, r):
+    ws = [synth.normal_f32(seed + 10 * i, (o, n_in), synth.W_STD) for i, o in enumerate(outs)]
+    As = [synth.bf16_bits(synth.normal_f32(seed + 10 * i + 2, (r, n_in), 1.0 / n_in)) for i in range(len(outs))]
+    Bs = [synth.bf16_bits(synth.normal_f32(seed + 10 * i + 3, (o, r), 0.05)) for i, o in enumerate(outs)]
+    X = synth.bf16_bits(synth.normal_f32(seed + 1, (T, n_in), 1.0))
+    dY = synth.bf16_bits(synth.normal_f32(seed + 4, (T, sum(outs)), 1.0))
+    return ws, As, Bs, X, dY
+
+
+def _w_hat(w):
+    packed, aq, sc = onf4.quantize(w, nearest=onative.nearest_level)
+    return onf4.dequantize(packed, aq, sc).reshape(w.shape)
+
+
+def _min_ws(q, T, n_in, outs, r, dropout=False):
+    need = q.qlora_workspace_bytes_bwd_min(T, n_in, outs, r, dropout)
+    full = q.qlora_workspace_bytes_flags(T, n_in, outs, r, True, dropout)
+    assert 0 < need < full, (need, full)
+    return q.make_workspace(need, "cuda")
+
+
+def _both(q, T, n_in, outs, r, alpha, seed):
+    """dX, dA, dB of the multi call through the fused route and the expanded one."""
+    ws, As, Bs, X, dY = _inputs(seed, T, n_in, outs, r)
+    Ws = [q.nf4_quantize_weight(dev_f32(w)) for w in ws]
+    Xd, dYd = dev_bf16(X), dev_bf16(dY)
+    Ad, Bd = [dev_bf16(a) for a in As], [dev_bf16(b) for b in Bs]
+    fused = q.qlora_linear_bwd_multi(Ws, Xd, dYd, Ad, Bd, r, alpha, ws=_min_ws(q, T, n_in, outs, r))
+    fused = (host_bits(fused[0]), [host(a) for a in fused[1]], [host(b) for b in fused[2]])
+    full = q.qlora_linear_bwd_multi(Ws, Xd, dYd, Ad, Bd, r, alpha)
+    full = (host_bits(full[0]), [host(a) for a in full[1]], [host(b) for b in full[2]])
+    return (ws, As, Bs, X, dY), fused, full
+
+
+def _same_route_result(fused, full):
+    assert np.array_equal(fused[0], full[0]), "dX differs between the fused and the expanded route"
+    for a, b in zip(fused[1] + fused[2], full[1] + full[2]):
+        # the gradient kernels are the same; only their atomics' order may differ
+        assert odense.rel_frobenius(a.astype(np.float64), b.astype(np.float64)) <= 1e-5
+
+
+@pytest.mark.parametrize("T,n_in,outs,r,alpha", [
+    (37, 192, [320], 12, 24.0),       # ragged T, 128 x 128 kernel, 192 columns: half a tile past `in`
+    (200, 512, [128], 64, 16.0),      # ragged tail of a 128-row tile, r = 64
+    (300, 320, [512, 256], 16, 32.0), # two projections: a K-step switches weight mid-call
+])
+def test_fused_route_matches_oracle(T, n_in, outs, r, alpha):
+    q = require_gpu()
+    banner(f"fused dX vs oracle T={T} in={n_in} outs={outs} r={r}")
+    (ws, As, Bs, X, dY), fused, full = _both(q, T, n_in, outs, r, alpha, 1300 + T)
+    _same_route_result(fused, full)
+    w_hats = [_w_hat(w) for w in ws]
+    rdX = np.zeros((T, n_in))
+    col = 0
+    for i, (w_hat, o) in enumerate(zip(w_hats, outs)):
+        g = np.ascontiguousarray(dY[:, col:col + o])
+        dXi, rdA, rdB = odense.linear_bwd(w_hat, X, g, As[i], Bs[i], alpha, r)
+        rdX += dXi
+        assert odense.rel_frobenius(fused[1][i].astype(np.float64), rdA) <= TOL
+        assert odense.rel_frobenius(fused[2][i].astype(np.float64), rdB) <= TOL
+        col += o
+    err = odense.rel_frobenius(onf4.bf16_bits_to_f32(fused[0]).astype(np.float64), rdX)
+    print(f"  dX rel_frob={err:.3e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("T,n_in,outs,r,alpha", [
+    (4096, 4096, [14336], 64, 128.0),          # 8B MLP gate: 256 x 256 tiles, K = 14336
+    (1024, 8192, [1024], 16, 32.0),            # 128 x 256 tiles (8 x 32 of them)
+    (4096, 4096, [4096, 1024, 1024], 16, 32.0),  # 8B q|k|v: 256 x 256 tiles over three projections
+    (8192, 4096, [1024], 16, 32.0),            # 8B attention k: 32 x 16 tiles, K = 1024
+])
+def test_fused_route_equals_expanded_route(T, n_in, outs, r, alpha):
+    q = require_gpu()
+    banner(f"fused dX vs expanded T={T} in={n_in} outs={outs} r={r}")
+    _, fused, full = _both(q, T, n_in, outs, r, alpha, 1400 + T % 97)
+    _same_route_result(fused, full)
+
+
+@pytest.mark.parametrize("T,n_in,n_out,r,p", [(600, 1024, 512, 16, 0.1), (4096, 4096, 4096, 16, 0.05)])
+def test_fused_route_with_dropout(T, n_in, n_out, r, p):
+    q = require_gpu()
+    banner(f"fused dX with dropout T={T} in={n_in} out={n_out} p={p}")
+    (w,), (A,), (B,), X, dY = _inputs(1500 + T % 89, T, n_in, [n_out], r)
+    rng = np.random.Generator(np.random.PCG64(1501))
+    keep = np.packbits(rng.random((T, n_in)) >= p, axis=1, bitorder="little")
+    W = q.nf4_quantize_weight(dev_f32(w))
+    Xd, dYd, Ad, Bd = dev_bf16(X), dev_bf16(dY), dev_bf16(A), dev_bf16(B)
+    K = torch.from_numpy(np.ascontiguousarray(keep)).cuda()
+    f = q.qlora_linear_bwd_dropout(W, Xd, dYd, K, p, Ad, Bd, r, 2.0 * r,
+                                   ws=_min_ws(q, T, n_in, [n_out], r, dropout=True))
+    f = (host_bits(f[0]), [host(f[1])], [host(f[2])])
+    e = q.qlora_linear_bwd_dropout(W, Xd, dYd, K, p, Ad, Bd, r, 2.0 * r)
+    e = (host_bits(e[0]), [host(e[1])], [host(e[2])])
+    _same_route_result(f, e)
+
+
+def _one_hot(n, idx):
+    m = np.zeros((len(idx), n), dtype=np.uint16)
+    m[np.arange(len(idx)), idx] = 0x3F80  # bf16 1.0
+    return m
+
+
+@pytest.mark.parametrize("T,n_out,n_in", [
+    (70, 192, 320),      # 128 x 128 kernel, partial column tile
+    (2048, 512, 8192),   # 256 x 256 tiles (8 x 32)
+    (1024, 512, 8192),   # 128 x 256 tiles (8 x 32)
+])
+def test_fused_route_one_hot_rows_bit_exact(T, n_out, n_in):
+    # dY rows one-hot and A = 0: dX[t, :] = W_hat[n_t, :] exactly
+    q = require_gpu()
+    banner(f"fused dX one-hot T={T} out={n_out} in={n_in}")
+    r = 16
+    w = synth.normal_f32(78_000 + n_out + n_in, (n_out, n_in), synth.W_STD)
+    rng = np.random.default_rng(T + n_in)
+    gi = rng.integers(0, n_out, T)
+    X = synth.bf16_bits(synth.normal_f32(7, (T, n_in), 1.0))
+    B = synth.bf16_bits(synth.normal_f32(6, (n_out, r), synth.B_STD))
+    W = q.nf4_quantize_weight(dev_f32(w))
+    dX, dA, dB = q.qlora_linear_bwd(W, dev_bf16(X), dev_bf16(_one_hot(n_out, gi)),
+                                    dev_bf16(np.zeros((r, n_in), np.uint16)), dev_bf16(B), r, 32.0,
+                                    ws=_min_ws(q, T, n_in, [n_out], r))
+    assert np.array_equal(host_bits(dX), _w_hat(w)[gi, :])
+    assert np.all(host(dB) == 0)  # U = X A^T = 0

@@ -120,6 +120,8 @@ def _one_hot(n, idx):
     (2048, 512, 320),    # weight expanded once into the workspace, 128 x 128 tiles
     (2048, 8192, 512),   # the same on 256 x 256 tiles (8 x 32 = 256 tiles)
     (1792, 8192, 512),   # the fused NF4 GEMM on 256 x 256 tiles (7 x 32 tiles)
+    (2048, 512, 8192),   # the expanded-weight dX GEMM on 256 x 256 tiles (8 x 32)
+    (1024, 512, 8192),   # the same on 128 x 256 tiles (8 x 32)
 ])
 def test_one_hot_large_token_paths_bit_exact(T, n_out, n_in):
     # X rows one-hot and B = 0: Y[t, :] = W_hat[:, i_t] exactly (one non-zero
