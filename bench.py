@@ -331,6 +331,16 @@ def main():
         for wid, key in ((3, "mlp8b_fwd_bwd"), (4, "attn8b_fwd_bwd"), (5, "mlp70b_fwd_bwd")):
             extra[key] = large_step_leg(q, synth, dev, bf, wid, steps=10 if wid < 5 else 5)
         extra["mlp8b_variants"] = train_leg(q, synth, dev, bf, extra["mlp8b_fwd_bwd"])
+        # the projections that share X as one multi-projection call (q|k|v, gate|up)
+        extra["attn8b_qkv_fused"] = grouped_step_leg(q, synth, dev, bf, 4, [[0, 1, 2], [3]], 10,
+                                                     extra["attn8b_fwd_bwd"]["step_flop"])
+        extra["mlp70b_gate_up_fused"] = grouped_step_leg(q, synth, dev, bf, 5, [[0, 1], [2]], 5,
+                                                         extra["mlp70b_fwd_bwd"]["step_flop"])
+        # the backward in its smallest workspace: dX without the expanded W_hat^T
+        extra["mlp8b_bwd_min_workspace"] = grouped_step_leg(q, synth, dev, bf, 3, [[0], [1], [2]], 10,
+                                                            extra["mlp8b_fwd_bwd"]["step_flop"], bwd_min=True)
+        extra["mlp70b_bwd_min_workspace"] = grouped_step_leg(q, synth, dev, bf, 5, [[0], [1], [2]], 5,
+                                                             extra["mlp70b_fwd_bwd"]["step_flop"], bwd_min=True)
         extra["gpu_sclk_mhz"] = sampler.stop()
         if not args.no_cpu_baseline:
             for wid, key in ((3, "mlp8b_fwd_bwd"), (4, "attn8b_fwd_bwd"), (5, "mlp70b_fwd_bwd")):
@@ -1031,6 +1041,79 @@ def large_step_leg(q, synth, dev, bf, wid, steps):
     tf = tot_flop / (step_ms * 1e-3) / 1e12
     res.update({"step_flop": tot_flop, "step_ms": round(step_ms, 3), "sum_of_calls_ms": round(tot_ms, 3),
                 "fwd_bwd_TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+    del items, wsf, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
+def grouped_step_leg(q, synth, dev, bf, wid, groups, steps, step_flop, bwd_min=False):
+    """The fwd + bwd step of workload `wid` with the projections that share
+    their input X as one multi-projection call each way (`groups`: lists of
+    projection indices, e.g. q|k|v then o): one LoRA down-projection pass over
+    X, one GEMM launch over the group's stacked weights, one dX GEMM over
+    their concatenated outputs.  bwd_min: the backward gets the smallest
+    workspace it accepts, so its dX GEMM dequantizes the weight tiles while
+    staging them instead of expanding W_hat^T.  2 untimed steps, then `steps`
+    timed steps with events around every call."""
+    import torch
+    wl = synth.WORKLOADS[wid]
+    T, r, alpha = wl.tokens[0], wl.r, wl.alpha
+    items = []
+    ws_f = ws_b = 0
+    for g in groups:
+        projs = [wl.projections[i] for i in g]
+        n_in = projs[0].in_features
+        outs = [p.out_features for p in projs]
+        Ws, As, Bs = [], [], []
+        for i, p in zip(g, projs):
+            w = torch.from_numpy(synth.weight(wid, i, p.out_features, n_in)).to(dev)
+            Ws.append(q.nf4_quantize_weight(w))
+            del w
+            As.append(bf(synth.lora_A(wid, i, r, n_in)))
+            Bs.append(bf(synth.lora_B(wid, i, p.out_features, r)))
+        N = sum(outs)
+        items.append({"name": "|".join(p.name for p in projs), "Ws": Ws, "As": As, "Bs": Bs,
+                      "X": bf(synth.activations(wid, g[0], T, n_in)),
+                      "dY": bf(synth.activations(wid, g[0], T, N, "dY")),
+                      "Y": torch.empty(T, N, dtype=torch.bfloat16, device=dev),
+                      "dX": torch.empty(T, n_in, dtype=torch.bfloat16, device=dev),
+                      "dAs": [torch.empty(r, n_in, dtype=torch.float32, device=dev) for _ in g],
+                      "dBs": [torch.empty(o, r, dtype=torch.float32, device=dev) for o in outs]})
+        ws_f = max(ws_f, q.qlora_workspace_bytes_multi(T, n_in, outs, r, False))
+        need_b = (q.qlora_workspace_bytes_bwd_min(T, n_in, outs, r) if bwd_min
+                  else q.qlora_workspace_bytes_multi(T, n_in, outs, r, True))
+        ws_b = max(ws_b, need_b)
+    wsf, wsb = q.make_workspace(ws_f, dev), q.make_workspace(ws_b, dev)
+
+    def run(evs=None):
+        for j, it in enumerate(items):
+            if evs is not None:
+                evs[j][0].record()
+            q.qlora_linear_fwd_multi(it["Ws"], it["X"], it["As"], it["Bs"], r, alpha, Y=it["Y"], ws=wsf)
+            if evs is not None:
+                evs[j][1].record()
+            q.qlora_linear_bwd_multi(it["Ws"], it["X"], it["dY"], it["As"], it["Bs"], r, alpha, dX=it["dX"],
+                                     dAs=it["dAs"], dBs=it["dBs"], ws=wsb)
+            if evs is not None:
+                evs[j][2].record()
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    all_evs = [[(mk(), mk(), mk()) for _ in items] for _ in range(steps)]
+    for k in range(steps):
+        run(all_evs[k])
+    torch.cuda.synchronize()
+    res = {"T": T, "r": r, "steps": steps, "bwd_workspace_bytes": int(ws_b)}
+    for j, it in enumerate(items):
+        f_ms = sum(all_evs[k][j][0].elapsed_time(all_evs[k][j][1]) for k in range(steps)) / steps
+        b_ms = sum(all_evs[k][j][1].elapsed_time(all_evs[k][j][2]) for k in range(steps)) / steps
+        res[it["name"]] = {"fwd_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3)}
+    step_ms = all_evs[0][0][0].elapsed_time(all_evs[-1][-1][2]) / steps
+    tf = step_flop / (step_ms * 1e-3) / 1e12
+    res.update({"step_ms": round(step_ms, 3), "fwd_bwd_TFLOPs": round(tf, 1),
+                "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
     del items, wsf, wsb
     torch.cuda.empty_cache()
     return res

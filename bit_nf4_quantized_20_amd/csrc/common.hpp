@@ -98,6 +98,15 @@ hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
 constexpr int kMaxFill = 2 * kMaxProj;
 hipError_t launch_fill_many_f32(float* const* dst, const int64_t* n, int count, float v, hipStream_t s);
 
+// Split-K of the GEMM launches below: grids of 128 x 128 tiles below one
+// workgroup per CU split K into gemm_splits(M, N, K0) ranges (1: none), each
+// written as fp32 partials into `part` (gemm_split_bytes(M, N, K0) bytes, part
+// of the caller's workspace), then added in order and rounded once; with no
+// or too small a `part` the launch does not split.  The split count depends
+// on the shape only.
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
+
 // C[M][N] (bf16, ldc) = sum over the two K segments of act_i[m][k] * wt_i[n][k]
 // (bf16, K-contiguous, leading dims lda_i / ldw_i).  K0, K1 multiples of 64
 // (K1 may be 0).  N % 64 == 0.
@@ -109,7 +118,7 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
                           int64_t ldc, hipStream_t s, const uint8_t* keep = nullptr, int64_t ldk = 0,
-                          float keep_scale = 1.f);
+                          float keep_scale = 1.f, float* part = nullptr, size_t part_bytes = 0);
 
 // Same, with the main segment's weight given as NF4 projections stacked
 // along N (nproj <= kMaxProj; projection i owns output columns
@@ -129,10 +138,12 @@ bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows);
 hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const uint16_t* const* act1,
                                const uint16_t* act0, int64_t lda0, const uint16_t* wt0, int64_t ldw0,
                                int64_t K0, int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1,
-                               uint16_t* C, int64_t ldc, hipStream_t s);
+                               uint16_t* C, int64_t ldc, hipStream_t s, float* part = nullptr,
+                               size_t part_bytes = 0);
 hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,
                            int64_t lda0, int64_t K0, int64_t lda1, const uint16_t* wt1,
-                           int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s);
+                           int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s,
+                           float* part = nullptr, size_t part_bytes = 0);
 // dX-shaped product with NF4 weights read transposed: C[M][N] = sum_i
 // act0[m][k_i + k] W_hat_i[k][n] + (LoRA segment, as in launch_gemm_nt), where
 // projection i (proj[i].rows rows of N = in columns, rows % 64 == 0) owns the
@@ -145,7 +156,8 @@ bool nf4t_fits(int64_t rows, int64_t in);
 hipError_t launch_gemm_nf4t(int64_t M, int64_t N, int nproj, const Nf4Proj* proj, const uint16_t* act0,
                             int64_t lda0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
                             int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s,
-                            const uint8_t* keep = nullptr, int64_t ldk = 0, float keep_scale = 1.f);
+                            const uint8_t* keep = nullptr, int64_t ldk = 0, float keep_scale = 1.f,
+                            float* part = nullptr, size_t part_bytes = 0);
 
 // W_merged[m][n] = bf16(W_hat[m][n] + s * sum_j Bp[m][j] Atp[n][j]) for the
 // NF4 weight [out][in] (out % 64 == 0, in % 64 == 0); Bp [out][ldp] and Atp

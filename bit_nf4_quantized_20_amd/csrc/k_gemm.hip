@@ -270,6 +270,11 @@ struct GemmArgs {
   // main segment adds to the same accumulator (bit n % 8 of byte
   // keep[m * ldk + n / 8])
   const uint8_t* keep; int64_t ldk; float keep_scale;
+  // split-K (k_gemm only; part == nullptr: none): workgroup z = blockIdx.z of
+  // gridDim.z takes main-segment K-steps [z ks, min((z + 1) ks, K0 / 64)),
+  // split 0 also the LoRA segment, and writes fp32 partials
+  // part[z][m][n] (row stride N) instead of C
+  float* part; int64_t ks;
 };
 
 // acc[a][c][e] holds C[m][n] with m = m_base + 32 c + r32 and
@@ -480,7 +485,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
     }
   };
 
-  const int64_t s0 = p.K0 / kBK, s1 = p.K1 / kBK;
+  const bool split = p.part != nullptr;
+  const int z = split ? static_cast<int>(blockIdx.z) : 0;
+  int64_t kb = 0, s0 = p.K0 / kBK;  // this workgroup's main-segment K-steps [kb, kb + s0)
+  if (split) {
+    kb = z * p.ks;
+    const int64_t end = kb + p.ks < s0 ? kb + p.ks : s0;
+    s0 = end > kb ? end - kb : 0;
+  }
+  const int64_t s1 = z == 0 ? p.K1 / kBK : 0;
   using TA = Bf16Tile<BM, NT>;
   using TW = Bf16Tile<BN, NT>;
   // main segment over global steps [first, first + s0)
@@ -495,8 +508,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
       R r0, r1;
       segment(r0, r1, first, first + s0,
               [&](R& r, int64_t e) {
-                ta.load(r.a, e * kBK);
-                tq.load(r.w, e * kBK);
+                ta.load(r.a, (kb + e) * kBK);
+                tq.load(r.w, (kb + e) * kBK);
               },
               [&](const R& r, int b) {
                 TA::store(r.a, s_act[b], tid);
@@ -513,8 +526,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
       R r0, r1;
       segment(r0, r1, first, first + s0,
               [&](R& r, int64_t e) {
-                ta.load(r.a, e * kBK);
-                tq.load(r.w, e * kBK);
+                ta.load(r.a, (kb + e) * kBK);
+                tq.load(r.w, (kb + e) * kBK);
               },
               [&](const R& r, int b) {
                 TA::store(r.a, s_act[b], tid);
@@ -529,8 +542,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
       R r0, r1;
       segment(r0, r1, first, first + s0,
               [&](R& r, int64_t e) {
-                ta.load(r.a, e * kBK);
-                tw.load(r.w, e * kBK);
+                ta.load(r.a, (kb + e) * kBK);
+                tw.load(r.w, (kb + e) * kBK);
               },
               [&](const R& r, int b) {
                 TA::store(r.a, s_act[b], tid);
@@ -567,7 +580,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
     lora_seg(s0);
   }
 
-  // epilogue: D[n][m] -> C[m][n]; lane holds m = r32, n = 8*(e/4) + 4*half + e%4
+  // epilogue: D[n][m] -> C[m][n] (or the split's fp32 partial); lane holds
+  // m = r32, n = 8*(e/4) + 4*half + e%4
 #pragma unroll
   for (int c = 0; c < FM; ++c) {
     const int64_t m = m0 + wm * WM + c * 32 + r32;
@@ -578,13 +592,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
       for (int g = 0; g < 4; ++g) {
         const int64_t n = n0 + wn * WN + a * 32 + 8 * g + 4 * half;
         if (n < p.N) {
-          const uint32_t p0 = pack_bf16x2(acc[a][c][4 * g + 0], acc[a][c][4 * g + 1]);
-          const uint32_t p1 = pack_bf16x2(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(p.C + m * p.ldc + n) = u32x2{p0, p1};
+          if (split) {
+            *reinterpret_cast<f32x4*>(p.part + (static_cast<int64_t>(z) * p.M + m) * p.N + n) =
+                f32x4{acc[a][c][4 * g + 0], acc[a][c][4 * g + 1], acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]};
+          } else {
+            const uint32_t p0 = pack_bf16x2(acc[a][c][4 * g + 0], acc[a][c][4 * g + 1]);
+            const uint32_t p1 = pack_bf16x2(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
+            *reinterpret_cast<u32x2*>(p.C + m * p.ldc + n) = u32x2{p0, p1};
+          }
         }
       }
     }
   }
+}
+
+// C[m][n] = bf16(sum over z = 0, 1, ... of part[z][m][n]), the splits added
+// in order (bit-reproducible), one rounding.  Thread: 8 consecutive columns
+// of one row; N % 8 == 0.
+__global__ __launch_bounds__(256) void k_split_sum(const float* part, int S, int64_t M, int64_t N,
+                                                   int64_t ldp, uint16_t* C, int64_t ldc) {
+  const int64_t groups = N / 8;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= M * groups) return;
+  const int64_t m = id / groups, n = (id % groups) * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int z = 0; z < S; ++z) {
+    const float* src = part + (static_cast<int64_t>(z) * M + m) * ldp + n;
+    const f32x4 u = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += u[e];
+      acc[4 + e] += v[e];
+    }
+  }
+  *reinterpret_cast<u32x4*>(C + m * ldc + n) =
+      u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+            pack_bf16x2(acc[6], acc[7])};
 }
 
 // BM x 256 tiles (BM = 256 or 128), 8 waves (see the file comment).
@@ -850,6 +896,29 @@ template __global__ void k_gemm_big<kWBf16, 128>(GemmArgs);
 template __global__ void k_gemm_big<kWNf4, 128>(GemmArgs);
 template __global__ void k_gemm_big<kWNf4T, 128>(GemmArgs);
 
+// Split-K of the 128 x 128 kernel: up to 1024 rows, a grid below one
+// workgroup per CU (of a 256-CU part; the count depends on the shape only, so
+// workspace sizes do not depend on the device) splits K into up to 8 ranges
+// of at least 8 K-steps, one workgroup each, with at most 32 MiB of fp32
+// partials.  1: no split.
+int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kTarget = 256, kMaxSplits = 8, kMinSteps = 8, kMaxRows = 1024;
+  constexpr int64_t kMaxPartBytes = int64_t(32) << 20;
+  if (M <= 0 || N <= 0 || M > kMaxRows) return 1;
+  if (ceil_div(M, 128) * ceil_div(N, 256) >= kTarget) return 1;  // a 256-column kernel
+  const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+  int64_t S = kTarget / tiles;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S > K / kBK / kMinSteps) S = K / kBK / kMinSteps;
+  if (S > kMaxPartBytes / (M * N * 4)) S = kMaxPartBytes / (M * N * 4);
+  return S > 1 ? static_cast<int>(S) : 1;
+}
+
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = gemm_splits(M, N, K);
+  return S > 1 ? static_cast<size_t>(S) * M * N * 4 : 0;
+}
+
 namespace {
 // Tile shape of a launch.  The 8-wave kernel takes 256-column tiles of
 // 256 rows when they fill at least one wave of CUs (one tile per CU at a
@@ -869,8 +938,24 @@ TileChoice choose_tiles(int64_t M, int64_t N) {
 }
 
 template <int kW>
-hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
-  const TileChoice tc = choose_tiles(a.M, a.N);
+hipError_t launch_tiles(const GemmArgs& a0, hipStream_t s, float* part = nullptr, size_t part_bytes = 0) {
+  const TileChoice tc = choose_tiles(a0.M, a0.N);
+  GemmArgs a = a0;
+  const int S = gemm_splits(a.M, a.N, a.K0);
+  if (tc.bn == 128 && S > 1 && part != nullptr && part_bytes >= gemm_split_bytes(a.M, a.N, a.K0)) {
+    // split-K: S partial products, then their ordered sum
+    a.part = part;
+    a.ks = ceil_div(a.K0 / kBK, S);
+    const int Sr = static_cast<int>(ceil_div(a.K0 / kBK, a.ks));  // splits that hold K-steps
+    dim3 grid(static_cast<uint32_t>(ceil_div(a.M, 128)), static_cast<uint32_t>(ceil_div(a.N, 128)),
+              static_cast<uint32_t>(Sr));
+    hipLaunchKernelGGL((k_gemm<128, 128, 2, 2, kW>), grid, dim3(256), 0, s, a);
+    const int64_t threads = a.M * (a.N / 8);
+    hipLaunchKernelGGL(k_split_sum, dim3(static_cast<uint32_t>(ceil_div(threads, 256))), dim3(256), 0, s,
+                       static_cast<const float*>(part), Sr, a.M, a.N, a.N, a.C, a.ldc);
+    return hipGetLastError();
+  }
+  a.part = nullptr;
   if (tc.bn == 256) {
     dim3 grid(static_cast<uint32_t>(ceil_div(a.M, tc.bm)), static_cast<uint32_t>(ceil_div(a.N, 256)));
     if (tc.bm == 256) hipLaunchKernelGGL((k_gemm_big<kW, 256>), grid, dim3(512), 0, s, a);
@@ -887,18 +972,18 @@ hipError_t launch_gemm_nt(int64_t M, int64_t N, const uint16_t* act0, int64_t ld
                           const uint16_t* wt0, int64_t ldw0, int64_t K0, const uint16_t* act1,
                           int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1, uint16_t* C,
                           int64_t ldc, hipStream_t s, const uint8_t* keep, int64_t ldk,
-                          float keep_scale) {
+                          float keep_scale, float* part, size_t part_bytes) {
   GemmArgs a{};
   a.M = M; a.N = N; a.act0 = act0; a.lda0 = lda0; a.wt0 = wt0; a.ldw0 = ldw0; a.nseg = 0; a.K0 = K0;
   a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1; a.C = C; a.ldc = ldc;
   a.keep = keep; a.ldk = ldk; a.keep_scale = keep_scale;
-  return launch_tiles<kWBf16>(a, s);
+  return launch_tiles<kWBf16>(a, s, part, part_bytes);
 }
 
 hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const uint16_t* const* act1,
                                const uint16_t* act0, int64_t lda0, const uint16_t* wt0, int64_t ldw0,
                                int64_t K0, int64_t lda1, const uint16_t* wt1, int64_t ldw1, int64_t K1,
-                               uint16_t* C, int64_t ldc, hipStream_t s) {
+                               uint16_t* C, int64_t ldc, hipStream_t s, float* part, size_t part_bytes) {
   if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   GemmArgs a{};
   a.M = M; a.act0 = act0; a.lda0 = lda0; a.wt0 = wt0; a.ldw0 = ldw0; a.K0 = K0;
@@ -915,7 +1000,7 @@ hipError_t launch_gemm_nt_proj(int64_t M, int nproj, const int64_t* rows, const 
     a.seg[i] = Nf4Seg{nullptr, nullptr, nullptr, n0, rows[i], act1[i]};
     n0 += rows[i];
   }
-  return launch_tiles<kWBf16>(a, s);
+  return launch_tiles<kWBf16>(a, s, part, part_bytes);
 }
 
 bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows) {
@@ -929,7 +1014,8 @@ bool gemm_proj_aligned(int64_t M, int nproj, const int64_t* rows) {
 
 hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint16_t* act0,
                            int64_t lda0, int64_t K0, int64_t lda1, const uint16_t* wt1,
-                           int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s) {
+                           int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s,
+                           float* part, size_t part_bytes) {
   if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   GemmArgs a{};
   a.M = M; a.act0 = act0; a.lda0 = lda0; a.K0 = K0; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1;
@@ -949,7 +1035,7 @@ hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint
       n0 += proj[i].rows;
     }
     a.C = C;
-    return launch_tiles<kWNf4>(a, s);
+    return launch_tiles<kWNf4>(a, s, part, part_bytes);
   }
   int64_t n0 = 0;
   for (int i = 0; i < nproj; ++i) {
@@ -969,7 +1055,8 @@ hipError_t launch_gemm_nf4(int64_t M, int nproj, const Nf4Proj* proj, const uint
 hipError_t launch_gemm_nf4t(int64_t M, int64_t N, int nproj, const Nf4Proj* proj, const uint16_t* act0,
                             int64_t lda0, const uint16_t* act1, int64_t lda1, const uint16_t* wt1,
                             int64_t ldw1, int64_t K1, uint16_t* C, int64_t ldc, hipStream_t s,
-                            const uint8_t* keep, int64_t ldk, float keep_scale) {
+                            const uint8_t* keep, int64_t ldk, float keep_scale, float* part,
+                            size_t part_bytes) {
   if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   GemmArgs a{};
   a.M = M; a.N = N; a.act0 = act0; a.lda0 = lda0; a.nseg = nproj;
@@ -983,7 +1070,7 @@ hipError_t launch_gemm_nf4t(int64_t M, int64_t N, int nproj, const Nf4Proj* proj
   a.act1 = act1; a.lda1 = lda1; a.wt1 = wt1; a.ldw1 = ldw1; a.K1 = K1;
   a.C = C; a.ldc = ldc;
   a.keep = keep; a.ldk = ldk; a.keep_scale = keep_scale;
-  return launch_tiles<kWNf4T>(a, s);
+  return launch_tiles<kWNf4T>(a, s, part, part_bytes);
 }
 
 bool nf4t_fits(int64_t rows, int64_t in) { return rows * (in / 2) <= 0x7fffffff; }

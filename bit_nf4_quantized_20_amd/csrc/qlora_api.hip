@@ -79,7 +79,7 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t u_pad, b_pad, part, w_dq, total;
+  size_t u_pad, b_pad, part, w_dq, split, total;
 };
 
 // From this many tokens on, the forward dequantizes each weight once into the
@@ -88,7 +88,7 @@ struct FwdLayout {
 // costs more than one extra pass of 2.5 bytes per weight.
 constexpr int64_t kMaterializeTokens = 2048;
 struct BwdLayout {
-  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, uvp, suv, total;
+  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, uvp, suv, split, total;
 };
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
@@ -115,9 +115,20 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 // whose fp32 block absmax only the standalone dequantize reads)
 bool fwd_expands(int64_t T, bool absmax_fp32) { return absmax_fp32 || T >= kMaterializeTokens; }
 
+// split-K partials of a forward GEMM over n projections: one launch over all
+// of them, or one per projection where a tile would straddle two
+size_t split_bytes(int64_t T, int64_t N, int64_t in, const int64_t* outs, int n) {
+  size_t b = gemm_split_bytes(T, N, in);
+  for (int i = 0; i < n && n > 1; ++i) {
+    const size_t bi = gemm_split_bytes(T, outs[i], in);
+    b = bi > b ? bi : b;
+  }
+  return b;
+}
+
 FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout,
                      bool absmax_fp32 = false) {
-  FwdLayout l{0, 0, 0, 0, 0};
+  FwdLayout l{0, 0, 0, 0, 0, 0};
   Carve c;
   if (!dropout && !absmax_fp32 && fwd_uses_decode(T, in, outs, n, r)) {
     l.u_pad = c.take(decode_u_bytes(n, T, r));  // U [n][T][r] fp32
@@ -129,11 +140,13 @@ FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
   l.b_pad = c.take(static_cast<size_t>(N * n * rp * 4));  // [N][2rp] or [N][n 2rp] bf16
   l.part = c.take(lora_down_part_bytes(T, in, n * rp));
   if (fwd_expands(T, absmax_fp32)) l.w_dq = c.take(static_cast<size_t>(N * in * 2));  // [N][in] bf16
+  l.split = c.take(split_bytes(T, N, in, outs, n));  // split-K partials of the GEMM
   l.total = c.off;
   return l;
 }
 
 int64_t token_pitch(int64_t T) { return round_up(T, 8); }
+
 
 // Up to kDxSmallMaxT tokens without dropout the backward is the three
 // launches of k_dx_small.hip: no W_hat^T, no padded factors; the W_hat^T
@@ -183,6 +196,7 @@ BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
     l.a_t_pad = c.take(static_cast<size_t>(in * n * rp * 4));             // [in][n 2rp] bf16
     if (expand) l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));       // [in][N] bf16
     l.part = c.take(part);
+    l.split = c.take(gemm_split_bytes(T, in, N));  // split-K partials of the dX GEMM
   }
   l.total = c.off;
   return l;
@@ -414,6 +428,8 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   uint16_t* u_pad = reinterpret_cast<uint16_t*>(base + lay.u_pad);
   uint16_t* b_pad = reinterpret_cast<uint16_t*>(base + lay.b_pad);
   float* part = reinterpret_cast<float*>(base + lay.part);
+  float* split = reinterpret_cast<float*>(base + lay.split);
+  const size_t split_n = lay.total - lay.split;
   // s X A_i^T for every projection in one pass over X: [T][n 2rp]; with
   // dropout s / (1 - p) (keep o X) A^T
   const float uscale = dropout ? scale / (1.f - p) : scale;
@@ -445,9 +461,10 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
         const uint16_t* act1[kMaxProj];
         for (int i = 0; i < n; ++i) act1[i] = u_pad + i * 2 * rp;
         e = launch_gemm_nt_proj(T, n, outs, act1, X, in, w_dq, in, in, n * 2 * rp, b_pad, ldb, 2 * rp, Y, N,
-                                s);
+                                s, split, split_n);
       } else {
-        e = launch_gemm_nt(T, N, X, in, w_dq, in, in, u_pad, ldb, b_pad, ldb, ldb, Y, N, s);
+        e = launch_gemm_nt(T, N, X, in, w_dq, in, in, u_pad, ldb, b_pad, ldb, ldb, Y, N, s, nullptr, 0, 1.f,
+                           split, split_n);
       }
     }
     return launched(e);
@@ -460,7 +477,7 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
     off += outs[i];
   }
   if (e == hipSuccess)
-    e = launch_gemm_nf4(T, n, proj, X, in, in, n * 2 * rp, b_pad, 2 * rp, 2 * rp, Y, N, s);
+    e = launch_gemm_nf4(T, n, proj, X, in, in, n * 2 * rp, b_pad, 2 * rp, 2 * rp, Y, N, s, split, split_n);
   return launched(e);
 }
 
@@ -544,6 +561,8 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   uint16_t* a_t_pad = reinterpret_cast<uint16_t*>(base + lay.a_t_pad);
   uint16_t* w_dq_t = reinterpret_cast<uint16_t*>(base + lay.w_dq_t);
   float* part = reinterpret_cast<float*>(base + lay.part);
+  float* split = reinterpret_cast<float*>(base + lay.split);
+  const size_t split_n = lay.total - lay.split;
 
   // (sU_i)^T for every projection in one pass over X (with dropout the
   // masked input: s / (1 - p) (keep o X) A^T, which dB then uses as is)
@@ -570,13 +589,13 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     Nf4Proj proj[kMaxProj];
     for (int i = 0; i < n; ++i) proj[i] = Nf4Proj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], nullptr};
     e = launch_gemm_nf4t(T, in, n, proj, dY, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp, dX, in, s,
-                         keep, in / 8, inv_keep);
+                         keep, in / 8, inv_keep, split, split_n);
   } else if (e == hipSuccess) {
     // dX = sum_i dY_i W_hat_i + (sV_i) A_i: one GEMM over the concatenated K
     // (with dropout the adapter term is masked and scaled by 1 / (1 - p)
     // before the base is added)
     e = launch_gemm_nt(T, in, dY, N, w_dq_t, N, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp,
-                       dX, in, s, keep, in / 8, inv_keep);
+                       dX, in, s, keep, in / 8, inv_keep, split, split_n);
   }
   off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {

@@ -12,7 +12,10 @@ Checks:
   the atomics' summation order, at shapes that run every kernel form (the
   128 x 128 kernel with a partial column tile, the 256-column kernel with 128-
   and 256-row tiles), several projections, and dropout;
-- one-hot dY rows select rows of W_hat bit for bit through the fused route."""
+- one-hot dY rows select rows of W_hat bit for bit through the fused route;
+- split-K (grids below one workgroup per CU, forward and backward, both
+  routes): oracle parity, repeated calls bit for bit, one-hot pins, several
+  projections, dropout."""
 
 import numpy as np
 import pytest
@@ -152,3 +155,114 @@ def test_fused_route_one_hot_rows_bit_exact(T, n_out, n_in):
                                     ws=_min_ws(q, T, n_in, [n_out], r))
     assert np.array_equal(host_bits(dX), _w_hat(w)[gi, :])
     assert np.all(host(dB) == 0)  # U = X A^T = 0
+
+
+# ------------------------------------------------------------------ split-K
+# Grids of 128 x 128 tiles below one workgroup per CU (e.g. 64 tokens against
+# 4096 output columns: 32 tiles) split K into up to 8 ranges of fp32 partials,
+# summed in order and rounded once.
+
+def _single(seed, T, n_out, n_in, r):
+    (w,), (A,), (B,), X, dY = _inputs(seed, T, n_in, [n_out], r)
+    return w, A, B, X, dY
+
+
+@pytest.mark.parametrize("T,n_out,n_in,r", [
+    (64, 4096, 4096, 16),    # fwd: 32 tiles, 8 splits of 8 K-steps; dX: 32 tiles, 8 splits
+    (64, 14336, 4096, 64),   # dX over K = 14336: 8 splits of 28 K-steps
+    (100, 1024, 640, 16),    # ragged T, partial column tile, 2 splits of 8 K-steps (dX)
+])
+def test_split_k_matches_oracle_and_repeats(T, n_out, n_in, r):
+    q = require_gpu()
+    banner(f"split-K T={T} out={n_out} in={n_in} r={r}")
+    alpha = 2.0 * r
+    w, A, B, X, dY = _single(1600 + T, T, n_out, n_in, r)
+    W = q.nf4_quantize_weight(dev_f32(w))
+    Xd, dYd, Ad, Bd = dev_bf16(X), dev_bf16(dY), dev_bf16(A), dev_bf16(B)
+    w_hat = _w_hat(w)
+    Y = host_bits(q.qlora_linear_fwd(W, Xd, Ad, Bd, r, alpha))
+    ref = odense.linear_fwd(w_hat, X, A, B, alpha, r)
+    ey = odense.rel_frobenius(onf4.bf16_bits_to_f32(Y).astype(np.float64), ref)
+    rdX, rdA, rdB = odense.linear_bwd(w_hat, X, dY, A, B, alpha, r)
+    for ws in (None, _min_ws(q, T, n_in, [n_out], r)):
+        dX, dA, dB = q.qlora_linear_bwd(W, Xd, dYd, Ad, Bd, r, alpha, ws=ws)
+        ex = odense.rel_frobenius(onf4.bf16_bits_to_f32(host_bits(dX)).astype(np.float64), rdX)
+        ea = odense.rel_frobenius(host(dA).astype(np.float64), rdA)
+        eb = odense.rel_frobenius(host(dB).astype(np.float64), rdB)
+        print(f"  {'min' if ws is not None else 'full'} ws: Y={ey:.3e} dX={ex:.3e} dA={ea:.3e} dB={eb:.3e}",
+              flush=True)
+        assert max(ey, ex, ea, eb) <= TOL
+        # the partial sums are added in a fixed order: a second call repeats dX bit for bit
+        dX2 = q.qlora_linear_bwd(W, Xd, dYd, Ad, Bd, r, alpha, ws=ws)[0]
+        assert np.array_equal(host_bits(dX2), host_bits(dX))
+    assert np.array_equal(host_bits(q.qlora_linear_fwd(W, Xd, Ad, Bd, r, alpha)), Y)
+
+
+def test_split_k_routes_equal():
+    # 8B gate dX at 64 tokens: both routes split K the same way, dX bit for bit
+    q = require_gpu()
+    banner("split-K fused vs expanded T=64 in=4096 out=14336")
+    _, fused, full = _both(q, 64, 4096, [14336], 64, 128.0, 1700)
+    _same_route_result(fused, full)
+
+
+@pytest.mark.parametrize("T,n_in,outs", [(64, 4096, [4096, 1024, 1024]), (64, 1024, [4160, 4032])])
+def test_split_k_multi_forward(T, n_in, outs):
+    # one launch over q|k|v-like stacked projections, and one launch per
+    # projection where a 128-column tile would straddle two
+    q = require_gpu()
+    banner(f"split-K multi fwd T={T} in={n_in} outs={outs}")
+    r, alpha = 16, 32.0
+    ws, As, Bs, X, _ = _inputs(1800 + len(outs), T, n_in, outs, r)
+    Ws = [q.nf4_quantize_weight(dev_f32(w)) for w in ws]
+    Y = host_bits(q.qlora_linear_fwd_multi(Ws, dev_bf16(X), [dev_bf16(a) for a in As],
+                                           [dev_bf16(b) for b in Bs], r, alpha))
+    col = 0
+    for w, A, B, o in zip(ws, As, Bs, outs):
+        ref = odense.linear_fwd(_w_hat(w), X, A, B, alpha, r)
+        got = onf4.bf16_bits_to_f32(np.ascontiguousarray(Y[:, col:col + o])).astype(np.float64)
+        assert odense.rel_frobenius(got, ref) <= TOL
+        col += o
+
+
+@pytest.mark.parametrize("T,n_out,n_in", [(64, 512, 8192), (64, 8192, 512)])
+def test_split_k_one_hot_bit_exact(T, n_out, n_in):
+    # one-hot X (B = 0): Y[t] = W_hat[:, i_t]; one-hot dY (A = 0): dX[t] = W_hat[n_t]
+    # -- the one nonzero product lands in one split, the others add exact zeros
+    q = require_gpu()
+    banner(f"split-K one-hot T={T} out={n_out} in={n_in}")
+    r = 16
+    w = synth.normal_f32(79_000 + n_out, (n_out, n_in), synth.W_STD)
+    rng = np.random.default_rng(T + n_out)
+    xi, gi = rng.integers(0, n_in, T), rng.integers(0, n_out, T)
+    A = synth.bf16_bits(synth.normal_f32(5, (r, n_in), 1.0 / n_in))
+    B = synth.bf16_bits(synth.normal_f32(6, (n_out, r), synth.B_STD))
+    W = q.nf4_quantize_weight(dev_f32(w))
+    w_hat = _w_hat(w)
+    Y = q.qlora_linear_fwd(W, dev_bf16(_one_hot(n_in, xi)), dev_bf16(A), dev_bf16(np.zeros_like(B)), r, 32.0)
+    assert np.array_equal(host_bits(Y), w_hat[:, xi].T)
+    Xr = synth.bf16_bits(synth.normal_f32(7, (T, n_in), 1.0))
+    for ws in (None, _min_ws(q, T, n_in, [n_out], r)):
+        dX = q.qlora_linear_bwd(W, dev_bf16(Xr), dev_bf16(_one_hot(n_out, gi)), dev_bf16(np.zeros_like(A)),
+                                dev_bf16(B), r, 32.0, ws=ws)[0]
+        assert np.array_equal(host_bits(dX), w_hat[gi, :])
+
+
+def test_split_k_with_dropout():
+    q = require_gpu()
+    T, n_in, n_out, r, p = 64, 1024, 4096, 16, 0.1
+    banner(f"split-K dropout T={T} in={n_in} out={n_out}")
+    w, A, B, X, dY = _single(1900, T, n_out, n_in, r)
+    rng = np.random.Generator(np.random.PCG64(1901))
+    keep_bool = rng.random((T, n_in)) >= p
+    keep = np.packbits(keep_bool, axis=1, bitorder="little")
+    W = q.nf4_quantize_weight(dev_f32(w))
+    K = torch.from_numpy(np.ascontiguousarray(keep)).cuda()
+    args = (dev_bf16(X), dev_bf16(dY), K, p, dev_bf16(A), dev_bf16(B), r, 32.0)
+    rdX, rdA, rdB = odense.linear_bwd_dropout(_w_hat(w), X, dY, A, B, 32.0, r, keep_bool, p)
+    for ws in (None, _min_ws(q, T, n_in, [n_out], r, dropout=True)):
+        dX, dA, dB = q.qlora_linear_bwd_dropout(W, *args, ws=ws)
+        ex = odense.rel_frobenius(onf4.bf16_bits_to_f32(host_bits(dX)).astype(np.float64), rdX)
+        assert ex <= TOL, ex
+        assert odense.rel_frobenius(host(dA).astype(np.float64), rdA) <= TOL
+        assert odense.rel_frobenius(host(dB).astype(np.float64), rdB) <= TOL
