@@ -63,6 +63,9 @@ def parse():
                          "3 = 8B MLP, 4 = 8B attention, 5 = 70B MLP) and print its figures (for "
                          "rocprofv3 --pmc passes over the large-token GEMMs)")
     ap.add_argument("--probe-workload", type=int, default=3, choices=(3, 4, 5))
+    ap.add_argument("--bwd-min", action="store_true",
+                    help="with --mlp-probe: every backward in its smallest workspace (the dX GEMM "
+                         "dequantizes the weight tiles while staging them)")
     ap.add_argument("--only-leg", choices=("quantize", "merge", "bwd_small"),
                     help="only run one standalone leg (the 2^30 flat quantize, or the 8B and 70B gate "
                          "merges) and then the 256 MiB copy, and print its figures (for rocprofv3 "
@@ -176,7 +179,15 @@ def main():
         return
     if args.mlp_probe:
         del pool
-        print(json.dumps(large_step_leg(q, synth, dev, bf, args.probe_workload, steps=5)), flush=True)
+        wid = args.probe_workload
+        if args.bwd_min:
+            wl = synth.WORKLOADS[wid]
+            flop = sum(step_flop(wl.tokens[0], p.in_features, p.out_features, wl.r) for p in wl.projections)
+            res = grouped_step_leg(q, synth, dev, bf, wid, [[i] for i in range(len(wl.projections))], 5, flop,
+                                   bwd_min=True)
+        else:
+            res = large_step_leg(q, synth, dev, bf, wid, steps=5)
+        print(json.dumps(res), flush=True)
         return
 
     b1 = decode_call_bytes(n_out, n_in, 1, r)
@@ -336,6 +347,7 @@ def main():
                                                      extra["attn8b_fwd_bwd"]["step_flop"])
         extra["mlp70b_gate_up_fused"] = grouped_step_leg(q, synth, dev, bf, 5, [[0, 1], [2]], 5,
                                                          extra["mlp70b_fwd_bwd"]["step_flop"])
+        extra["mid_tokens"] = mid_tokens_leg(q, synth, dev, bf)
         # the backward in its smallest workspace: dX without the expanded W_hat^T
         extra["mlp8b_bwd_min_workspace"] = grouped_step_leg(q, synth, dev, bf, 3, [[0], [1], [2]], 10,
                                                             extra["mlp8b_fwd_bwd"]["step_flop"], bwd_min=True)
@@ -1042,6 +1054,63 @@ def large_step_leg(q, synth, dev, bf, wid, steps):
     res.update({"step_flop": tot_flop, "step_ms": round(step_ms, 3), "sum_of_calls_ms": round(tot_ms, 3),
                 "fwd_bwd_TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
     del items, wsf, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
+def mid_tokens_leg(q, synth, dev, bf, n=20):
+    """Forward and backward calls at token counts between the small-token
+    kernels and full GEMM grids (64 and 256 tokens: the GEMMs split K), on the
+    8B gate (4096 -> 14336) and down (14336 -> 4096) shapes at r = 64 and the
+    q_proj shape (4096 -> 4096) at r = 16; the backward with the full workspace
+    (expanded W_hat^T) and with the smallest (fused dX).  Each call is warmed
+    up, then timed over n calls with events."""
+    import torch
+    res = {}
+    for name, wid, pi in (("8b_gate", 3, 0), ("8b_down", 3, 2), ("q_proj", 4, 0)):
+        wl = synth.WORKLOADS[wid]
+        p = wl.projections[pi]
+        n_out, n_in, r, alpha = p.out_features, p.in_features, wl.r, wl.alpha
+        w = torch.from_numpy(synth.weight(wid, pi, n_out, n_in)).to(dev)
+        W = q.nf4_quantize_weight(w)
+        del w
+        A = bf(synth.lora_A(wid, pi, r, n_in))
+        B = bf(synth.lora_B(wid, pi, n_out, r))
+        res[name] = {"out": n_out, "in": n_in, "r": r}
+        for T in (64, 256):
+            X = bf(synth.activations(wid, pi, T, n_in))
+            dY = bf(synth.activations(wid, pi, T, n_out, "dY"))
+            Y = torch.empty(T, n_out, dtype=torch.bfloat16, device=dev)
+            dX = torch.empty(T, n_in, dtype=torch.bfloat16, device=dev)
+            dA = torch.empty(r, n_in, dtype=torch.float32, device=dev)
+            dB = torch.empty(n_out, r, dtype=torch.float32, device=dev)
+            wf = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, False), dev)
+            wb = q.make_workspace(q.qlora_workspace_bytes(T, n_in, n_out, r, True), dev)
+            wm = q.make_workspace(q.qlora_workspace_bytes_bwd_min(T, n_in, [n_out], r), dev)
+
+            def timed(fn):
+                for _ in range(4):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(n):
+                    fn()
+                e1.record()
+                e1.synchronize()
+                return e0.elapsed_time(e1) / n * 1e3
+
+            f_us = timed(lambda: q.qlora_linear_fwd(W, X, A, B, r, alpha, Y=Y, ws=wf))
+            b_us = timed(lambda: q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX, dA, dB, ws=wb))
+            m_us = timed(lambda: q.qlora_linear_bwd(W, X, dY, A, B, r, alpha, dX, dA, dB, ws=wm))
+            flop_f = 2 * T * n_in * n_out + 2 * T * r * (n_in + n_out)
+            flop_b = 2 * T * n_in * n_out + 4 * T * r * (n_in + n_out)
+            res[name][f"T{T}"] = {"fwd_us": round(f_us, 1), "bwd_us": round(b_us, 1),
+                                  "bwd_min_workspace_us": round(m_us, 1),
+                                  "fwd_TFLOPs": round(flop_f / (f_us * 1e-6) / 1e12, 1),
+                                  "bwd_TFLOPs": round(flop_b / (b_us * 1e-6) / 1e12, 1),
+                                  "bwd_workspace_bytes": {"full": int(wb.numel()), "min": int(wm.numel())}}
+            del X, dY, Y, dX, dA, dB, wf, wb, wm
+        del W
     torch.cuda.empty_cache()
     return res
 
