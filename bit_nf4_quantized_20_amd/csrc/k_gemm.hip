@@ -49,8 +49,6 @@ constexpr int kBK = 64;
 constexpr int kWBf16 = 0;  // bf16 matrix [N][K]
 constexpr int kWNf4 = 1;   // NF4 weight [N][K], dequantized while staged
 constexpr int kWNf4T = 2;  // NF4 weight [K][N] (dX), dequantized and transposed while staged
-// row pitch (elements) of a transposed NF4 weight tile in LDS
-constexpr int kPitchT = kBK + 8;
 
 // 16-byte chunk swizzle of a 128-byte LDS row.  A fragment read has 32
 // lanes on 32 consecutive rows at one chunk; the key (row & 7) ^ (row >> 3 & 1)
@@ -209,16 +207,42 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chu
   const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kBK + swz(row, chunk) * 8);
   return __builtin_bit_cast(bf16x8, v);
 }
-// The same from a padded tile (rows of kPitchT elements, no swizzle).
-__device__ __forceinline__ bf16x8 lds_frag_pad(const uint16_t* lds, int row, int chunk) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kPitchT + chunk * 8);
-  return __builtin_bit_cast(bf16x8, v);
+// Transposed NF4 weight tiles (the dX GEMM) are stored K-row-major: row k
+// of W (a K index) holds the tile's BN columns, 16-byte chunk c of row k at
+// chunk c ^ tswz(k).  tswz(k) = 4 (k % 4) + (k / 4) % 4 keeps both accesses
+// conflict-free on the 64-bank LDS: a dequantize write (16 lanes, 16
+// consecutive rows, one chunk) lands in 16 distinct chunk slots, and a
+// transposed fragment read (32 lanes: 4 consecutive rows x 4 consecutive
+// chunks, 8 bytes per lane) covers 16 distinct slots.
+__device__ __forceinline__ int tswz(int k) { return 4 * (k & 3) + ((k >> 2) & 3); }
+
+// MFMA operand fragment of rows n = n0 .. n0 + 31 (n0 wave-uniform), K
+// sub-step j, from a transposed tile of BN columns: lane l holds n = n0 + l % 32
+// and k = 16 j + 8 (l / 32) + 0..7.  ds_read_b64_tr_b16 hands each group of
+// 16 lanes a 16 x 4 block transposed: lane i of the group supplies the address
+// of row i / 4 (of four consecutive rows) at columns 4 (i % 4) .. + 3, and
+// receives column i of the four rows.  Two such reads give the eight k.
+template <int BN>
+__device__ __forceinline__ bf16x8 lds_frag_tr(const uint16_t* lds, int n0, int j) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const int l = threadIdx.x & 63, i = l & 15, G = l >> 4;
+  const int n = n0 + 16 * (G & 1) + 4 * (i & 3);
+  v4s v[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int k = 16 * j + 8 * (G >> 1) + 4 * s2 + (i >> 2);
+    const int e = k * BN + (((n >> 3) ^ tswz(k)) << 3) + (n & 4);
+    v[s2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(const_cast<uint16_t*>(lds) + e));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
-// A weight fragment of the main segment (kPad: a transposed NF4 tile) or of
-// the LoRA segment (always swizzled).
-template <bool kPad>
-__device__ __forceinline__ bf16x8 wt_frag(const uint16_t* lds, int row, int chunk) {
-  if constexpr (kPad) return lds_frag_pad(lds, row, chunk);
+// A weight fragment of the main segment (kTr: a transposed NF4 tile of BN
+// columns) or of the LoRA segment (always the swizzled N-row-major tile);
+// row = n0 + lane % 32, chunk = 2 j + lane / 32.
+template <bool kTr, int BN>
+__device__ __forceinline__ bf16x8 wt_frag(const uint16_t* lds, int n0, int row, int j, int chunk) {
+  if constexpr (kTr) return lds_frag_tr<BN>(lds, n0, j);
   else return lds_frag(lds, row, chunk);
 }
 
@@ -323,20 +347,16 @@ struct RegsOf { using type = NoRegs; };
 template <class T>
 struct RegsOf<T, true> { using type = typename T::Regs; };
 
-// NF4 weights read transposed, for dX = dY W_hat: the tile holds W_hat^T rows
-// [n0, n0 + ROWS) -- columns of W -- by 64 K, and K runs along W's rows (over
-// several projections, the projections' rows one after another: each K-step
-// picks its projection from the table).  The 64-weight blocks run along W's
-// rows, i.e. across the tile's rows, so wave g takes the 32 columns
-// [n0 + 32 g, n0 + 32 g + 32) and lane k row k of each K-step: its 16 code
-// bytes (half a block), the block's absmax code and group scale.  At store
-// time the lane expands its 32 weights with the block's table and writes each
-// one into its column's LDS row, 16 bits at a time.  This tile uses padded
-// rows (kPitchT elements, no XOR swizzle), so (column n, row k) sits at
-// n kPitchT + k: one per-lane base plus an immediate offset per column, and a
-// wave's 64 lanes write one whole 128-byte row per instruction.  Eight
-// consecutive rows of 144 bytes start in distinct 16-byte bank groups, so the
-// fragment reads stay conflict-free.
+// NF4 weights for dX = dY W_hat: the tile holds W_hat^T rows [n0, n0 + ROWS)
+// -- columns of W -- by 64 K, and K runs along W's rows (over several
+// projections, the projections' rows one after another: each K-step picks its
+// projection from the table).  The 64-weight blocks run along W's rows, so
+// wave g takes the 32 columns [n0 + 32 g, n0 + 32 g + 32) and lane k row k of
+// each K-step: its 16 code bytes (half a block), the block's absmax code and
+// group scale.  At store time the lane expands its 32 weights with the block's
+// table and writes them as four 16-byte chunks of row k, so the stage holds
+// the tile K-row-major (swizzled by tswz) and the MFMA fragments are read
+// with transposing loads (lds_frag_tr).
 template <int ROWS, int NT>
 struct Nf4TileT {
   static_assert(NT == 2 * ROWS, "one wave per 32 columns");
@@ -350,7 +370,7 @@ struct Nf4TileT {
   int64_t in;
   uint32_t coff, qoff;  // this lane's code byte / absmax code in row 0 of a projection
   uint32_t bcol;        // its column block
-  uint32_t slot;        // LDS element index of (column 32 g, row k)
+  uint32_t wofs[kDw];   // LDS element offsets of its four 16-byte chunks
 
   // the tile's first column n0 (columns past `in` load valid data that is never stored)
   __device__ __forceinline__ void init(const GemmArgs& args, int64_t n0, int tid) {
@@ -362,7 +382,8 @@ struct Nf4TileT {
     coff = static_cast<uint32_t>(k * (in / 2) + c0 / 2);
     qoff = static_cast<uint32_t>(k * (in / 64) + c0 / 64);
     bcol = static_cast<uint32_t>(c0 / 64);
-    slot = static_cast<uint32_t>(32 * g * kPitchT + k);
+#pragma unroll
+    for (int d = 0; d < kDw; ++d) wofs[d] = static_cast<uint32_t>(k * ROWS + (((4 * g + d) ^ tswz(k)) << 3));
   }
   // K-step starting at row k0 of the stacked projections
   __device__ __forceinline__ void load(Regs& r, int64_t k0) const {
@@ -378,17 +399,11 @@ struct Nf4TileT {
     r.sg = sg.scale[((kr + k) * (in / 64) + bcol) >> 8];
   }
   __device__ __forceinline__ static Nf4Table table(const Regs& r) { return make_table(dq_absmax(r.q, r.sg)); }
-  // code dword d: the lane's columns 8 d .. 8 d + 7
+  // code dword d: the lane's columns 8 d .. 8 d + 7, one 16-byte chunk
   __device__ __forceinline__ void store_part(const Regs& r, const Nf4Table& tab, uint16_t* lds, int, int d) const {
-    uint32_t v[4];
-    lookup8_split(tab, r.cw[d], v);
-    uint16_t* const dst = lds + slot;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = kSplitOrder[q];  // element e of the dword sits at split position q
-      const uint32_t w = v[q >> 1];
-      dst[(8 * d + e) * kPitchT] = static_cast<uint16_t>((q & 1) ? (w >> 16) : w);
-    }
+    uint32_t o[4];
+    lookup8(tab, r.cw[d], o);
+    *reinterpret_cast<u32x4*>(lds + wofs[d]) = u32x4{o[0], o[1], o[2], o[3]};
   }
   __device__ __forceinline__ void store(const Regs& r, uint16_t* lds, int tid) const {
     const Nf4Table tab = table(r);
@@ -411,8 +426,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / 32, FN = WN / 32;
   __shared__ __attribute__((aligned(16))) uint16_t s_act[2][BM * kBK];
-  constexpr bool kPadW = kW == kWNf4T;  // main-segment weight tile in padded rows
-  __shared__ __attribute__((aligned(16))) uint16_t s_wt[2][BN * (kPadW ? kPitchT : kBK)];
+  __shared__ __attribute__((aligned(16))) uint16_t s_wt[2][BN * kBK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
       const int chunk = 2 * j + half;
       bf16x8 fw[FN], fa[FM];
 #pragma unroll
-      for (int a = 0; a < FN; ++a) fw[a] = wt_frag<P>(sw, wn * WN + a * 32 + r32, chunk);
+      for (int a = 0; a < FN; ++a) fw[a] = wt_frag<P, BN>(sw, wn * WN + a * 32, wn * WN + a * 32 + r32, j, chunk);
 #pragma unroll
       for (int c = 0; c < FM; ++c) fa[c] = lds_frag(sa, wm * WM + c * 32 + r32, chunk);
 #pragma unroll
@@ -642,8 +656,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   constexpr int FN = 2, WN = 64, FM = BM / 64, WM = BM / 2;  // wave tile BM/2 (m) x 64 (n)
   __shared__ __attribute__((aligned(1024))) uint16_t s_act0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t s_act1[BM * kBK];
-  constexpr bool kPadW = kW == kWNf4T;  // main-segment weight tile in padded rows
-  constexpr int kWtElems = BN * (kPadW ? kPitchT : kBK);
+  constexpr bool kTrW = kW == kWNf4T;  // main-segment weight tile K-row-major (transposed reads)
+  constexpr int kWtElems = BN * kBK;
   __shared__ __attribute__((aligned(1024))) uint16_t s_wt0[kWtElems];
   __shared__ __attribute__((aligned(1024))) uint16_t s_wt1[kWtElems];
   uint16_t* const s_act[2] = {s_act0, s_act1};
@@ -666,12 +680,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.f;
 
   typedef bf16x8 Frags[FN + FM];  // [0, FN) weight rows, [FN, FN + FM) activation rows
-  // kPad: the weight stage holds a padded (transposed NF4) tile
+  // pad: the weight stage holds a transposed NF4 tile (K-row-major)
   auto read_frags = [&](Frags& f, const uint16_t* sw, const uint16_t* sa, int j, auto pad) {
     constexpr bool P = decltype(pad)::value;
     const int chunk = 2 * j + half;
 #pragma unroll
-    for (int a = 0; a < FN; ++a) f[a] = wt_frag<P>(sw, wn * WN + a * 32 + r32, chunk);
+    for (int a = 0; a < FN; ++a) f[a] = wt_frag<P, BN>(sw, wn * WN + a * 32, wn * WN + a * 32 + r32, j, chunk);
 #pragma unroll
     for (int c = 0; c < FM; ++c) f[FN + c] = lds_frag(sa, wm * WM + c * 32 + r32, chunk);
   };
@@ -698,8 +712,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using PadMain = std::integral_constant<bool, kPadW>;
-  using NoPad = std::integral_constant<bool, false>;
+  using TrMain = std::integral_constant<bool, kTrW>;
+  using NoTr = std::integral_constant<bool, false>;
 
   // Main segment.  TW: DtlTile (bf16 weight), Nf4Tile or Nf4TileT (codes in registers).
   auto main_loop = [&](DtlTile<BM, NW>& ta, auto& tw, int64_t steps) {
@@ -724,7 +738,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     Frags f0, f1;
-    read_frags(f0, s_wt0, s_act0, 0, PadMain{});
+    read_frags(f0, s_wt0, s_act0, 0, TrMain{});
     // Step e: stage B holds step e; code set (C + 1) % 3 holds step e + 1 and
     // set C (step e's, consumed) takes step e + 3.
     auto step = [&](int64_t e, auto bc, auto cc) {
@@ -750,15 +764,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       __builtin_amdgcn_s_setprio(1);  // the MFMA phase issues ahead of the other wave's loads
       if constexpr (kRegW) tab = TW::table(nxt);
       part(0);
-      read_frags(f1, sw, sa, 1, PadMain{});
+      read_frags(f1, sw, sa, 1, TrMain{});
       mfmas(f0);
       interleave();
       part(1);
-      read_frags(f0, sw, sa, 2, PadMain{});
+      read_frags(f0, sw, sa, 2, TrMain{});
       mfmas(f1);
       interleave();
       part(2);
-      read_frags(f1, sw, sa, 3, PadMain{});
+      read_frags(f1, sw, sa, 3, TrMain{});
       mfmas(f0);
       interleave();
       part(3);
@@ -771,7 +785,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       if constexpr (kRegW) __builtin_amdgcn_s_waitcnt(0x73);  // vmcnt(3) lgkmcnt(0)
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      read_frags(f0, nw, na, 0, PadMain{});
+      read_frags(f0, nw, na, 0, TrMain{});
     };
     int64_t e = 0;
     for (; e + 6 <= steps; e += 6) {
@@ -813,14 +827,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         Frags f;
-        read_frags(f, s_wt0, s_act0, j, NoPad{});
+        read_frags(f, s_wt0, s_act0, j, NoTr{});
         mfmas(f);
       }
       if (two) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           Frags f;
-          read_frags(f, s_wt1, s_act1, j, NoPad{});
+          read_frags(f, s_wt1, s_act1, j, NoTr{});
           mfmas(f);
         }
       }
