@@ -346,11 +346,14 @@ __device__ __forceinline__ int grad_qslot(int c, int w) { return kGradPitch * c 
 // follows it, so a wave's 32 lanes always add to 32 consecutive floats.
 // kMask: Q[t][c] counts only where bit c % 8 of keep[t * ldk + c / 8] is set;
 // every output sum is multiplied by oscale.
+// The workgroup of token slice y writes its sums (times oscale) to slice y of
+// `part` ([slices][r * C] floats, each element written once per slice); a
+// second launch adds the slices in order (k_sum_slices).
 template <int JT, bool kJC, bool kMask>
 __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ Pt, int64_t T,
                                                    int64_t ldt, int rp, const uint16_t* __restrict__ Q,
                                                    int64_t C, int64_t ldq, int r, int j0,
-                                                   float* __restrict__ out, int64_t TS,
+                                                   float* __restrict__ part, int64_t TS,
                                                    const uint8_t* __restrict__ keep, int64_t ldk,
                                                    float oscale) {
   constexpr int kPRows = 64 * JT;  // hi rows [0, 32JT), lo rows [32JT, 64JT)
@@ -478,6 +481,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
     body(step, I0{});
     body(step + 1, I1{});
   }
+  float* const out = part + static_cast<int64_t>(blockIdx.y) * r * C;  // this slice's sums
   if constexpr (kJC) {
     // D[j][c]: lane holds column c, rows j = 8*(e/4) + 4*h + e%4
     const int64_t cc = c0 + c;
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = j0 + 32 * jt + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (j < r) atomicAdd(out + static_cast<int64_t>(j) * C + cc, acc[jt][e] * oscale);
+        if (j < r) out[static_cast<int64_t>(j) * C + cc] = acc[jt][e] * oscale;
       }
   } else {
     // D[c][j]: lane holds rank j, rows c = 8*(e/4) + 4*h + e%4 of the wave's tile
@@ -498,32 +502,44 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t cc = c0 + 32 * wv + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (cc < C) atomicAdd(out + cc * r + j, acc[jt][e] * oscale);
+        if (cc < C) out[cc * r + j] = acc[jt][e] * oscale;
       }
     }
   }
 }
 
-hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
-                            int64_t C, int64_t ldq, int64_t r, float* out, bool out_jc, hipStream_t s,
-                            const uint8_t* keep, int64_t ldk, float oscale) {
-  if (T <= 0) return hipSuccess;
-  // token slices (multiples of 64) for about one workgroup per CU: more
-  // slices shorten each workgroup's stream but add their partial sums with
-  // atomics (measured on the 8B-MLP shapes: 256-450 workgroups are fastest,
-  // 560 were 35% slower for 14336 columns, 512 were 30% slower for 4096)
+// Token slices (multiples of 64 tokens) for about one workgroup per CU: more
+// slices shorten each workgroup's stream but add partial sums (measured on
+// the 8B-MLP shapes: 256-450 workgroups are fastest, 560 were 35% slower for
+// 14336 columns, 512 were 30% slower for 4096).  The count depends on the
+// shape only.
+namespace {
+int64_t grad_slice_tokens(int64_t T, int64_t C, int64_t ldq) {
   const int64_t ctiles = ceil_div(C, kGradCT);
   int64_t slices = ceil_div(256, ctiles);
   const int64_t max_slices = ceil_div(T, 64);
   if (slices > max_slices) slices = max_slices;
   if (slices < 1) slices = 1;
-  // 32-bit buffer offsets: a slice of Q stays under 2^30 bytes, Pt under 2^31
+  // 32-bit buffer offsets: a slice of Q stays under 2^30 bytes
   const int64_t min_slices = ceil_div(T * ldq * 2, int64_t(1) << 30);
   if (slices < min_slices) slices = min_slices;
-  if (2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  return round_up(ceil_div(T, slices), 64);
+}
+}  // namespace
+
+int64_t lora_grad_slices(int64_t T, int64_t C, int64_t ldq) {
+  return T > 0 ? ceil_div(T, grad_slice_tokens(T, C, ldq)) : 0;
+}
+
+hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
+                            int64_t C, int64_t ldq, int64_t r, float* part, bool out_jc, hipStream_t s,
+                            const uint8_t* keep, int64_t ldk, float oscale) {
+  if (T <= 0) return hipSuccess;
+  if (2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // Pt under 2^31 bytes
   if (keep != nullptr && T * ldk >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const int64_t TS = round_up(ceil_div(T, slices), 64);
-  slices = ceil_div(T, TS);
+  const int64_t TS = grad_slice_tokens(T, C, ldq);
+  const int64_t slices = ceil_div(T, TS);
+  const int64_t ctiles = ceil_div(C, kGradCT);
   const dim3 grid(static_cast<uint32_t>(ctiles), static_cast<uint32_t>(slices));
   const int irp = static_cast<int>(rp), ir = static_cast<int>(r);
   for (int64_t j0 = 0; j0 < r; j0 += 32 * kGradMaxJT) {
@@ -532,7 +548,7 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
     const int ij0 = static_cast<int>(j0);
 #define QLORA_GRAD(JTV, JC, MK)                                                                      \
   hipLaunchKernelGGL((k_lora_grad<JTV, JC, MK>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ldq, ir, ij0, \
-                     out, TS, keep, ldk, oscale)
+                     part, TS, keep, ldk, oscale)
     if (keep != nullptr) {  // the masked operand is X: dA, out_jc
       if (jt <= 1) QLORA_GRAD(1, true, true);
       else if (jt <= 2) QLORA_GRAD(2, true, true);
@@ -636,6 +652,69 @@ hipError_t launch_fill_many_f32(float* const* dst, const int64_t* n, int count, 
   L.first[count] = wgs;
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_many_f32, dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, s, L, v);
+  return hipGetLastError();
+}
+
+// out_b[i] = sum over z = 0, 1, ... of part_b[z * n_b + i] for each job b, the
+// slices added in order (bit-reproducible); 4 floats per thread, n_b % 4 == 0.
+struct SumList {
+  const float* part[kMaxFill];
+  float* out[kMaxFill];
+  int64_t n[kMaxFill];
+  int64_t first[kMaxFill + 1];
+  int slices[kMaxFill];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void k_sum_slices(SumList L) {
+  const int64_t wg = blockIdx.x;
+  int b = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxFill; ++i)
+    if (i < L.count && wg >= L.first[i]) b = i;
+  const float* part = L.part[0];
+  float* out = L.out[0];
+  int64_t n = L.n[0], first = L.first[0];
+  int S = L.slices[0];
+#pragma unroll
+  for (int i = 1; i < kMaxFill; ++i)
+    if (i == b) {
+      part = L.part[i]; out = L.out[i]; n = L.n[i]; first = L.first[i]; S = L.slices[i];
+    }
+  const int64_t idx = ((wg - first) * 256 + threadIdx.x) * 4;
+  if (idx >= n) return;
+  // eight slices' loads in flight at a time, added in slice order
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < S; z0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = z0 + u < S ? *reinterpret_cast<const f32x4*>(part + (z0 + u) * n + idx) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < S) acc += v[u];
+  }
+  *reinterpret_cast<f32x4*>(out + idx) = acc;
+}
+
+hipError_t launch_sum_slices(const float* const* part, const int* slices, const int64_t* n, float* const* out,
+                             int count, hipStream_t s) {
+  if (count < 1 || count > kMaxFill) return hipErrorInvalidValue;
+  SumList L{};
+  L.count = count;
+  int64_t wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    if (n[i] % 4 != 0 || slices[i] < 1) return hipErrorInvalidValue;
+    L.part[i] = part[i];
+    L.out[i] = out[i];
+    L.n[i] = n[i];
+    L.slices[i] = slices[i];
+    L.first[i] = wgs;
+    wgs += ceil_div(n[i], 1024);
+  }
+  L.first[count] = wgs;
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sum_slices, dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, s, L);
   return hipGetLastError();
 }
 

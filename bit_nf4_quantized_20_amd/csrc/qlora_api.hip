@@ -88,7 +88,7 @@ struct FwdLayout {
 // costs more than one extra pass of 2.5 bytes per weight.
 constexpr int64_t kMaterializeTokens = 2048;
 struct BwdLayout {
-  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, uvp, suv, split, total;
+  size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, grad, uvp, suv, split, total;
 };
 
 int64_t padded_rank(int64_t r) { return round_up(r, 64); }
@@ -114,6 +114,20 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 // bf16 GEMM (from kMaterializeTokens on, and always for the 4.5-bit format,
 // whose fp32 block absmax only the standalone dequantize reads)
 bool fwd_expands(int64_t T, bool absmax_fp32) { return absmax_fp32 || T >= kMaterializeTokens; }
+
+// token-slice partial sums of one projection's dA_i [r][in] and dB_i
+// [out_i][r] (general backward; the region is reused for every projection)
+size_t grad_part_bytes(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
+  int64_t N = 0;
+  for (int i = 0; i < n; ++i) N += outs[i];
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t bi =
+        static_cast<size_t>(lora_grad_slices(T, in, in) * r * in + lora_grad_slices(T, outs[i], N) * outs[i] * r) * 4;
+    b = bi > b ? bi : b;
+  }
+  return b;
+}
 
 // split-K partials of a forward GEMM over n projections: one launch over all
 // of them, or one per projection where a tile would straddle two
@@ -196,6 +210,7 @@ BwdLayout bwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
     l.a_t_pad = c.take(static_cast<size_t>(in * n * rp * 4));             // [in][n 2rp] bf16
     if (expand) l.w_dq_t = c.take(static_cast<size_t>(in * N * 2));       // [in][N] bf16
     l.part = c.take(part);
+    l.grad = c.take(grad_part_bytes(T, in, outs, n, r));  // token-slice sums of dA_i, dB_i
     l.split = c.take(gemm_split_bytes(T, in, N));  // split-K partials of the dX GEMM
   }
   l.total = c.off;
@@ -540,18 +555,19 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     a.dX = dX;
     return launched(launch_bwd_small(a, lay.uvp - lay.w_dq_t, absmax_fp32(W[0]), s));
   }
-  // dA_i, dB_i are overwritten: zeroed here (one launch), the gradient
-  // kernels then add their token slices
-  float* zero_dst[kMaxFill];
-  int64_t zero_n[kMaxFill];
-  for (int i = 0; i < n; ++i) {
-    zero_dst[2 * i] = dA[i];
-    zero_n[2 * i] = r * in;
-    zero_dst[2 * i + 1] = dB[i];
-    zero_n[2 * i + 1] = outs[i] * r;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    // no tokens: dA_i and dB_i are zero (one launch)
+    float* zero_dst[kMaxFill];
+    int64_t zero_n[kMaxFill];
+    for (int i = 0; i < n; ++i) {
+      zero_dst[2 * i] = dA[i];
+      zero_n[2 * i] = r * in;
+      zero_dst[2 * i + 1] = dB[i];
+      zero_n[2 * i + 1] = outs[i] * r;
+    }
+    return launched(launch_fill_many_f32(zero_dst, zero_n, 2 * n, 0.f, s));
   }
-  hipError_t e = launch_fill_many_f32(zero_dst, zero_n, 2 * n, 0.f, s);
-  if (T == 0 || e != hipSuccess) return launched(e);
 
   const int64_t rp = padded_rank(r), tp = token_pitch(T);
   uint16_t* ut = reinterpret_cast<uint16_t*>(base + lay.ut);
@@ -597,12 +613,25 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     e = launch_gemm_nt(T, in, dY, N, w_dq_t, N, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp,
                        dX, in, s, keep, in / 8, inv_keep, split, split_n);
   }
+  // dA_i and dB_i: token-slice sums into the workspace (one region, reused
+  // projection after projection in stream order), then both outputs written
+  // once with their slices added in order (bit-reproducible)
+  float* const gp = reinterpret_cast<float*>(base + lay.grad);
   off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
-    e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, dA[i], true, s, keep, in / 8,
+    const int64_t sa = lora_grad_slices(T, in, in), sb = lora_grad_slices(T, outs[i], N);
+    float* const pb = gp + sa * r * in;
+    e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, gp, true, s, keep, in / 8,
                          inv_keep);  // dA_i
     if (e == hipSuccess)
-      e = launch_lora_grad(ut + i * 2 * rp * tp, T, tp, rp, dY + off, outs[i], N, r, dB[i], false, s);
+      e = launch_lora_grad(ut + i * 2 * rp * tp, T, tp, rp, dY + off, outs[i], N, r, pb, false, s);  // dB_i
+    if (e == hipSuccess) {
+      const float* part[2] = {gp, pb};
+      const int slices[2] = {static_cast<int>(sa), static_cast<int>(sb)};
+      const int64_t cnt[2] = {r * in, outs[i] * r};
+      float* outp[2] = {dA[i], dB[i]};
+      e = launch_sum_slices(part, slices, cnt, outp, 2, s);
+    }
     off += outs[i];
   }
   return launched(e);

@@ -300,9 +300,9 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
  * paperclase "QLoRA", Parte 4: dL/dx = (W_hat + (alpha/r) B A)^T dL/dh; no
  * gradient for W_hat (the codes are not parameters); A and B are the only
  * trained tensors.  dA and dB are overwritten, not accumulated.  From
- * T = 17 on (or with dropout) they are sums over token slices added with fp32
- * atomics, so two identical calls can differ in their last bits (summation
- * order), and the dX product takes one of two routes, chosen by ws_bytes:
+ * T = 17 on (or with dropout) they are sums over token slices (a count fixed
+ * by the shape) written to the workspace and added in a fixed order, and the
+ * dX product takes one of two routes, chosen by ws_bytes:
  *   ws_bytes >= qlora_workspace_bytes(T, in, out, r, 1): W_hat^T is expanded
  *     into the workspace (2 * out * in bytes) and read by a bf16 GEMM (the
  *     faster route);
@@ -310,11 +310,11 @@ int qlora_linear_bwd_multi(const qlora_nf4_weight* W, int n, const qlora_bf16* X
  *     the codes and dequantizes each weight tile, transposed, while staging
  *     it into on-chip memory, so W_hat^T is never stored and the workspace
  *     holds only the rank-r products (megabytes).
- * Both routes give the same dX bit for bit.  Up to T = 16 without dropout the
- * backward streams the codes once, W_hat existing only in LDS tiles, sums
- * fp32 row-split partials of dX in a fixed order (one rounding) and writes
- * each element of dA and dB once (reproducible); both size functions give
- * the same size there.  Y and dX are reproducible bit for bit.
+ * Both routes give the same dX, dA and dB bit for bit.  Up to T = 16 without
+ * dropout the backward streams the codes once, W_hat existing only in LDS
+ * tiles, sums fp32 row-split partials of dX in a fixed order (one rounding)
+ * and writes each element of dA and dB once; both size functions give the
+ * same size there.  Y, dX, dA and dB are reproducible bit for bit.
  *   dY [T, out] bf16; other arguments as in qlora_linear_fwd;
  *   ws of ws_bytes >= qlora_workspace_bytes_bwd_min(T, in, &out, 1, r, 0, flags)
  * T == 0 writes zeros to dA and dB and nothing else (X, dY, dX may be NULL).
