@@ -77,8 +77,10 @@ hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t
                             const uint16_t* const* P, int nP, int64_t r, float scale, uint16_t* pad,
                             int64_t ldpad, uint16_t* hilo_t, int64_t ldt, int64_t rp, float* part,
                             hipStream_t s, const uint8_t* keep = nullptr, int64_t ldk = 0);
-// out(j, c) = sum_t (Pt[j][t] + Pt[rp + j][t]) Q[t][c] for j < r, c < C (C % 64
-// == 0), laid out as out[j * C + c] (out_jc) or out[c * r + j], as
+// out(j, c) = sum_t (Pt[j'][t] + Pt[rp + j'][t]) Q[t][c] for j < r, c < C (C % 64
+// == 0), laid out as out[j * C + c] (out_jc) or out[c * r + j], where rank j is
+// rank j' = j % rproj of the projection j / rproj of Pt (projections stacked,
+// 2 rp rows each; rproj = r: one projection, j' = j), as
 // lora_grad_slices(T, C, ldq) token-slice sums: slice z written to
 // part[z * r * C ...] (every element once), to be added in order by
 // launch_sum_slices.  (Q rows have stride ldq elements, ldq >= C.)  keep
@@ -87,7 +89,8 @@ hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t
 int64_t lora_grad_slices(int64_t T, int64_t C, int64_t ldq);
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
                             int64_t C, int64_t ldq, int64_t r, float* part, bool out_jc, hipStream_t s,
-                            const uint8_t* keep = nullptr, int64_t ldk = 0, float oscale = 1.f);
+                            const uint8_t* keep = nullptr, int64_t ldk = 0, float oscale = 1.f,
+                            int64_t rproj = 0);
 // dst[c][r] = src[r][c] for src [R][C]
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
                                  hipStream_t s);
@@ -100,10 +103,11 @@ hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
 // count (<= kMaxFill) buffers dst[i] of n[i] floats set to v in one launch
 constexpr int kMaxFill = 2 * kMaxProj;
 hipError_t launch_fill_many_f32(float* const* dst, const int64_t* n, int count, float v, hipStream_t s);
-// out[b][i] = sum over z < slices[b] of part[b][z * n[b] + i], in order, for
-// count (<= kMaxFill) jobs in one launch; n[b] % 4 == 0, 16-byte aligned.
+// out[b][i] = sum over z < slices[b] of part[b][z * stride[b] + i] (stride
+// NULL: n), in order, for count (<= kMaxFill) jobs in one launch; n[b] and
+// stride[b] multiples of 4, 16-byte aligned.
 hipError_t launch_sum_slices(const float* const* part, const int* slices, const int64_t* n, float* const* out,
-                             int count, hipStream_t s);
+                             int count, hipStream_t s, const int64_t* stride = nullptr);
 
 // Split-K of the GEMM launches below: grids of 128 x 128 tiles below one
 // workgroup per CU split K into gemm_splits(M, N, K0) ranges (1: none), each

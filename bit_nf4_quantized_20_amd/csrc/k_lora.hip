@@ -352,7 +352,7 @@ __device__ __forceinline__ int grad_qslot(int c, int w) { return kGradPitch * c 
 template <int JT, bool kJC, bool kMask>
 __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ Pt, int64_t T,
                                                    int64_t ldt, int rp, const uint16_t* __restrict__ Q,
-                                                   int64_t C, int64_t ldq, int r, int j0,
+                                                   int64_t C, int64_t ldq, int r, int j0, int rproj,
                                                    float* __restrict__ part, int64_t TS,
                                                    const uint8_t* __restrict__ keep, int64_t ldk,
                                                    float oscale) {
@@ -373,8 +373,21 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
   const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Q + ts * ldq), 0, static_cast<int>(q_bytes < 0x7fffffffu ? q_bytes : 0x7fffffffu),
       kBufferWord3);
+  // Pt holds ceil(r / rproj) stacked projections of 2 rp rows each
+  const int nproj = (r + rproj - 1) / rproj;
   const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Pt), 0, static_cast<int>(static_cast<uint64_t>(2 * rp) * ldt * 2), kBufferWord3);
+      const_cast<uint16_t*>(Pt), 0, static_cast<int>(static_cast<uint64_t>(nproj) * 2 * rp * ldt * 2),
+      kBufferWord3);
+  // Rank J of the call is rank J % rproj of projection J / rproj, whose hi and
+  // lo rows are i 2rp + J % rproj and i 2rp + rp + J % rproj; ranks past r read zeros.
+  int64_t prow_base[2 * JT];
+#pragma unroll
+  for (int i = 0; i < 2 * JT; ++i) {
+    const int prow = (tid + 256 * i) >> 3;
+    const int J = j0 + (prow < 32 * JT ? prow : prow - 32 * JT);
+    const int pi = J / rproj, jl = J - pi * rproj;
+    prow_base[i] = J < r ? static_cast<int64_t>(pi) * 2 * rp + jl + (prow < 32 * JT ? 0 : rp) : -1;
+  }
 
   // Q staging items: column group cg (8 columns), token pairs tp and tp + 16
   const int cg = tid & 15, tp0 = tid >> 4;
@@ -406,10 +419,10 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < 2 * JT; ++i) {
-      const int id = tid + 256 * i, prow = id >> 3, q = id & 7;
-      const int64_t grow = prow < 32 * JT ? j0 + prow : rp + j0 + (prow - 32 * JT);
+      const int id = tid + 256 * i, q = id & 7;
+      const int64_t grow = prow_base[i];
       const int64_t tk = t0 + 8 * q;  // tokens in [T, ldt) are zero in Pt
-      const uint32_t off = tk < ldt ? static_cast<uint32_t>((grow * ldt + tk) * 2) | pe : kPastEnd;
+      const uint32_t off = (tk < ldt && grow >= 0) ? static_cast<uint32_t>((grow * ldt + tk) * 2) | pe : kPastEnd;
       pv[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_p, off, 0, 0));
     }
   };
@@ -533,9 +546,10 @@ int64_t lora_grad_slices(int64_t T, int64_t C, int64_t ldq) {
 
 hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t rp, const uint16_t* Q,
                             int64_t C, int64_t ldq, int64_t r, float* part, bool out_jc, hipStream_t s,
-                            const uint8_t* keep, int64_t ldk, float oscale) {
+                            const uint8_t* keep, int64_t ldk, float oscale, int64_t rproj) {
   if (T <= 0) return hipSuccess;
-  if (2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // Pt under 2^31 bytes
+  if (rproj <= 0) rproj = r;
+  if (ceil_div(r, rproj) * 2 * rp * ldt * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // Pt under 2^31 bytes
   if (keep != nullptr && T * ldk >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int64_t TS = grad_slice_tokens(T, C, ldq);
   const int64_t slices = ceil_div(T, TS);
@@ -548,7 +562,7 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
     const int ij0 = static_cast<int>(j0);
 #define QLORA_GRAD(JTV, JC, MK)                                                                      \
   hipLaunchKernelGGL((k_lora_grad<JTV, JC, MK>), grid, dim3(256), 0, s, Pt, T, ldt, irp, Q, C, ldq, ir, ij0, \
-                     part, TS, keep, ldk, oscale)
+                     static_cast<int>(rproj), part, TS, keep, ldk, oscale)
     if (keep != nullptr) {  // the masked operand is X: dA, out_jc
       if (jt <= 1) QLORA_GRAD(1, true, true);
       else if (jt <= 2) QLORA_GRAD(2, true, true);
@@ -655,12 +669,13 @@ hipError_t launch_fill_many_f32(float* const* dst, const int64_t* n, int count, 
   return hipGetLastError();
 }
 
-// out_b[i] = sum over z = 0, 1, ... of part_b[z * n_b + i] for each job b, the
-// slices added in order (bit-reproducible); 4 floats per thread, n_b % 4 == 0.
+// out_b[i] = sum over z = 0, 1, ... of part_b[z * stride_b + i] for each job b,
+// the slices added in order (bit-reproducible); 4 floats per thread, n_b % 4 == 0.
 struct SumList {
   const float* part[kMaxFill];
   float* out[kMaxFill];
   int64_t n[kMaxFill];
+  int64_t stride[kMaxFill];  // elements between consecutive slices
   int64_t first[kMaxFill + 1];
   int slices[kMaxFill];
   int count;
@@ -674,12 +689,12 @@ __global__ __launch_bounds__(256) void k_sum_slices(SumList L) {
     if (i < L.count && wg >= L.first[i]) b = i;
   const float* part = L.part[0];
   float* out = L.out[0];
-  int64_t n = L.n[0], first = L.first[0];
+  int64_t n = L.n[0], first = L.first[0], stride = L.stride[0];
   int S = L.slices[0];
 #pragma unroll
   for (int i = 1; i < kMaxFill; ++i)
     if (i == b) {
-      part = L.part[i]; out = L.out[i]; n = L.n[i]; first = L.first[i]; S = L.slices[i];
+      part = L.part[i]; out = L.out[i]; n = L.n[i]; first = L.first[i]; S = L.slices[i]; stride = L.stride[i];
     }
   const int64_t idx = ((wg - first) * 256 + threadIdx.x) * 4;
   if (idx >= n) return;
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(256) void k_sum_slices(SumList L) {
     f32x4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = z0 + u < S ? *reinterpret_cast<const f32x4*>(part + (z0 + u) * n + idx) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[u] = z0 + u < S ? *reinterpret_cast<const f32x4*>(part + (z0 + u) * stride + idx) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (z0 + u < S) acc += v[u];
@@ -698,7 +713,7 @@ __global__ __launch_bounds__(256) void k_sum_slices(SumList L) {
 }
 
 hipError_t launch_sum_slices(const float* const* part, const int* slices, const int64_t* n, float* const* out,
-                             int count, hipStream_t s) {
+                             int count, hipStream_t s, const int64_t* stride) {
   if (count < 1 || count > kMaxFill) return hipErrorInvalidValue;
   SumList L{};
   L.count = count;
@@ -708,6 +723,8 @@ hipError_t launch_sum_slices(const float* const* part, const int* slices, const 
     L.part[i] = part[i];
     L.out[i] = out[i];
     L.n[i] = n[i];
+    L.stride[i] = stride != nullptr ? stride[i] : n[i];
+    if (L.stride[i] % 4 != 0 || L.stride[i] < n[i]) return hipErrorInvalidValue;
     L.slices[i] = slices[i];
     L.first[i] = wgs;
     wgs += ceil_div(n[i], 1024);

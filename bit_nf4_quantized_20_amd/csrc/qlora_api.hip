@@ -115,18 +115,17 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 // whose fp32 block absmax only the standalone dequantize reads)
 bool fwd_expands(int64_t T, bool absmax_fp32) { return absmax_fp32 || T >= kMaterializeTokens; }
 
-// token-slice partial sums of one projection's dA_i [r][in] and dB_i
-// [out_i][r] (general backward; the region is reused for every projection)
+// token-slice partial sums of every dA_i [r][in] (one pass over X for all
+// projections) and of one dB_i [out_i][r] at a time (general backward)
 size_t grad_part_bytes(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r) {
   int64_t N = 0;
   for (int i = 0; i < n; ++i) N += outs[i];
   size_t b = 0;
   for (int i = 0; i < n; ++i) {
-    const size_t bi =
-        static_cast<size_t>(lora_grad_slices(T, in, in) * r * in + lora_grad_slices(T, outs[i], N) * outs[i] * r) * 4;
+    const size_t bi = static_cast<size_t>(lora_grad_slices(T, outs[i], N) * outs[i] * r) * 4;
     b = bi > b ? bi : b;
   }
-  return b;
+  return static_cast<size_t>(lora_grad_slices(T, in, in) * n * r * in) * 4 + b;
 }
 
 // split-K partials of a forward GEMM over n projections: one launch over all
@@ -613,24 +612,40 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
     e = launch_gemm_nt(T, in, dY, N, w_dq_t, N, N, v_pad, n * 2 * rp, a_t_pad, n * 2 * rp, n * 2 * rp,
                        dX, in, s, keep, in / 8, inv_keep, split, split_n);
   }
-  // dA_i and dB_i: token-slice sums into the workspace (one region, reused
-  // projection after projection in stream order), then both outputs written
-  // once with their slices added in order (bit-reproducible)
+  // dA_i and dB_i: token-slice sums into the workspace, then every output
+  // written once with its slices added in order (bit-reproducible).  dA of
+  // every projection comes from one pass over X (the projections' ranks
+  // stacked); dB_i from dY's columns of projection i, its region reused
+  // projection after projection in stream order.
   float* const gp = reinterpret_cast<float*>(base + lay.grad);
+  const int64_t sa = lora_grad_slices(T, in, in);
+  float* const pb = gp + sa * n * r * in;
+  if (e == hipSuccess)
+    e = launch_lora_grad(vt, T, tp, rp, X, in, in, n * r, gp, true, s, keep, in / 8, inv_keep, r);  // dA
   off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
-    const int64_t sa = lora_grad_slices(T, in, in), sb = lora_grad_slices(T, outs[i], N);
-    float* const pb = gp + sa * r * in;
-    e = launch_lora_grad(vt + i * 2 * rp * tp, T, tp, rp, X, in, in, r, gp, true, s, keep, in / 8,
-                         inv_keep);  // dA_i
-    if (e == hipSuccess)
-      e = launch_lora_grad(ut + i * 2 * rp * tp, T, tp, rp, dY + off, outs[i], N, r, pb, false, s);  // dB_i
+    const int64_t sb = lora_grad_slices(T, outs[i], N);
+    e = launch_lora_grad(ut + i * 2 * rp * tp, T, tp, rp, dY + off, outs[i], N, r, pb, false, s);  // dB_i
     if (e == hipSuccess) {
-      const float* part[2] = {gp, pb};
-      const int slices[2] = {static_cast<int>(sa), static_cast<int>(sb)};
-      const int64_t cnt[2] = {r * in, outs[i] * r};
-      float* outp[2] = {dA[i], dB[i]};
-      e = launch_sum_slices(part, slices, cnt, outp, 2, s);
+      const float* part[kMaxFill];
+      int slices[kMaxFill];
+      int64_t cnt[kMaxFill], stride[kMaxFill];
+      float* outp[kMaxFill];
+      part[0] = pb;
+      slices[0] = static_cast<int>(sb);
+      cnt[0] = stride[0] = outs[i] * r;
+      outp[0] = dB[i];
+      int jobs = 1;
+      if (i == n - 1) {  // with the last dB, every dA
+        for (int j = 0; j < n; ++j, ++jobs) {
+          part[jobs] = gp + j * r * in;
+          slices[jobs] = static_cast<int>(sa);
+          cnt[jobs] = r * in;
+          stride[jobs] = n * r * in;
+          outp[jobs] = dA[j];
+        }
+      }
+      e = launch_sum_slices(part, slices, cnt, outp, jobs, s, stride);
     }
     off += outs[i];
   }

@@ -283,7 +283,7 @@ def test_backward_minimum_workspace():
         weight = 2 * n_in * sum(o)
         for T in (17, 300, 4096):
             assert full(T, n_in, o) - mn(T, n_in, o) == weight, (n_in, o, T)
-            assert mn(T, n_in, o) < (weight // 2 if len(o) == 1 else weight)
+            assert mn(T, n_in, o) < (weight // 2 if len(o) == 1 else full(T, n_in, o))
             assert mn(T, n_in, o, flags=1) == full(T, n_in, o, flags=1)     # 4.5-bit: always expanded
         if len(o) == 1:
             assert full(64, n_in, o, drop=1) - mn(64, n_in, o, drop=1) == weight
