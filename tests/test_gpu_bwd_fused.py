@@ -8,14 +8,16 @@ Checks:
 - against the fp64 oracle (relative Frobenius <= 2e-3 for dX, dA, dB) at
   small ragged shapes, full tensors;
 - against the expanded route on the same inputs: dX bit for bit (both routes
-  feed the same bf16 W_hat values to the same MFMA sequence), dA and dB up to
-  bit for bit too, at shapes that run every kernel form (the
-  128 x 128 kernel with a partial column tile, the 256-column kernel with 128-
-  and 256-row tiles), several projections, and dropout;
+  feed the same bf16 W_hat values to the same MFMA sequence), dA and dB bit for
+  bit too (token-slice sums added in a fixed order), at shapes that run every
+  kernel form (the 128 x 128 kernel with a partial column tile, the 256-column
+  kernel with 128- and 256-row tiles), several projections, and dropout;
 - one-hot dY rows select rows of W_hat bit for bit through the fused route;
 - split-K (grids below one workgroup per CU, forward and backward, both
   routes): oracle parity, repeated calls bit for bit, one-hot pins, several
-  projections, dropout."""
+  projections, dropout;
+- dA and dB repeated bit for bit, and the large-token forward / backward
+  replayed from a captured graph bit for bit."""
 
 import numpy as np
 import pytest
@@ -299,3 +301,53 @@ def test_gradients_reproducible_with_dropout():
     a2 = [host(t) for t in q.qlora_linear_bwd_dropout(*args)[1:]]
     for a, b in zip(a1, a2):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_large_token_paths_under_graph_replay():
+    # A captured graph replays forwards and backwards that use the split-K
+    # partials, the fused dX route and the gradients' slice sums (every launch a
+    # kernel, no memory-set nodes), sharing workspaces with eager calls made
+    # between the replays; every replay must equal the eager results bit for bit.
+    q = require_gpu()
+    banner("graph replay of the large-token forward / backward")
+    n_out, n_in, r, alpha = 4096, 4096, 16, 32.0
+    (w,), (A,), (B,), X, dY = _inputs(2200, 300, n_in, [n_out], r)
+    W = q.nf4_quantize_weight(dev_f32(w))
+    Ad, Bd = dev_bf16(A), dev_bf16(B)
+    Xs = {T: dev_bf16(X[:T]) for T in (64, 300)}
+    dYs = {T: dev_bf16(dY[:T]) for T in (64, 300)}
+    wsf = q.make_workspace(max(q.qlora_workspace_bytes(T, n_in, n_out, r, False) for T in (64, 300)), "cuda")
+    wsb = q.make_workspace(max(q.qlora_workspace_bytes(T, n_in, n_out, r, True) for T in (64, 300)), "cuda")
+    wsm = q.make_workspace(max(q.qlora_workspace_bytes_bwd_min(T, n_in, [n_out], r) for T in (64, 300)), "cuda")
+    calls = []  # (outputs, launcher)
+    for T in (64, 300):
+        Y = torch.empty(T, n_out, dtype=torch.bfloat16, device="cuda")
+        calls.append(([Y], lambda T=T, Y=Y: q.qlora_linear_fwd(W, Xs[T], Ad, Bd, r, alpha, Y=Y, ws=wsf)))
+        for ws in (wsb, wsm):
+            o = [torch.empty(T, n_in, dtype=torch.bfloat16, device="cuda"),
+                 torch.empty(r, n_in, dtype=torch.float32, device="cuda"),
+                 torch.empty(n_out, r, dtype=torch.float32, device="cuda")]
+            calls.append((o, lambda T=T, o=o, ws=ws: q.qlora_linear_bwd(W, Xs[T], dYs[T], Ad, Bd, r, alpha, *o, ws=ws)))
+    bits = lambda t: host(t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)).copy()
+    eager = []
+    for o, f in calls:
+        f()
+        eager.append([bits(t) for t in o])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, f in calls:
+            f()
+    for rep in range(3):
+        for o, _ in calls:
+            for t in o:
+                t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (o, _) in enumerate(calls):
+            for t, ref in zip(o, eager[k]):
+                assert np.array_equal(bits(t), ref), (rep, k)
+        calls[2][1]()  # eager work on the shared workspaces between replays
+        calls[4][1]()
+        torch.cuda.synchronize()
