@@ -104,6 +104,8 @@ def test_fused_route_matches_oracle(T, n_in, outs, r, alpha):
     (1024, 8192, [1024], 16, 32.0),            # 128 x 256 tiles (8 x 32 of them)
     (4096, 4096, [4096, 1024, 1024], 16, 32.0),  # 8B q|k|v: 256 x 256 tiles over three projections
     (8192, 4096, [1024], 16, 32.0),            # 8B attention k: 32 x 16 tiles, K = 1024
+    (4096, 8192, [28672], 64, 16.0),           # 70B MLP gate: K = 28672
+    (4096, 28672, [8192], 64, 16.0),           # 70B MLP down: 16 x 112 tiles
 ])
 def test_fused_route_equals_expanded_route(T, n_in, outs, r, alpha):
     q = require_gpu()
