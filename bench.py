@@ -653,8 +653,9 @@ def train_leg(q, synth, dev, bf, plain):
     14336 -> 4096; T = 4096, r = 64, alpha = 128), next to its plain figures
     `plain` (large_step_leg): every projection with LoRA dropout p = 0.05;
     gate and up as one multi-projection call each way; and the forward of
-    gate|up at T = 1792, where the dequantization stays inside the GEMM's LDS
-    staging.  Each call is warmed up, then timed over 20 calls."""
+    gate|up at T = 1792 through both routes (dequantization inside the GEMM's
+    LDS staging with the smallest workspace, the weight expanded first with
+    the full one).  Each call is warmed up, then timed over 20 calls."""
     import torch
     wl = synth.WORKLOADS[3]
     T, r, alpha = wl.tokens[0], wl.r, wl.alpha
@@ -752,24 +753,28 @@ def train_leg(q, synth, dev, bf, plain):
     res["mlp_fused_fwd_bwd_TFLOPs"] = round(tf2, 1)
     res["mlp_fused_frac_of_bf16_peak"] = round(tf2 / BF16_PEAK_TFLOPS, 4)
 
-    # below 2048 tokens the forward keeps the dequantization inside the GEMM's
-    # LDS staging (W_hat never written): gate and up at T = 1792 (7 x 112 tiles)
+    # gate and up at T = 1792 (7 x 112 tiles): with the smallest forward
+    # workspace the GEMM dequantizes the weight inside its LDS staging (W_hat
+    # never written); with the full one (the default) it expands W_hat first
     Tf = 1792
     Xf = X[:Tf].contiguous()
     Yf = torch.empty(Tf, N, dtype=torch.bfloat16, device=dev)
-    wsff = q.make_workspace(q.qlora_workspace_bytes_multi(Tf, n_in, outs, r, False), dev)
-
-    def fwdf():
-        q.qlora_linear_fwd_multi(Ws, Xf, As, Bs, r, alpha, Y=Yf, ws=wsff)
-
-    for _ in range(4):
-        fwdf()
-    ms_ff = timed(fwdf, 20)
     flop_ff = 2 * Tf * n_in * N + 2 * Tf * r * (2 * n_in + N)
-    tff = flop_ff / (ms_ff * 1e-3) / 1e12
-    res["gate_up_fused_nf4_fwd_T1792"] = {"fwd_ms": round(ms_ff, 3), "fwd_TFLOPs": round(tff, 1),
-                                          "frac_of_bf16_peak": round(tff / BF16_PEAK_TFLOPS, 4)}
-    del Ws, X, dY, Y, dX, wsf, wsb, wsff
+    for key, need in (("gate_up_fused_nf4_fwd_T1792", q.qlora_workspace_bytes_fwd_min(Tf, n_in, outs, r)),
+                      ("gate_up_expanded_fwd_T1792", q.qlora_workspace_bytes_multi(Tf, n_in, outs, r, False))):
+        wsff = q.make_workspace(need, dev)
+
+        def fwdf():
+            q.qlora_linear_fwd_multi(Ws, Xf, As, Bs, r, alpha, Y=Yf, ws=wsff)
+
+        for _ in range(4):
+            fwdf()
+        ms_ff = timed(fwdf, 20)
+        tff = flop_ff / (ms_ff * 1e-3) / 1e12
+        res[key] = {"fwd_ms": round(ms_ff, 3), "fwd_TFLOPs": round(tff, 1),
+                    "frac_of_bf16_peak": round(tff / BF16_PEAK_TFLOPS, 4), "workspace_bytes": int(need)}
+        del wsff
+    del Ws, X, dY, Y, dX, wsf, wsb
     torch.cuda.empty_cache()
     return res
 

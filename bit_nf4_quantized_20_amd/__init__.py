@@ -100,6 +100,9 @@ _lib.qlora_workspace_bytes_flags.restype = _sz
 _lib.qlora_workspace_bytes_bwd_min.argtypes = [_i64, _i64, ctypes.POINTER(_i64), ctypes.c_int, _i64,
                                                 ctypes.c_int, ctypes.c_uint32]
 _lib.qlora_workspace_bytes_bwd_min.restype = _sz
+_lib.qlora_workspace_bytes_fwd_min.argtypes = [_i64, _i64, ctypes.POINTER(_i64), ctypes.c_int, _i64,
+                                                ctypes.c_int, ctypes.c_uint32]
+_lib.qlora_workspace_bytes_fwd_min.restype = _sz
 _lib.nf4_code_buckets.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_uint32)]
 _lib.nf4_code_buckets.restype = None
 _lib.qlora_noalloc_scratch_bytes.argtypes = []
@@ -260,6 +263,15 @@ def qlora_workspace_bytes_flags(T: int, in_features: int, out_features, r: int, 
     outs = (_i64 * len(out_features))(*[int(o) for o in out_features])
     return int(_lib.qlora_workspace_bytes_flags(T, in_features, outs, len(out_features), r,
                                                 1 if backward else 0, 1 if dropout else 0, flags))
+
+
+def qlora_workspace_bytes_fwd_min(T: int, in_features: int, out_features, r: int, dropout: bool = False,
+                                  flags: int = 0) -> int:
+    """The smallest forward workspace: no expanded W_hat (the GEMM then
+    dequantizes the weight tiles while staging them)."""
+    outs = (_i64 * len(out_features))(*[int(o) for o in out_features])
+    return int(_lib.qlora_workspace_bytes_fwd_min(T, in_features, outs, len(out_features), r,
+                                                  1 if dropout else 0, flags))
 
 
 def qlora_workspace_bytes_bwd_min(T: int, in_features: int, out_features, r: int, dropout: bool = False,

@@ -83,10 +83,13 @@ struct FwdLayout {
 };
 
 // From this many tokens on, the forward dequantizes each weight once into the
-// workspace and runs the bf16 GEMM: the fused kernel repeats the
-// dequantization for every 256-token tile (16 times at T = 4096), which
-// costs more than one extra pass of 2.5 bytes per weight.
-constexpr int64_t kMaterializeTokens = 2048;
+// workspace and runs the bf16 GEMM when the workspace holds the expanded
+// weight: the fused kernel repeats the dequantization for every token tile,
+// which from here on costs more than one extra pass of 2.5 bytes per weight
+// (same-box A/B: 8B gate / down / q_proj / k shapes at 512-1792 tokens, the
+// expanded route 0.74-1.01x the fused one's time).  With a smaller workspace
+// (at least qlora_workspace_bytes_fwd_min) the fused kernel runs at every T.
+constexpr int64_t kMaterializeTokens = 512;
 struct BwdLayout {
   size_t ut, vt, v_pad, b_t, a_t_pad, w_dq_t, part, grad, uvp, suv, split, total;
 };
@@ -111,8 +114,9 @@ bool fwd_uses_decode(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
 // dropout: the small-token kernel has no mask, so that call always takes the
 // general path
 // expanded: the forward dequantizes W_hat into the workspace and runs the
-// bf16 GEMM (from kMaterializeTokens on, and always for the 4.5-bit format,
-// whose fp32 block absmax only the standalone dequantize reads)
+// bf16 GEMM (from kMaterializeTokens on when the workspace holds W_hat, and
+// always for the 4.5-bit format, whose fp32 block absmax only the standalone
+// dequantize reads)
 bool fwd_expands(int64_t T, bool absmax_fp32) { return absmax_fp32 || T >= kMaterializeTokens; }
 
 // token-slice partial sums of every dA_i [r][in] (one pass over X for all
@@ -139,8 +143,10 @@ size_t split_bytes(int64_t T, int64_t N, int64_t in, const int64_t* outs, int n)
   return b;
 }
 
+// expand = false: the layout without W_hat (the fused GEMM's), for the
+// double-quantized format
 FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t r, bool dropout,
-                     bool absmax_fp32 = false) {
+                     bool absmax_fp32 = false, bool expand = true) {
   FwdLayout l{0, 0, 0, 0, 0, 0};
   Carve c;
   if (!dropout && !absmax_fp32 && fwd_uses_decode(T, in, outs, n, r)) {
@@ -152,7 +158,8 @@ FwdLayout fwd_layout(int64_t T, int64_t in, const int64_t* outs, int n, int64_t 
   l.u_pad = c.take(static_cast<size_t>(T * n * rp * 4));  // [T][n 2rp] bf16
   l.b_pad = c.take(static_cast<size_t>(N * n * rp * 4));  // [N][2rp] or [N][n 2rp] bf16
   l.part = c.take(lora_down_part_bytes(T, in, n * rp));
-  if (fwd_expands(T, absmax_fp32)) l.w_dq = c.take(static_cast<size_t>(N * in * 2));  // [N][in] bf16
+  if (fwd_expands(T, absmax_fp32) && (expand || absmax_fp32))
+    l.w_dq = c.take(static_cast<size_t>(N * in * 2));  // [N][in] bf16
   l.split = c.take(split_bytes(T, N, in, outs, n));  // split-K partials of the GEMM
   l.total = c.off;
   return l;
@@ -341,6 +348,18 @@ size_t qlora_workspace_bytes_flags(int64_t T, int64_t in_features, const int64_t
   return need > kMinWorkspace ? need : kMinWorkspace;
 }
 
+size_t qlora_workspace_bytes_fwd_min(int64_t T, int64_t in_features, const int64_t* out_features, int n,
+                                     int64_t r, int dropout, uint32_t flags) {
+  if ((flags & ~QLORA_NF4_FLAGS_KNOWN) != 0) return 0;
+  if (n < 1 || n > kMaxProj || out_features == nullptr || (dropout && n != 1)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!linear_shapes_ok(T, in_features, out_features[i], r)) return 0;
+  if (!operands_fit(T, in_features, total_out(out_features, n))) return 0;
+  const bool fp32 = (flags & QLORA_NF4_ABSMAX_FP32) != 0;
+  const size_t need = fwd_layout(T, in_features, out_features, n, r, dropout != 0, fp32, false).total;
+  return need > kMinWorkspace ? need : kMinWorkspace;
+}
+
 size_t qlora_workspace_bytes_bwd_min(int64_t T, int64_t in_features, const int64_t* out_features, int n,
                                      int64_t r, int dropout, uint32_t flags) {
   if ((flags & ~QLORA_NF4_FLAGS_KNOWN) != 0) return 0;
@@ -416,7 +435,11 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   if (int st = check_dropout(keep, p)) return st;
   if (T == 0) return QLORA_OK;
   const bool fp32 = absmax_fp32(W[0]);
-  const FwdLayout lay = fwd_layout(T, in, outs, n, r, dropout, fp32);
+  // the expanded route when the workspace holds W_hat, else the fused GEMM
+  const FwdLayout full = fwd_layout(T, in, outs, n, r, dropout, fp32, true);
+  const FwdLayout least = fwd_layout(T, in, outs, n, r, dropout, fp32, false);
+  const bool expand = fwd_expands(T, fp32) && ws != nullptr && ws_bytes >= full.total;
+  const FwdLayout lay = expand ? full : least;
   // The small-token forward also runs without a workspace where U need not
   // be computed up front (r <= 16, at most 4096 output rows): ws = NULL
   // selects its single-launch form.
@@ -449,7 +472,7 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
   const float uscale = dropout ? scale / (1.f - p) : scale;
   hipError_t e = launch_lora_down(X, in, T, in, A, n, r, uscale, u_pad, n * 2 * rp, nullptr, 0, rp, part, s,
                                   keep, in / 8);
-  if (fwd_expands(T, fp32)) {
+  if (expand) {
     // W_hat of every projection into [N][in] bf16, then the bf16 GEMM.  The
     // LoRA term runs as extra K-steps: when no tile straddles two projections
     // each tile reads its own projection's sU_i against B_i (stacked [N][2rp]);
@@ -669,7 +692,7 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const qlora_bf16* X, int
   // the size check comes first, before any HIP call: a call whose workspace
   // would not fit in the library's scratch is refused without side effects
   if (W == nullptr) return QLORA_ERR_NULL;
-  const size_t need = qlora_workspace_bytes_flags(T, W->cols, &W->rows, 1, r, 0, 0, W->flags);
+  const size_t need = qlora_workspace_bytes_fwd_min(T, W->cols, &W->rows, 1, r, 0, W->flags);
   if (need == 0) return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, nullptr, 0, stream);  // shape error
   if (need > kNoAllocScratchBytes) return QLORA_ERR_WORKSPACE;
   if (T == 0) return linear_fwd_impl(W, 1, X, T, &A, &B, r, alpha, Y, nullptr, 0, stream);

@@ -169,9 +169,9 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  *
  * The workspace is scratch for intermediate products (padded LoRA factors,
  * the transposed dequantized weight of the backward from T = 17 on or with
- * dropout, and, from T = 2048 on, the forward's dequantized weight: 2 * out
- * * in bytes each; the backward also runs without that weight in the
- * smaller workspace of qlora_workspace_bytes_bwd_min).  Up to T = 16 without dropout the backward keeps no
+ * dropout, and, from T = 512 on, the forward's dequantized weight: 2 * out
+ * * in bytes each; both also run without that weight in the smaller
+ * workspaces of qlora_workspace_bytes_fwd_min / _bwd_min).  Up to T = 16 without dropout the backward keeps no
  * dequantized weight: it holds fp32 row-split partials of dX
  * (splits * T * in * 4 bytes, splits <= ceil(512 / (in / 64))) and the
  * rank-r reductions' partials (T * r * 4 bytes per 128 columns / rows).  It needs no
@@ -213,20 +213,34 @@ size_t qlora_workspace_bytes_bwd_min(int64_t T, int64_t in_features, const int64
                                      int64_t r, int dropout, uint32_t flags);
 
 /*
+ * The smallest workspace a forward call accepts (single, multi or dropout
+ * form; arguments as in qlora_workspace_bytes_flags with backward = 0): the
+ * layout without the expanded W_hat, where the GEMM dequantizes each weight
+ * tile while it stages it.  Equal to the full size where no such route exists
+ * (below 512 tokens, where the forward never expands W_hat; the 4.5-bit
+ * format, which always expands it).  Returns 0 for invalid arguments.  Host
+ * only.
+ */
+size_t qlora_workspace_bytes_fwd_min(int64_t T, int64_t in_features, const int64_t* out_features, int n,
+                                     int64_t r, int dropout, uint32_t flags);
+
+/*
  * qlora_linear_fwd -- F1 + F2: Y = X W_hat^T + (alpha/r) (X A^T) B^T.
  * paperclase "QLoRA", Parte 4, h = W_hat x + (alpha/r) B A x, with
  * W_hat = dq(codes, absmax) as nf4_dequantize defines it.  Where W_hat lives
- * depends on T: up to 16 tokens it is rebuilt in registers right before the
- * matrix cores use it; from 17 to 2047 tokens it is rebuilt while the
- * weight tile is staged into on-chip memory; from 2048 tokens on it is
- * expanded once into the workspace (2 * out * in bytes) and read back by the
- * GEMM.  bf16 inputs, fp32 accumulation, one rounding of Y to bf16 at the
- * end.
+ * depends on T and the workspace: up to 16 tokens it is rebuilt in registers
+ * right before the matrix cores use it; from 17 to 511 tokens it is rebuilt
+ * while each weight tile is staged into on-chip memory; from 512 tokens on it
+ * is expanded once into the workspace (2 * out * in bytes) and read back by
+ * the GEMM when ws_bytes >= qlora_workspace_bytes(T, in, out, r, 0) (the
+ * faster route there), and otherwise rebuilt in the staging as below 512
+ * (any ws_bytes >= qlora_workspace_bytes_fwd_min; Y is the same bit for bit).
+ * bf16 inputs, fp32 accumulation, one rounding of Y to bf16 at the end.
  *   W   NF4 weight [out, in]; in % 64 == 0, out % 64 == 0
  *   X   [T, in] bf16;  T >= 0 (0 is a no-op; X and Y may then be NULL)
  *   A   [r, in] bf16;  B [out, r] bf16;  1 <= r <= 256;  alpha finite
  *   Y   [T, out] bf16 out
- *   ws  workspace of ws_bytes >= qlora_workspace_bytes(T, in, out, r, 0)
+ *   ws  workspace of ws_bytes >= qlora_workspace_bytes_fwd_min(T, in, &out, 1, r, 0, flags)
  * Size limit (all linear calls, also multi / dropout / merge): X, Y, dY, dX
  * and the dequantized weight [out, in] in bf16 must each be smaller than
  * 2^31 bytes (QLORA_ERR_SHAPE otherwise); larger token batches are split
@@ -244,12 +258,14 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const qlora_bf16* X, int64_t T,
  * without a workspace.  It uses the library's own scratch instead: a static
  * device array of qlora_noalloc_scratch_bytes() bytes (16 MiB), one copy per
  * GPU, held until the process ends; the call itself allocates nothing.
- *   Calls whose workspace (qlora_workspace_bytes(T, in, out, r, 0)) exceeds
- *   the scratch are refused with QLORA_ERR_WORKSPACE before any HIP call.
- *   The small-token path (T <= 16) needs at most T x r x 4 bytes and always
- *   fits; from 2048 tokens on the workspace also holds the dequantized
- *   weight (2 bytes per weight), so weights above about 8 M elements do not
- *   fit there: such calls take qlora_linear_fwd with a caller workspace.
+ *   The call takes the route the scratch holds: from 512 tokens on W_hat is
+ *   expanded into it when the whole layout fits, else each weight tile is
+ *   dequantized in the GEMM's staging (as qlora_linear_fwd with a smaller
+ *   workspace; Y is the same bit for bit).  Calls whose smallest workspace
+ *   (qlora_workspace_bytes_fwd_min) exceeds the scratch -- very large
+ *   token counts or ranks -- are refused with QLORA_ERR_WORKSPACE before any
+ *   HIP call.  The small-token path (T <= 16) needs at most T x r x 4 bytes
+ *   and always fits.
  *   Every call on one GPU shares that GPU's scratch (it needs no
  *   initialisation and keeps nothing between calls): calls that overlap in
  *   time on one GPU (different streams, or different host threads without

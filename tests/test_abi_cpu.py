@@ -301,6 +301,42 @@ def test_backward_minimum_workspace():
     assert bwd(full(300, 256, [128], r=8)) == -6
 
 
+def test_forward_minimum_workspace():
+    # qlora_workspace_bytes_fwd_min: the forward's layout without the expanded
+    # W_hat (its GEMM then dequantizes the weight tiles while staging them);
+    # from 512 tokens on exactly the expanded weight's bytes below the full
+    # size, equal to it below 512 tokens and for the 4.5-bit format
+    lib = _api(_lib())
+    i64, sz, F = ctypes.c_int64, ctypes.c_size_t, _FAKE
+    lib.qlora_workspace_bytes_fwd_min.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64,
+                                                  ctypes.c_int, ctypes.c_uint32]
+    lib.qlora_workspace_bytes_fwd_min.restype = sz
+    lib.qlora_workspace_bytes_flags.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.c_int, i64, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_uint32]
+    lib.qlora_workspace_bytes_flags.restype = sz
+    outs = lambda *o: (i64 * len(o))(*o)
+    mn = lambda T, n_in, o, r=16, drop=0, flags=0: lib.qlora_workspace_bytes_fwd_min(
+        T, n_in, outs(*o), len(o), r, drop, flags)
+    full = lambda T, n_in, o, r=16, drop=0, flags=0: lib.qlora_workspace_bytes_flags(
+        T, n_in, outs(*o), len(o), r, 0, drop, flags)
+    for n_in, o in ((4096, [14336]), (14336, [4096]), (4096, [4096, 1024, 1024])):
+        weight = 2 * n_in * sum(o)
+        for T in (512, 2048, 4096):
+            assert full(T, n_in, o) - mn(T, n_in, o) == weight, (n_in, o, T)
+            assert mn(T, n_in, o, flags=1) == full(T, n_in, o, flags=1)
+        for T in (1, 16, 17, 300, 511):
+            assert mn(T, n_in, o) == full(T, n_in, o)
+        if len(o) == 1:
+            assert full(1024, n_in, o, drop=1) - mn(1024, n_in, o, drop=1) == weight
+    assert mn(17, 100, [128]) == 0 and mn(17, 256, [128], flags=2) == 0 and mn(17, 256, [128, 64], drop=1) == 0
+    # the call accepts the minimum and refuses one byte less (before any HIP call)
+    W = _W(F, F, F, 128, 256)
+    least = mn(600, 256, [128], r=8)
+    fwd = lambda wsb: lib.qlora_linear_fwd(ctypes.byref(W), F, 600, F, F, 8, 16.0, F, F, wsb, None)
+    assert fwd(least - 1) == -4
+    assert fwd(least) == -6 and fwd(full(600, 256, [128], r=8)) == -6   # valid: fail at the device check
+
+
 def test_format_flags():
     # qlora_nf4_weight.flags: 0 = double-quantized, 1 = the 4.5-bit format
     # (fp32 block absmax in absmax_scale, absmax_q unused); other bits reserved

@@ -353,3 +353,26 @@ def test_large_token_paths_under_graph_replay():
         calls[2][1]()  # eager work on the shared workspaces between replays
         calls[4][1]()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,n_in,outs,r", [
+    (1536, 4096, [14336], 64),             # 6 x 56 tiles of 256
+    (4096, 14336, [4096], 64),             # 8B down, K = 14336
+    (4096, 4096, [4096, 1024, 1024], 16),  # q|k|v stacked in one launch
+    (600, 1024, [4160, 4032], 8),          # 128 x 128 tiles, one launch per projection, split-K
+])
+def test_forward_routes_equal(T, n_in, outs, r):
+    # from 512 tokens on the forward expands W_hat when the workspace holds it
+    # and dequantizes in the GEMM's staging otherwise: same bf16 W_hat, same
+    # MFMA sequence, so Y is the same bit for bit
+    q = require_gpu()
+    banner(f"forward routes T={T} in={n_in} outs={outs} r={r}")
+    ws, As, Bs, X, _ = _inputs(2300 + T % 83, T, n_in, outs, r)
+    Ws = [q.nf4_quantize_weight(dev_f32(w)) for w in ws]
+    args = (Ws, dev_bf16(X), [dev_bf16(a) for a in As], [dev_bf16(b) for b in Bs], r, 2.0 * r)
+    need = q.qlora_workspace_bytes_fwd_min(T, n_in, outs, r)
+    full = q.qlora_workspace_bytes_multi(T, n_in, outs, r, False)
+    assert 0 < need < full and full - need >= sum(outs) * n_in * 2
+    Yf = host_bits(q.qlora_linear_fwd_multi(*args, ws=q.make_workspace(need, "cuda")))
+    Ye = host_bits(q.qlora_linear_fwd_multi(*args, ws=q.make_workspace(full, "cuda")))
+    assert np.array_equal(Yf, Ye)

@@ -13,8 +13,9 @@ dX, dA and dB in fp64 (every output element of every call).  Acceptance:
 relative Frobenius error <= 2e-3 for each of Y, dX, dA and dB.
 
 Also here: bit-exact one-hot pins through the paths that only run at large
-token counts (the forward's weight expansion from 2048 tokens on, and the
-large-tile GEMMs of both directions)."""
+token counts (the forward's weight expansion from 512 tokens on, the fused
+NF4 GEMM given the smallest forward workspace, and the large-tile GEMMs of
+both directions)."""
 
 import numpy as np
 import pytest
@@ -42,7 +43,7 @@ def _case(wid, proj, T=None):
     return w, X, dY, A, B, r, alpha
 
 
-def _check(wid, proj, T=None):
+def _check(wid, proj, T=None, fwd_min_ws=False):
     q = require_gpu()
     w, X, dY, A, B, r, alpha = _case(wid, proj, T)
     T = X.shape[0]
@@ -51,7 +52,8 @@ def _check(wid, proj, T=None):
 
     W = q.nf4_quantize_weight(dev_f32(w))
     Xd, dYd, Ad, Bd = dev_bf16(X), dev_bf16(dY), dev_bf16(A), dev_bf16(B)
-    Y = q.qlora_linear_fwd(W, Xd, Ad, Bd, r, alpha)
+    wsf = q.make_workspace(q.qlora_workspace_bytes_fwd_min(T, n_in, [n_out], r), "cuda") if fwd_min_ws else None
+    Y = q.qlora_linear_fwd(W, Xd, Ad, Bd, r, alpha, ws=wsf)
     dX, dA, dB = q.qlora_linear_bwd(W, Xd, dYd, Ad, Bd, r, alpha)
     Yh = onf4.bf16_bits_to_f32(host_bits(Y)).astype(np.float64)
     dXh = onf4.bf16_bits_to_f32(host_bits(dX)).astype(np.float64)
@@ -101,11 +103,11 @@ def test_ragged_tokens_on_large_tiles():
     _check(4, 0, T=4136)
 
 
-def test_fused_dequant_gemm_below_materialize_threshold():
-    # 8B MLP gate at T = 1536 (6 x 56 tiles of 256): the forward takes the fused
-    # NF4 GEMM (codes dequantized while staged into LDS); from T = 2048 on it
-    # dequantizes the weight once into the workspace instead
-    _check(3, 0, T=1536)
+def test_fused_dequant_gemm_in_the_smallest_workspace():
+    # 8B MLP gate at T = 1536 (6 x 56 tiles of 256) with the smallest forward
+    # workspace: the forward takes the fused NF4 GEMM (codes dequantized while
+    # staged into LDS) instead of expanding the weight
+    _check(3, 0, T=1536, fwd_min_ws=True)
 
 
 # ------------------------------------------------------------ one-hot pins
@@ -119,7 +121,7 @@ def _one_hot(n, idx):
 @pytest.mark.parametrize("T,n_out,n_in", [
     (2048, 512, 320),    # weight expanded once into the workspace, 128 x 128 tiles
     (2048, 8192, 512),   # the same on 256 x 256 tiles (8 x 32 = 256 tiles)
-    (1792, 8192, 512),   # the fused NF4 GEMM on 256 x 256 tiles (7 x 32 tiles)
+    (1792, 8192, 512),   # 7 x 32 tiles of 256; with the smallest workspace the fused NF4 GEMM on 14 x 32 of 128 x 256
     (2048, 512, 8192),   # the expanded-weight dX GEMM on 256 x 256 tiles (8 x 32)
     (1024, 512, 8192),   # the same on 128 x 256 tiles (8 x 32)
 ])
@@ -147,3 +149,7 @@ def test_one_hot_large_token_paths_bit_exact(T, n_out, n_in):
     assert np.array_equal(host_bits(Y), w_hat[:, xi].T)
     assert np.array_equal(host_bits(dX), w_hat[gi, :])
     assert np.all(host(dB) == 0)  # U = X A^T = 0
+    # the forward in its smallest workspace (the fused NF4 GEMM from 512 tokens on)
+    wsm = q.make_workspace(q.qlora_workspace_bytes_fwd_min(T, n_in, [n_out], r), "cuda")
+    Ym = q.qlora_linear_fwd(W, dev_bf16(X), dev_bf16(A), dev_bf16(np.zeros_like(B)), r, alpha, ws=wsm)
+    assert np.array_equal(host_bits(Ym), w_hat[:, xi].T)
