@@ -167,20 +167,22 @@ int nf4_dequantize_nodq(const uint8_t* codes, const float* absmax, int64_t numel
  * qlora_linear_bwd (backward = 1) for T tokens, in/out features and rank r.
  * Returns 0 for invalid shapes and at least 256 otherwise.  Host only.
  *
- * The workspace is scratch for intermediate products (padded LoRA factors,
- * the transposed dequantized weight of the backward from T = 17 on or with
- * dropout, and, from T = 512 on, the forward's dequantized weight: 2 * out
- * * in bytes each; both also run without that weight in the smaller
- * workspaces of qlora_workspace_bytes_fwd_min / _bwd_min).  Up to T = 16 without dropout the backward keeps no
- * dequantized weight: it holds fp32 row-split partials of dX
- * (splits * T * in * 4 bytes, splits <= ceil(512 / (in / 64))) and the
- * rank-r reductions' partials (T * r * 4 bytes per 128 columns / rows).  It needs no
- * initialisation and keeps nothing between calls.  The small-token forward
- * (T <= 16 and r <= 64) uses it only for U = X A^T (n * T * r fp32 values),
- * computed once up front when r > 16 or the projections have more than 4096
- * output rows together; with r <= 16 and at most 4096 rows ws may be NULL.
- * Calls that
- * overlap in time (different streams) must not share a workspace.
+ * The workspace is scratch for intermediate products: padded LoRA factors,
+ * fp32 partial sums (the rank-r reductions, the token slices of dA and dB,
+ * and, below one workgroup per CU, the split-K ranges of a GEMM: at most
+ * 32 MiB), the transposed dequantized weight of the backward from T = 17 on
+ * or with dropout, and, from T = 512 on, the forward's dequantized weight
+ * (2 * out * in bytes each; both calls also run without that weight in the
+ * smaller workspaces of qlora_workspace_bytes_fwd_min / _bwd_min).  Up to
+ * T = 16 without dropout the backward keeps no dequantized weight: it holds
+ * fp32 row-split partials of dX (splits * T * in * 4 bytes, splits <=
+ * ceil(512 / (in / 64))) and the rank-r reductions' partials (T * r * 4 bytes
+ * per 128 columns / rows).  It needs no initialisation and keeps nothing
+ * between calls.  The small-token forward (T <= 16 and r <= 64) uses it only
+ * for U = X A^T (n * T * r fp32 values), computed once up front when r > 16
+ * or the projections have more than 4096 output rows together; with r <= 16
+ * and at most 4096 rows ws may be NULL.  Calls that overlap in time
+ * (different streams) must not share a workspace.
  */
 size_t qlora_workspace_bytes(int64_t T, int64_t in_features, int64_t out_features, int64_t r,
                              int backward);
