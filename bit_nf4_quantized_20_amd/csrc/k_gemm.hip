@@ -33,7 +33,12 @@
 //
 // k_gemm (smaller grids): 128 x 128 x 64 tiles, 4 waves, tiles staged
 // through two register sets (three K-steps of loads in flight) and two LDS
-// stages, one barrier per K-step.
+// stages, one barrier per K-step.  Below one workgroup per CU it splits K
+// (blockIdx.z) into fp32 partials that k_split_sum adds in order.
+//
+// For dX = dY W_hat the weight is read transposed (K runs along W's rows):
+// the NF4 tile is dequantized into LDS K-row-major and the MFMA fragments
+// are read with gfx950's transposing LDS loads (Nf4TileT, lds_frag_tr).
 #include <type_traits>
 
 #include "common.hpp"
@@ -447,8 +452,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  auto compute = [&](int b, auto pad) {
-    constexpr bool P = decltype(pad)::value;
+  auto compute = [&](int b, auto tr) {
+    constexpr bool P = decltype(tr)::value;
     const uint16_t* sa = s_act[b];
     const uint16_t* sw = s_wt[b];
 #pragma unroll
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
   // One K segment [first, last) of global steps; the LDS stage of step st is
   // st % 2 throughout.  Two register sets by step parity; Regs::fetch(r, e)
   // loads segment-relative step e, Regs::stash(r, b) writes stage b.
-  auto segment = [&](auto& r0, auto& r1, int64_t first, int64_t last, auto fetch, auto stash, auto pad) {
+  auto segment = [&](auto& r0, auto& r1, int64_t first, int64_t last, auto fetch, auto stash, auto tr) {
     const int64_t n = last - first;
     if (n <= 0) return;
     fetch(r0, 0);
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
         if (e + 1 < n) stash(nxt, static_cast<int>((first + e + 1) & 1));
         if (e + 3 < n) fetch(nxt, e + 3);
       }
-      compute(static_cast<int>((first + e) & 1), pad);
+      compute(static_cast<int>((first + e) & 1), tr);
       if (late) {
         if (e + 1 < n) stash(nxt, static_cast<int>((first + e + 1) & 1));
         if (e + 3 < n) fetch(nxt, e + 3);
@@ -680,9 +685,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.f;
 
   typedef bf16x8 Frags[FN + FM];  // [0, FN) weight rows, [FN, FN + FM) activation rows
-  // pad: the weight stage holds a transposed NF4 tile (K-row-major)
-  auto read_frags = [&](Frags& f, const uint16_t* sw, const uint16_t* sa, int j, auto pad) {
-    constexpr bool P = decltype(pad)::value;
+  // tr: the weight stage holds a transposed NF4 tile (K-row-major)
+  auto read_frags = [&](Frags& f, const uint16_t* sw, const uint16_t* sa, int j, auto tr) {
+    constexpr bool P = decltype(tr)::value;
     const int chunk = 2 * j + half;
 #pragma unroll
     for (int a = 0; a < FN; ++a) f[a] = wt_frag<P, BN>(sw, wn * WN + a * 32, wn * WN + a * 32 + r32, j, chunk);
