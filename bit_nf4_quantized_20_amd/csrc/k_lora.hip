@@ -196,10 +196,13 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
     const int64_t t = t0 + wm * 64 + c * 32 + r32;
     if (t >= T) continue;
     float* dst = part + (kc * T + t) * npr + pj * rp + j0 + wn * 32 + 4 * h;
+    // ranks >= r are zero and k_lora_down_fin does not read them: a store
+    // whose four ranks all lie there is skipped
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<f32x4v*>(dst + 8 * g) =
-          f32x4v{acc[c][4 * g], acc[c][4 * g + 1], acc[c][4 * g + 2], acc[c][4 * g + 3]};
+      if (j0 + wn * 32 + 4 * h + 8 * g < r)
+        *reinterpret_cast<f32x4v*>(dst + 8 * g) =
+            f32x4v{acc[c][4 * g], acc[c][4 * g + 1], acc[c][4 * g + 2], acc[c][4 * g + 3]};
   }
 }
 
@@ -209,10 +212,12 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
 //   hilo_t [2 rp][ldt]    transposed; tokens [T, ldt) are zero
 // One workgroup per 16 tokens x 64 ranks (4 per thread, the KC loads of one
 // value issued together); the transposed copy goes through an LDS tile so
-// both stores are coalesced.
+// both stores are coalesced.  Ranks r .. rp - 1 are written as zeros without
+// reading the partials (k_lora_down_part leaves them unwritten).
 constexpr int kDownMaxKC = 16;
 __global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__ part, int64_t T, int KC,
-                                                       int nP, int rp, float scale, uint16_t* __restrict__ pad,
+                                                       int nP, int r, int rp, float scale,
+                                                       uint16_t* __restrict__ pad,
                                                        int64_t ldpad, uint16_t* __restrict__ hilo_t,
                                                        int64_t ldt) {
   __shared__ uint32_t s_t[64][17];  // [rank][token] hi | lo << 16
@@ -224,6 +229,7 @@ __global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__
   const int npr = nP * rp;
   // rank columns of this workgroup: projection pj, ranks jj .. jj + 63 (rp % 64 == 0)
   const int pj = jb / rp, jj = jb % rp;
+  const bool live_rank = jj + jl < r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tl = (tid >> 6) + 4 * i;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256) void k_lora_down_fin(const float* __restrict__
     float pv[kDownMaxKC];
 #pragma unroll
     for (int q = 0; q < kDownMaxKC; ++q)
-      pv[q] = (ok && q < KC) ? part[(static_cast<int64_t>(q) * T + t) * npr + jb + jl] : 0.f;
+      pv[q] = (ok && live_rank && q < KC) ? part[(static_cast<int64_t>(q) * T + t) * npr + jb + jl] : 0.f;
     float v = 0.f;
 #pragma unroll
     for (int q = 0; q < kDownMaxKC; ++q) v += pv[q];
@@ -311,7 +317,7 @@ hipError_t launch_lora_down(const uint16_t* in, int64_t ldin, int64_t T, int64_t
   const int64_t tt = hilo_t != nullptr ? (ldt > T ? ldt : T) : T;
   const dim3 fgrid(static_cast<uint32_t>(ceil_div(tt, 16)), static_cast<uint32_t>(nP * rp / 64));
   hipLaunchKernelGGL(k_lora_down_fin, fgrid, dim3(256), 0, s, part, T, static_cast<int>(KC), nP,
-                     static_cast<int>(rp), scale, pad, ldpad, hilo_t, ldt);
+                     static_cast<int>(r), static_cast<int>(rp), scale, pad, ldpad, hilo_t, ldt);
   return hipGetLastError();
 }
 
