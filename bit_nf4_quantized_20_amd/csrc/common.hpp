@@ -99,6 +99,10 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint
 // (dst rows have stride ldd elements, ldd >= 2 Cp)
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
                            int64_t Cp, int64_t ldd, hipStream_t s);
+// one launch doing launch_transpose_bf16(B, out, r, bt) and
+// launch_pad_bf16(A, in, r, true, a_t_pad, rp, ldd)
+hipError_t launch_factor_prep(const uint16_t* B, int64_t out, int64_t r, uint16_t* bt, const uint16_t* A,
+                              int64_t in, uint16_t* a_t_pad, int64_t rp, int64_t ldd, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, int64_t n, float v, hipStream_t s);
 // count (<= kMaxFill) buffers dst[i] of n[i] floats set to v in one launch
 constexpr int kMaxFill = 2 * kMaxProj;

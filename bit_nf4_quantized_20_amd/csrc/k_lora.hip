@@ -592,17 +592,32 @@ hipError_t launch_lora_grad(const uint16_t* Pt, int64_t T, int64_t ldt, int64_t 
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_pad_bf16(const uint16_t* __restrict__ src, int64_t R,
-                                                  int64_t C, int transpose,
-                                                  uint16_t* __restrict__ dst, int64_t Cp, int64_t ldd) {
-  // dst row i = [src row i zero-padded to Cp | the same again]
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+namespace {
+// dst row i = [src row i zero-padded to Cp | the same again] (src transposed
+// when `transpose`: row i of src^T is column i of src [C][R]); element idx of R * Cp
+__device__ __forceinline__ void pad_elem(int64_t idx, const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                         int transpose, uint16_t* __restrict__ dst, int64_t Cp, int64_t ldd) {
   if (idx >= R * Cp) return;
   const int64_t i = idx / Cp, j = idx % Cp;
   uint16_t v = 0;
   if (j < C) v = transpose ? src[j * R + i] : src[i * C + j];
   dst[i * ldd + j] = v;
   dst[i * ldd + Cp + j] = v;
+}
+
+// dst[c][r] = src[r][c] for src [R][C]; element idx of R * C
+__device__ __forceinline__ void transpose_elem(int64_t idx, const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                               uint16_t* __restrict__ dst) {
+  if (idx >= R * C) return;
+  const int64_t c = idx / R, rr = idx % R;
+  dst[idx] = src[rr * C + c];
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_pad_bf16(const uint16_t* __restrict__ src, int64_t R,
+                                                  int64_t C, int transpose,
+                                                  uint16_t* __restrict__ dst, int64_t Cp, int64_t ldd) {
+  pad_elem(static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x, src, R, C, transpose, dst, Cp, ldd);
 }
 
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
@@ -614,17 +629,35 @@ hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool trans
 
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R,
                                                         int64_t C, uint16_t* __restrict__ dst) {
-  // dst[c][r] = src[r][c]
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= R * C) return;
-  const int64_t c = idx / R, rr = idx % R;
-  dst[idx] = src[rr * C + c];
+  transpose_elem(static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x, src, R, C, dst);
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
                                  hipStream_t s) {
   hipLaunchKernelGGL(k_transpose_bf16, dim3(static_cast<uint32_t>(ceil_div(R * C, 256))), dim3(256),
                      0, s, src, R, C, dst);
+  return hipGetLastError();
+}
+
+// The backward's two rank-factor copies in one launch: the first tb blocks
+// transpose B [out][r] into bt [r][out], the rest pad A [r][in] transposed
+// into a_t_pad [in][ldd] (A^T | A^T, each zero-padded to rp columns).
+__global__ __launch_bounds__(256) void k_factor_prep(const uint16_t* __restrict__ B, int64_t out, int64_t r,
+                                                     uint16_t* __restrict__ bt, int64_t tb,
+                                                     const uint16_t* __restrict__ A, int64_t in,
+                                                     uint16_t* __restrict__ a_t_pad, int64_t rp, int64_t ldd) {
+  const int64_t blk = blockIdx.x;
+  if (blk < tb)
+    transpose_elem(blk * 256 + threadIdx.x, B, out, r, bt);
+  else
+    pad_elem((blk - tb) * 256 + threadIdx.x, A, in, r, 1, a_t_pad, rp, ldd);
+}
+
+hipError_t launch_factor_prep(const uint16_t* B, int64_t out, int64_t r, uint16_t* bt, const uint16_t* A,
+                              int64_t in, uint16_t* a_t_pad, int64_t rp, int64_t ldd, hipStream_t s) {
+  const int64_t tb = ceil_div(out * r, 256), pb = ceil_div(in * rp, 256);
+  hipLaunchKernelGGL(k_factor_prep, dim3(static_cast<uint32_t>(tb + pb)), dim3(256), 0, s, B, out, r, bt, tb, A,
+                     in, a_t_pad, rp, ldd);
   return hipGetLastError();
 }
 

@@ -611,13 +611,13 @@ int linear_bwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, const
   // (small token counts without dropout took the streamed path above)
   int64_t off = 0;
   for (int i = 0; i < n && e == hipSuccess; ++i) {
-    // s V_i = s dY_i B_i with dY_i the projection's columns of dY
-    e = launch_transpose_bf16(B[i], outs[i], r, b_t, s);
+    // B_i^T and the padded A_i^T in one launch, then s V_i = s dY_i B_i with
+    // dY_i the projection's columns of dY
+    e = launch_factor_prep(B[i], outs[i], r, b_t, A[i], in, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
     const uint16_t* bt = b_t;
     if (e == hipSuccess)
       e = launch_lora_down(dY + off, N, T, outs[i], &bt, 1, r, scale, v_pad + i * 2 * rp, n * 2 * rp,
                            vt + i * 2 * rp * tp, tp, rp, part, s);
-    if (e == hipSuccess) e = launch_pad_bf16(A[i], in, r, true, a_t_pad + i * 2 * rp, rp, n * 2 * rp, s);
     if (e == hipSuccess && !fused)
       e = launch_nf4_dequantize_transposed(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], in,
                                            w_dq_t + off, N, s, absmax_fp32(W[i]));
