@@ -99,6 +99,10 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint
 // (dst rows have stride ldd elements, ldd >= 2 Cp)
 hipError_t launch_pad_bf16(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst,
                            int64_t Cp, int64_t ldd, hipStream_t s);
+// launch_pad_bf16(src[i], R[i], C, false, dst[i], Cp, ldd) for i < n (<= kMaxProj)
+// in one launch
+hipError_t launch_pad_many(const uint16_t* const* src, const int64_t* R, uint16_t* const* dst, int n, int64_t C,
+                           int64_t Cp, int64_t ldd, hipStream_t s);
 // one launch doing launch_transpose_bf16(B, out, r, bt) and
 // launch_pad_bf16(A, in, r, true, a_t_pad, rp, ldd)
 hipError_t launch_factor_prep(const uint16_t* B, int64_t out, int64_t r, uint16_t* bt, const uint16_t* A,

@@ -639,6 +639,43 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint
   return hipGetLastError();
 }
 
+// launch_pad_bf16 (not transposed) for up to kMaxProj sources in one launch:
+// job i takes blocks [blk0[i], blk0[i + 1])
+struct PadJobs {
+  const uint16_t* src[kMaxProj];
+  uint16_t* dst[kMaxProj];
+  int64_t R[kMaxProj];
+  int64_t blk0[kMaxProj + 1];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void k_pad_many(PadJobs J, int64_t C, int64_t Cp, int64_t ldd) {
+  const int64_t blk = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxProj; ++q)
+    if (q < J.n && blk >= J.blk0[q]) i = q;
+  pad_elem((blk - J.blk0[i]) * 256 + threadIdx.x, J.src[i], J.R[i], C, 0, J.dst[i], Cp, ldd);
+}
+
+hipError_t launch_pad_many(const uint16_t* const* src, const int64_t* R, uint16_t* const* dst, int n, int64_t C,
+                           int64_t Cp, int64_t ldd, hipStream_t s) {
+  if (n < 1 || n > kMaxProj) return hipErrorInvalidValue;
+  if (n == 1) return launch_pad_bf16(src[0], R[0], C, false, dst[0], Cp, ldd, s);
+  PadJobs J{};
+  J.n = n;
+  J.blk0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    J.src[i] = src[i];
+    J.dst[i] = dst[i];
+    J.R[i] = R[i];
+    J.blk0[i + 1] = J.blk0[i] + ceil_div(R[i] * Cp, 256);
+  }
+  if (J.blk0[n] == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pad_many, dim3(static_cast<uint32_t>(J.blk0[n])), dim3(256), 0, s, J, C, Cp, ldd);
+  return hipGetLastError();
+}
+
 // The backward's two rank-factor copies in one launch: the first tb blocks
 // transpose B [out][r] into bt [r][out], the rest pad A [r][in] transposed
 // into a_t_pad [in][ldd] (A^T | A^T, each zero-padded to rp columns).

@@ -483,14 +483,25 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
     const int64_t ldb = per_proj ? 2 * rp : n * 2 * rp;
     if (e == hipSuccess && n > 1 && !per_proj)
       e = launch_fill_f32(reinterpret_cast<float*>(b_pad), N * ldb / 2, 0.f, s);
+    {
+      // every projection's B_i padded in one launch
+      const uint16_t* bsrc[kMaxProj];
+      uint16_t* bdst[kMaxProj];
+      int64_t brows[kMaxProj];
+      int64_t o = 0;
+      for (int i = 0; i < n; ++i) {
+        bsrc[i] = B[i];
+        bdst[i] = b_pad + o * ldb + (per_proj ? 0 : i * 2 * rp);
+        brows[i] = outs[i];
+        o += outs[i];
+      }
+      if (e == hipSuccess) e = launch_pad_many(bsrc, brows, bdst, n, r, rp, ldb, s);
+    }
     int64_t off = 0;
     for (int i = 0; i < n && e == hipSuccess; ++i) {
-      e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * ldb + (per_proj ? 0 : i * 2 * rp), rp, ldb,
-                          s);
-      if (e == hipSuccess)
-        e = fp32 ? launch_nf4_dequantize_nodq(W[i].codes, W[i].absmax_scale, outs[i] * in, w_dq + off * in, s)
-                 : launch_nf4_dequantize(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i] * in,
-                                         w_dq + off * in, s);
+      e = fp32 ? launch_nf4_dequantize_nodq(W[i].codes, W[i].absmax_scale, outs[i] * in, w_dq + off * in, s)
+               : launch_nf4_dequantize(W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i] * in,
+                                       w_dq + off * in, s);
       off += outs[i];
     }
     if (e == hipSuccess) {
@@ -507,12 +518,18 @@ int linear_fwd_impl(const qlora_nf4_weight* W, int n, const qlora_bf16* X, int64
     return launched(e);
   }
   Nf4Proj proj[kMaxProj];
+  const uint16_t* bsrc[kMaxProj];
+  uint16_t* bdst[kMaxProj];
+  int64_t brows[kMaxProj];
   int64_t off = 0;
-  for (int i = 0; i < n && e == hipSuccess; ++i) {
-    e = launch_pad_bf16(B[i], outs[i], r, false, b_pad + off * 2 * rp, rp, 2 * rp, s);
+  for (int i = 0; i < n; ++i) {
+    bsrc[i] = B[i];
+    bdst[i] = b_pad + off * 2 * rp;
+    brows[i] = outs[i];
     proj[i] = Nf4Proj{W[i].codes, W[i].absmax_q, W[i].absmax_scale, outs[i], u_pad + i * 2 * rp};
     off += outs[i];
   }
+  if (e == hipSuccess) e = launch_pad_many(bsrc, brows, bdst, n, r, rp, 2 * rp, s);  // every B_i padded
   if (e == hipSuccess)
     e = launch_gemm_nf4(T, n, proj, X, in, in, n * 2 * rp, b_pad, 2 * rp, 2 * rp, Y, N, s, split, split_n);
   return launched(e);
